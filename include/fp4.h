@@ -1,0 +1,189 @@
+/*
+ * fp4.h -- C ABI of libfp4.so: NVFP4 / MXFP4 micro-scaled FP4 on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is DEVICE memory owned by the caller.  The library never
+ *    allocates or frees memory and never synchronizes: the work is enqueued on
+ *    `stream` (NULL = the null stream) and the call returns.
+ *  - Tensors are row-major and contiguous.  Blocks of 16 (NVFP4) or 32 (MXFP4)
+ *    values run along the last dimension ("cols", the GEMM's K); a last partial
+ *    block covers the remaining columns.
+ *  - Packed FP4: a row of C values takes ceil(C/2) bytes; value 2j sits in the
+ *    low nibble of byte j, value 2j+1 in the high nibble; the high nibble of an
+ *    odd row's last byte is 0.  FP4 code = sign<<3 | E2M1 magnitude code, values
+ *    {0, 0.5, 1, 1.5, 2, 3, 4, 6} ("FP4" wiki, 技術原理: ONNX FLOAT4E2M1 rule and
+ *    packing; 10100.com data-type article, "nvFP4的数据结构设计").
+ *  - Argument checks (NULL, shape, dtype, alignment, workspace size) run on the
+ *    host before anything is enqueued; on failure the call returns the status
+ *    and enqueues nothing.  A launch failure returns FP4_ERR_HIP.  Device faults
+ *    surface at the caller's next synchronization (HIP semantics).
+ *  - The device must be gfx950; anything else returns FP4_ERR_ARCH (no silent
+ *    fallback to another precision).
+ *  - Non-finite inputs, |x| >= 2^126 and tensors whose amax is below ~1e-30 are
+ *    outside the contract: no fault, outputs unspecified.
+ *  - Calls on distinct streams with distinct buffers are independent; the
+ *    library keeps no device state between calls.
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP4_OK = 0,
+  FP4_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  FP4_ERR_SHAPE = 2,     /* negative size, K not a multiple of the block, ... */
+  FP4_ERR_DTYPE = 3,     /* unknown dtype / format / rounding enum            */
+  FP4_ERR_ALIGN = 4,     /* a pointer misses the alignment the call states    */
+  FP4_ERR_ARCH = 5,      /* current device is not gfx950                      */
+  FP4_ERR_WORKSPACE = 6, /* workspace missing or smaller than required        */
+  FP4_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed        */
+} fp4_status;
+
+typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
+typedef enum { FP4_NVFP4 = 0, FP4_MXFP4 = 1 } fp4_format;
+typedef enum { FP4_RNE = 0, FP4_SR = 1 } fp4_rounding;
+
+/* Bytes of workspace that nvfp4_quantize / hadamard_quantize need when the
+ * global amax is computed on the device (amax_given == 0): per-workgroup
+ * partial maxima of the first pass. */
+#define FP4_AMAX_WORKSPACE_BYTES 4096
+
+/*
+ * nvfp4_quantize -- two-level NVFP4 quantization of x [rows, cols].
+ *
+ * "low-precision floats" blog, section "FP4 / MXFP4 / NVFP4" (s_global and
+ * s_block equations): s_global = amax / (6 * 448); per 16 values
+ * s_block = (block_amax / 6) / s_global stored as FP8 E4M3; each value is
+ * Q_E2M1(x / (s_global * s_block)).  NVIDIA "Introducing NVFP4" blog: one E4M3
+ * scale per 16-value micro-block plus one FP32 scale per tensor.
+ * Float32 operation order (exact contract, bit-identical to the CPU oracle):
+ *   G = max|x| (or *global_amax when amax_given); s_global = G / 2688 (1 if G == 0)
+ *   t = (A_b / 6) / s_global -> E4M3, nearest-even, saturating at 448, subnormals kept
+ *   s_b = s_global * E4M3(t);  r_b = 1 / s_b (0 if s_b == 0)
+ *   code_i = E2M1(x_i * r_b): nearest, ties to even, saturating at 6, sign of x_i kept
+ *
+ *  x            [rows, cols], FP4_F32 or FP4_BF16 (xt)
+ *  q            out [rows, ceil(cols/2)] packed codes
+ *  scales       out [rows, ceil(cols/16)] E4M3 bytes
+ *  global_amax  amax_given != 0: read (static / calibrated amax, one float);
+ *               amax_given == 0: written with the computed amax
+ *  global_scale out, one float: s_global (the g_a / g_b of fp4_scaled_gemm)
+ *  workspace    >= FP4_AMAX_WORKSPACE_BYTES bytes when amax_given == 0, else may be NULL
+ * rows == 0 or cols == 0 writes G = 0 and s_global = 1 only.
+ */
+fp4_status nvfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t cols,
+                          uint8_t* q, uint8_t* scales, float* global_amax, int amax_given,
+                          float* global_scale, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * mxfp4_quantize -- MXFP4: E2M1 values with one E8M0 power-of-two scale per 32
+ * values and no tensor scale (10100.com data-type article, "mxFP4的技术局限";
+ * NVIDIA blog Table 1).  Scale = the smallest 2^e with 6 * 2^e >= block amax,
+ * the rounded-up power of two of the "low-precision floats" blog (1.99 -> 2,
+ * 2.01 -> 4); byte = clamp(e + 127, 0, 254), 0 for an all-zero block.
+ * code_i = E2M1(x_i * 2^-e) (exact multiply).
+ *  q       out [rows, ceil(cols/2)];  scales out [rows, ceil(cols/32)] E8M0 bytes
+ */
+fp4_status mxfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t cols,
+                          uint8_t* q, uint8_t* scales, hipStream_t stream);
+
+/*
+ * fp4_dequantize -- x_hat = s * v ("low-precision floats" blog: x_hat =
+ * s_global * s_block * Q(.)).
+ *  NVFP4: x_hat = (s_global * E4M3(byte)) * v in float32 (two roundings, the
+ *         first product identical to the quantizer's s_b); global_scale is the
+ *         device float written by nvfp4_quantize.
+ *  MXFP4: x_hat = v * 2^(byte-127) (exact); global_scale must be NULL.
+ *  y      out [rows, cols] float32, or bf16 rounded to nearest-even from the float32 value.
+ */
+fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* q, const uint8_t* scales,
+                          const float* global_scale, int64_t rows, int64_t cols,
+                          void* y, fp4_dtype yt, hipStream_t stream);
+
+/*
+ * fp4_scaled_gemm -- D = g_d * ((g_a s_a . A) @ (g_b s_b . W)^T), fp32 accumulate.
+ *
+ * "NVIDIA NVFP4 与 Micro-Scaling" article, section 三 (scaled GEMM equation) and
+ * section 五 (operand layouts A_fp4 [M, K/2], a_scale [M, K/16]; the concept API
+ * passes W [N, K] as W.t()).  Both operands are K-major packed FP4:
+ *   A [M, K/2], a_scales [M, K/bs];  W [N, K/2], w_scales [N, K/bs]
+ * bs = 16 with E4M3 bytes (NVFP4) or 32 with E8M0 bytes (MXFP4).
+ *   g_a, g_b  device floats: NVFP4 -> the global_scale written by nvfp4_quantize;
+ *             MXFP4 -> must be NULL (tensor scale 1).
+ *   g_d       host float output multiplier.
+ *   D         out [M, N], float32 or bf16 (nearest-even from the float32 result).
+ * Each block product s_a * s_w * sum_k v_a v_w is exact; blocks are summed in
+ * float32; |D - D_ref| <= 1e-5 * |g_d| * sum_k |A_hat_mk W_hat_nk| (+ one bf16
+ * rounding for bf16 output).  K must be a multiple of bs (FP4_ERR_SHAPE);
+ * A, W must be 16-byte aligned and K a multiple of 32 (FP4_ERR_ALIGN / SHAPE).
+ */
+fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
+                           const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                           const float* g_b, float g_d, int64_t M, int64_t N, int64_t K,
+                           void* D, fp4_dtype dt, hipStream_t stream);
+
+/* Bytes of workspace fp4_gemv_batched needs for a batch of B rows of length K. */
+size_t fp4_gemv_workspace_bytes(int64_t B, int64_t K);
+
+/*
+ * fp4_gemv_batched -- decode-time batched GEMV y = g_d * x_hat @ W_hat^T
+ * (10100.com data-type article: "FP4 batch GEMV", written here from the scaled
+ * GEMM of the ybb.press article, section 三).
+ *   x   [B, K] float32 or bf16, quantized to NVFP4 on the fly with ONE dynamic
+ *       tensor scale over all of [B, K], bit-identical to nvfp4_quantize;
+ *   W   NVFP4 [N, K/2] + w_scales [N, K/16] + g_w (device float);
+ *   y   out [B, N] float32 or bf16.  1 <= B <= 16, K % 32 == 0.
+ *   workspace  >= fp4_gemv_workspace_bytes(B, K) bytes (holds quantized x).
+ * Accuracy as for fp4_scaled_gemm.
+ */
+fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_t* W,
+                            const uint8_t* w_scales, const float* g_w, int64_t N, int64_t K,
+                            float g_d, void* y, fp4_dtype yt, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * hadamard_quantize -- rotate every `group` (= 128) contiguous channels by the
+ * orthonormal Walsh-Hadamard matrix, then NVFP4-quantize the rotated tensor
+ * ("NVIDIA NVFP4 与 Micro-Scaling" article, section 4.1: x @ H with H H^T = I by
+ * a fast Walsh-Hadamard transform; "FP4" wiki, 技術實現與量化方法: Hadamard
+ * transform and stochastic rounding as NVFP4 quantization options).
+ * Transform: Sylvester order, butterfly stages h = 1, 2, ..., 64 in float32
+ * ((a, b) -> (a + b, a - b)), then one multiply by fl32(1/sqrt(128)).
+ * The global amax is that of the rotated tensor (computed unless amax_given).
+ *   mode FP4_RNE: as nvfp4_quantize.
+ *   mode FP4_SR:  element codes rounded stochastically (scales stay nearest):
+ *     for lo <= |q| < hi adjacent E2M1 magnitudes, round up iff
+ *     u16 < ((|q| - lo) / (hi - lo)) * 65536, where u16 are 16 bits of
+ *     Philox4x32-10 (Salmon et al., SC'11) with key (seed low, seed high) and
+ *     counter (i/8 low, i/8 high, 0, 0) for flat element index i, taking word
+ *     (i%8)/2, low half for even i%8, high half for odd.
+ *   cols % group == 0; group must be 128.
+ * Outputs and workspace as nvfp4_quantize.
+ */
+fp4_status hadamard_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, int group,
+                             fp4_rounding mode, uint64_t seed, uint8_t* q, uint8_t* scales,
+                             float* global_amax, int amax_given, float* global_scale,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable text of a status (static storage). */
+const char* fp4_status_string(fp4_status s);
+
+/* Text of the last HIP error seen by this thread inside the library ("" if none). */
+const char* fp4_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H */

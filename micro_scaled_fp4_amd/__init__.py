@@ -1,0 +1,244 @@
+"""micro_scaled_fp4_amd -- NVFP4 / MXFP4 micro-scaled FP4 on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of libfp4.so (include/fp4.h).  This module
+only marshals arguments: torch allocates outputs and workspaces and supplies
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  There is no CPU fallback: the functions raise if the library is
+missing, if a tensor is not on a GPU, or if the call returns an error status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp4.so")
+
+# enums of include/fp4.h
+FP4_OK = 0
+FP4_F32, FP4_BF16 = 0, 1
+FP4_NVFP4, FP4_MXFP4 = 0, 1
+FP4_RNE, FP4_SR = 0, 1
+AMAX_WORKSPACE_BYTES = 4096
+
+NV_BLOCK, MX_BLOCK = 16, 32
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "nvfp4_quantize": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p,
+                                      ctypes.c_int, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "mxfp4_quantize": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "fp4_dequantize": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p,
+                                      ctypes.c_int, _c_p]),
+    "fp4_scaled_gemm": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                       ctypes.c_float, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_int,
+                                       _c_p]),
+    "fp4_gemv_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "fp4_gemv_batched": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_p, _c_p, _c_p, _c_i64,
+                                        _c_i64, ctypes.c_float, _c_p, ctypes.c_int, _c_p,
+                                        ctypes.c_size_t, _c_p]),
+    "hadamard_quantize": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_uint64, _c_p, _c_p, _c_p,
+                                         ctypes.c_int, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "fp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fp4_last_hip_error": (ctypes.c_char_p, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfp4.so and attach the C signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m micro_scaled_fp4_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+class FP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load_library()
+        msg = lib.fp4_status_string(status).decode()
+        extra = lib.fp4_last_hip_error().decode() if status == 7 else ""
+        super().__init__(f"{where}: status {status} ({msg}) {extra}".strip())
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != FP4_OK:
+        raise FP4Error(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return FP4_BF16
+    if dt == torch.float32:
+        return FP4_F32
+    raise TypeError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _gpu_2d(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    return t.contiguous()
+
+
+def _amax_arg(amax, device):
+    """Static amax as a 1-element float32 device tensor, or None (dynamic)."""
+    if amax is None:
+        return None
+    if isinstance(amax, torch.Tensor):
+        return amax.to(device=device, dtype=torch.float32).reshape(1).contiguous()
+    return torch.tensor([float(amax)], dtype=torch.float32, device=device)
+
+
+# ------------------------------------------------------------------ API ----
+def nvfp4_quantize(x: torch.Tensor, amax=None, workspace: Optional[torch.Tensor] = None):
+    """x [rows, cols] bf16/f32 -> (codes u8 [rows, ceil(cols/2)], scales u8
+    [rows, ceil(cols/16)] (E4M3 bytes), amax f32[1], s_global f32[1])."""
+    x = _gpu_2d(x, "x")
+    dev = x.device
+    rows, cols = x.shape
+    q = torch.empty((rows, (cols + 1) // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((rows, (cols + NV_BLOCK - 1) // NV_BLOCK), dtype=torch.uint8, device=dev)
+    g_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    a = _amax_arg(amax, dev)
+    given = a is not None
+    if not given:
+        a = torch.empty(1, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(AMAX_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    lib = load_library()
+    st = lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(q), _ptr(sc), _ptr(a),
+                            int(given), _ptr(g_scale), _ptr(workspace),
+                            0 if workspace is None else workspace.numel() * workspace.element_size(),
+                            _stream(dev))
+    _check(st, "nvfp4_quantize")
+    return q, sc, a, g_scale
+
+
+def mxfp4_quantize(x: torch.Tensor):
+    """x [rows, cols] -> (codes u8 [rows, ceil(cols/2)], scales u8 [rows, ceil(cols/32)] E8M0)."""
+    x = _gpu_2d(x, "x")
+    dev = x.device
+    rows, cols = x.shape
+    q = torch.empty((rows, (cols + 1) // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((rows, (cols + MX_BLOCK - 1) // MX_BLOCK), dtype=torch.uint8, device=dev)
+    st = load_library().mxfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(q), _ptr(sc),
+                                       _stream(dev))
+    _check(st, "mxfp4_quantize")
+    return q, sc
+
+
+def fp4_dequantize(fmt: int, q: torch.Tensor, scales: torch.Tensor, global_scale, cols: int,
+                   out_dtype: torch.dtype = torch.float32):
+    """Packed codes + scales (+ NVFP4 s_global) -> [rows, cols] out_dtype."""
+    q = _gpu_2d(q, "q")
+    scales = _gpu_2d(scales, "scales")
+    dev = q.device
+    rows = q.shape[0]
+    y = torch.empty((rows, cols), dtype=out_dtype, device=dev)
+    gs = None if global_scale is None else global_scale.reshape(1).contiguous()
+    st = load_library().fp4_dequantize(fmt, _ptr(q), _ptr(scales), _ptr(gs), rows, cols, _ptr(y),
+                                       _dtype_code(out_dtype), _stream(dev))
+    _check(st, "fp4_dequantize")
+    return y
+
+
+def fp4_scaled_gemm(fmt: int, A: torch.Tensor, a_scales: torch.Tensor, g_a, W: torch.Tensor,
+                    w_scales: torch.Tensor, g_b, K: int, g_d: float = 1.0,
+                    out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """D [M, N] = g_d * ((g_a s_a . A) @ (g_b s_b . W)^T); A [M, K/2], W [N, K/2] packed."""
+    A = _gpu_2d(A, "A")
+    W = _gpu_2d(W, "W")
+    a_scales = _gpu_2d(a_scales, "a_scales")
+    w_scales = _gpu_2d(w_scales, "w_scales")
+    dev = A.device
+    M, N = A.shape[0], W.shape[0]
+    if A.shape[1] != K // 2 or W.shape[1] != K // 2:
+        raise ValueError("A and W must be [rows, K/2] packed codes")
+    D = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
+    ga = None if g_a is None else g_a.reshape(1).contiguous()
+    gb = None if g_b is None else g_b.reshape(1).contiguous()
+    st = load_library().fp4_scaled_gemm(fmt, _ptr(A), _ptr(a_scales), _ptr(ga), _ptr(W),
+                                        _ptr(w_scales), _ptr(gb), float(g_d), M, N, K, _ptr(D),
+                                        _dtype_code(D.dtype), _stream(dev))
+    _check(st, "fp4_scaled_gemm")
+    return D
+
+
+def gemv_workspace_bytes(B: int, K: int) -> int:
+    return int(load_library().fp4_gemv_workspace_bytes(B, K))
+
+
+def fp4_gemv_batched(x: torch.Tensor, W: torch.Tensor, w_scales: torch.Tensor, g_w, K: int,
+                     g_d: float = 1.0, out_dtype: torch.dtype = torch.bfloat16,
+                     workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """y [B, N] = g_d * NVFP4(x) @ W_hat^T; x [B, K] bf16/f32 quantized on the fly."""
+    x = _gpu_2d(x, "x")
+    W = _gpu_2d(W, "W")
+    w_scales = _gpu_2d(w_scales, "w_scales")
+    dev = x.device
+    B = x.shape[0]
+    N = W.shape[0]
+    if x.shape[1] != K or W.shape[1] != K // 2:
+        raise ValueError("x must be [B, K] and W [N, K/2]")
+    y = out if out is not None else torch.empty((B, N), dtype=out_dtype, device=dev)
+    need = gemv_workspace_bytes(B, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load_library().fp4_gemv_batched(_ptr(x), _dtype_code(x.dtype), B, _ptr(W), _ptr(w_scales),
+                                         _ptr(g_w.reshape(1).contiguous()), N, K, float(g_d),
+                                         _ptr(y), _dtype_code(y.dtype), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "fp4_gemv_batched")
+    return y
+
+
+def hadamard_quantize(x: torch.Tensor, group: int = 128, mode: int = FP4_RNE, seed: int = 0,
+                      amax=None, workspace: Optional[torch.Tensor] = None):
+    """FWHT over 128-channel groups fused with NVFP4 quantization (RNE or SR).
+    Returns what nvfp4_quantize returns."""
+    x = _gpu_2d(x, "x")
+    dev = x.device
+    rows, cols = x.shape
+    q = torch.empty((rows, (cols + 1) // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((rows, (cols + NV_BLOCK - 1) // NV_BLOCK), dtype=torch.uint8, device=dev)
+    g_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    a = _amax_arg(amax, dev)
+    given = a is not None
+    if not given:
+        a = torch.empty(1, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(AMAX_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    st = load_library().hadamard_quantize(
+        _ptr(x), _dtype_code(x.dtype), rows, cols, group, mode, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+        _ptr(q), _ptr(sc), _ptr(a), int(given), _ptr(g_scale), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "hadamard_quantize")
+    return q, sc, a, g_scale

@@ -1,0 +1,112 @@
+// Device-side codecs for micro-scaled FP4 on gfx950.
+//
+// Every function here performs the exact float32 operation sequence stated in
+// include/fp4.h; sources of the formats:
+//   E2M1 values and packing: "FP4" wiki (newton.com.tw), 技術原理 (ONNX rule);
+//   E4M3 block scale, s_global / s_block: "low-precision floats" blog,
+//     section "FP4 / MXFP4 / NVFP4";
+//   E8M0 rounded-up power of two: same section (1.99 -> 2, 2.01 -> 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4dev {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 --
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- E2M1 --
+// Code of the nearest E2M1 magnitude (ties to the even code), saturating at 6,
+// with the sign bit of q.  The thresholds are the midpoints of
+// {0, .5, 1, 1.5, 2, 3, 4, 6}; a midpoint goes to its even-coded neighbour.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  uint32_t u = __float_as_uint(q);
+  float m = __uint_as_float(u & 0x7fffffffu);
+  uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+               (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+               (uint32_t)(m > 5.0f);
+  return c | ((u >> 28) & 8u);
+}
+
+// Value of a 4-bit code as float32.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  uint32_t bits = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3f000000u : 0u);
+  return __uint_as_float(bits | ((c & 8u) << 28));
+}
+
+// ---------------------------------------------------------------- E4M3 --
+// Nearest E4M3 (bias 7) code of t >= 0, ties to even, subnormals kept,
+// saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_code(float t) {
+  if (t < 0x1p-6f) {
+    // subnormal range: multiples of 2^-9; t * 512 is exact, adding 2^23 rounds
+    // it to the nearest integer with ties to even.
+    float s = t * 512.0f;
+    s = s + 8388608.0f;
+    return __float_as_uint(s) - 0x4b000000u;
+  }
+  uint32_t u = __float_as_uint(t);
+  u = u + 0x7ffffu + ((u >> 20) & 1u);      // round the mantissa to 3 bits
+  uint32_t c = (u >> 20) - (120u << 3);     // exponent bias 127 -> 7
+  return c > 0x7eu ? 0x7eu : c;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// NVFP4 tensor scale: s_global = G / (6 * 448), 1 for an all-zero tensor.
+__device__ __forceinline__ float nv_global_scale(float G) { return G != 0.0f ? G / 2688.0f : 1.0f; }
+
+// NVFP4 block scale byte and element multiplier for block amax A_b:
+//   t = (A_b / 6) / s_global -> E4M3;  s_b = s_global * E4M3(t);  r = 1 / s_b.
+// r == 0 when s_b == 0: then x * r is a signed zero and every code is sign|0.
+__device__ __forceinline__ void nv_block_scale(float Ab, float s_global, uint32_t& code, float& r) {
+  float t = Ab / 6.0f;
+  t = t / s_global;
+  code = e4m3_code(t);
+  float sb = s_global * e4m3_value(code);
+  r = sb != 0.0f ? 1.0f / sb : 0.0f;
+}
+
+// ---------------------------------------------------------------- E8M0 --
+// MXFP4 scale byte of block amax A (bit pattern of |A|): the smallest e with
+// 6 * 2^e >= A, as clamp(e + 127, 0, 254).  For A = m * 2^E (1 <= m < 2):
+// e = E - 2 when m <= 1.5, else E - 1.
+__device__ __forceinline__ uint32_t e8m0_code(uint32_t abits) {
+  int ef = (int)(abits >> 23);
+  int c = ef - 2 + (int)((abits & 0x7fffffu) > 0x400000u);
+  return c < 0 ? 0u : (uint32_t)c;
+}
+
+// 2^(127 - code): the exact element multiplier of an E8M0 byte.
+__device__ __forceinline__ float e8m0_inv(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+__device__ __forceinline__ float e8m0_value(uint32_t code) {
+  return code ? __uint_as_float(code << 23) : 0x1p-127f;
+}
+
+// ------------------------------------------------------- wave reductions --
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+}  // namespace fp4dev

@@ -1,0 +1,54 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernels.
+// Every launcher enqueues on `stream`, never synchronizes and returns the HIP
+// status of its launches.  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp4impl {
+
+constexpr int kAmaxPartials = 1024;  // FP4_AMAX_WORKSPACE_BYTES / 4
+
+// ---- quantize.hip ---------------------------------------------------------
+// Per-workgroup partial max|x| (float bit patterns) of n elements; writes
+// *npart <= kAmaxPartials entries of partials.
+hipError_t launch_amax(const void* x, bool bf16, int64_t n, uint32_t* partials, int* npart,
+                       hipStream_t stream);
+
+// NVFP4 quantize.  Exactly one of (amax_in) or (partials, npart) gives G.
+hipError_t launch_nv_quant(const void* x, bool bf16, int64_t rows, int64_t cols, uint8_t* q,
+                           uint8_t* scales, const float* amax_in, const uint32_t* partials,
+                           int npart, float* amax_out, float* scale_out, hipStream_t stream);
+
+hipError_t launch_mx_quant(const void* x, bool bf16, int64_t rows, int64_t cols, uint8_t* q,
+                           uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_dequant(bool mx, const uint8_t* q, const uint8_t* scales,
+                          const float* global_scale, int64_t rows, int64_t cols, void* y,
+                          bool bf16_out, hipStream_t stream);
+
+// Writes G = 0 and s_global = 1 (empty tensors).
+hipError_t launch_empty_scales(float* amax_out, float* scale_out, hipStream_t stream);
+
+// ---- hadamard.hip ---------------------------------------------------------
+hipError_t launch_hadamard_amax(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                uint32_t* partials, int* npart, hipStream_t stream);
+hipError_t launch_hadamard_quant(const void* x, bool bf16, int64_t rows, int64_t cols, bool sr,
+                                 uint64_t seed, uint8_t* q, uint8_t* scales, const float* amax_in,
+                                 const uint32_t* partials, int npart, float* amax_out,
+                                 float* scale_out, hipStream_t stream);
+
+// ---- gemv.hip -------------------------------------------------------------
+size_t gemv_workspace_bytes(int64_t B, int64_t K);
+hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
+                       const uint8_t* w_scales, const float* g_w, int64_t N, int64_t K, float g_d,
+                       void* y, bool y_bf16, void* workspace, hipStream_t stream);
+
+// ---- gemm.hip -------------------------------------------------------------
+hipError_t launch_gemm(bool mx, const uint8_t* A, const uint8_t* a_scales, const float* g_a,
+                       const uint8_t* W, const uint8_t* w_scales, const float* g_b, float g_d,
+                       int64_t M, int64_t N, int64_t K, void* D, bool d_bf16, hipStream_t stream);
+
+}  // namespace fp4impl

@@ -1,0 +1,289 @@
+// Fused Walsh-Hadamard rotation + NVFP4 quantization for gfx950.
+//
+// "NVIDIA NVFP4 与 Micro-Scaling" article, section 4.1: activations are rotated
+// by an orthogonal Hadamard matrix (x @ H, H H^T = I, fast Walsh-Hadamard)
+// before quantization; "FP4" wiki, 技術實現與量化方法: Hadamard transform and
+// stochastic rounding as NVFP4 quantization options.
+//
+// Layout: a 128-channel group is held by 4 adjacent lanes (an aligned DPP quad),
+// 32 contiguous channels per lane, i.e. two whole NVFP4 blocks per lane.
+// Butterfly stages h = 1..16 run inside a lane; h = 32 and h = 64 exchange
+// registers with the lane at xor distance 1 and 2 through DPP quad
+// permutations.  Every stage computes (a, b) -> (a + b, a - b) in float32 on the
+// same operand pairs as the plain transform, so the result is bit-identical
+// whatever lane holds which value.
+//
+// Pass 1 (dynamic amax only) rotates and reduces max|y|; pass 2 rotates again
+// and encodes, so the rotated tensor never touches HBM.
+#include "fp4_device.h"
+#include "fp4_internal.h"
+
+using namespace fp4dev;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxGrid = 2048;
+constexpr int kPer = 32;             // channels per lane
+constexpr float kNorm = 0x1.6a09e6p-4f;  // fl32(1/sqrt(128)) = 0.0883883461...
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t red[kThreads / 64];
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = umax(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load32(const void* __restrict__ x, int64_t s, float (&v)[kPer]) {
+  if (BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(x) + 4 * s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 a = p[k];
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * k + 2 * j] = bf16_lo(w[j]);
+        v[8 * k + 2 * j + 1] = bf16_hi(w[j]);
+      }
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(x) + 8 * s;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f32x4 a = p[k];
+      v[4 * k] = a.x;
+      v[4 * k + 1] = a.y;
+      v[4 * k + 2] = a.z;
+      v[4 * k + 3] = a.w;
+    }
+  }
+}
+
+// DPP quad permutations: lane ^ 1 and lane ^ 2 inside each group of 4 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+// Orthonormal 128-point FWHT of the group held by this lane's quad; p = lane's
+// position (0..3) in the quad.
+__device__ __forceinline__ void fwht128(float (&v)[kPer], int p) {
+#pragma unroll
+  for (int h = 1; h < kPer; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if ((j & h) == 0) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+  // h = 32: partner lane p ^ 1.  Lower lane keeps a + b, upper lane a - b,
+  // computed as partner + (-own) (the same IEEE operation as a - b).
+  {
+    const uint32_t neg = (p & 1) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float other = dpp_f<kQuadXor1>(v[j]);
+      v[j] = other + __uint_as_float(__float_as_uint(v[j]) ^ neg);
+    }
+  }
+  {
+    const uint32_t neg = (p & 2) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float other = dpp_f<kQuadXor2>(v[j]);
+      v[j] = other + __uint_as_float(__float_as_uint(v[j]) ^ neg);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = v[j] * kNorm;
+}
+
+// ---------------------------------------------------------- Philox4x32-10 --
+// Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3"
+// (SC'11): 10 rounds of two 32x32->64 multiplies with the Philox constants,
+// the round key bumped by the Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// Stochastic E2M1 code of q given 16 random bits u: for lo <= |q| < hi
+// adjacent magnitudes, round up iff u < (|q| - lo) / (hi - lo) * 65536,
+// evaluated exactly as u * (hi - lo) * 2^-16 < |q| - lo.  |q| >= 6 gives 6.
+__device__ __forceinline__ uint32_t e2m1_code_sr(float q, uint32_t u) {
+  const uint32_t bits = __float_as_uint(q);
+  const float m = __uint_as_float(bits & 0x7fffffffu);
+  const uint32_t sign = (bits >> 28) & 8u;
+  if (m >= 6.0f) return 7u | sign;
+  uint32_t lo_code;
+  float lo, span;
+  if (m < 1.0f) {
+    const bool half = m >= 0.5f;
+    lo_code = half ? 1u : 0u;
+    lo = half ? 0.5f : 0.0f;
+    span = 0.5f;
+  } else {
+    const uint32_t mb = bits & 0x7fffffffu;
+    lo_code = (mb >> 22) - 252u;                               // 1.0 -> 2, ..., 4.0 -> 6
+    lo = __uint_as_float(mb & 0xffc00000u);                     // truncate to 1 mantissa bit
+    span = __uint_as_float((mb & 0x7f800000u) - 0x00800000u);   // half the binade's power
+  }
+  const float d = m - lo;                   // exact
+  const float t = (float)u * span * 0x1p-16f;   // exact
+  return (lo_code + (t < d ? 1u : 0u)) | sign;
+}
+
+__device__ __forceinline__ uint32_t pack8(const uint32_t (&c)[8]) {
+  return c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) | (c[5] << 20) |
+         (c[6] << 24) | (c[7] << 28);
+}
+
+// ------------------------------------------------------------------ kernels --
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads)
+    k_had_amax(const void* __restrict__ x, int64_t nslots, uint32_t* __restrict__ partials) {
+  const int p = threadIdx.x & 3;
+  uint32_t m = 0;
+  // nslots and the slot stride are multiples of 4, so a quad enters and leaves
+  // the loop together (DPP partners are always active).
+  for (int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x; s < nslots;
+       s += (int64_t)gridDim.x * kThreads) {
+    float v[kPer];
+    load32<BF16>(x, s, v);
+    fwht128(v, p);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) m = umax(m, __float_as_uint(v[j]) & 0x7fffffffu);
+  }
+  m = block_max_u32(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+template <bool BF16, bool SR>
+__global__ void __launch_bounds__(kThreads)
+    k_had_quant(const void* __restrict__ x, int64_t nslots, uint64_t seed, uint8_t* __restrict__ q,
+                uint8_t* __restrict__ scales, const float* __restrict__ amax_in,
+                const uint32_t* __restrict__ partials, int npart, float* __restrict__ amax_out,
+                float* __restrict__ scale_out) {
+  float G;
+  if (partials == nullptr) {
+    G = *amax_in;
+  } else {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npart; i += kThreads) m = umax(m, partials[i]);
+    G = __uint_as_float(block_max_u32(m));
+  }
+  const float s_global = nv_global_scale(G);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (amax_out) *amax_out = G;
+    *scale_out = s_global;
+  }
+  const int p = threadIdx.x & 3;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  for (int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x; s < nslots;
+       s += (int64_t)gridDim.x * kThreads) {
+    float v[kPer];
+    load32<BF16>(x, s, v);
+    fwht128(v, p);
+    uint32_t w[4];
+    uint32_t sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      uint32_t am = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[16 * blk + j]) & 0x7fffffffu);
+      float r;
+      nv_block_scale(__uint_as_float(am), s_global, sc[blk], r);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t c[8];
+        const int base = 16 * blk + 8 * half;
+        if (SR) {
+          // elements 32s + base .. +7 share Philox counter (32s + base) / 8
+          const uint64_t g = (uint64_t)(4 * s + 2 * blk + half);
+          uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), 0u, 0u};
+          philox4x32_10(ctr, k0, k1);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t u = (j & 1) ? (ctr[j >> 1] >> 16) : (ctr[j >> 1] & 0xffffu);
+            c[j] = e2m1_code_sr(v[base + j] * r, u);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) c[j] = e2m1_code(v[base + j] * r);
+        }
+        w[2 * blk + half] = pack8(c);
+      }
+    }
+    reinterpret_cast<u32x4*>(q)[s] = u32x4{w[0], w[1], w[2], w[3]};
+    reinterpret_cast<uint16_t*>(scales)[s] = (uint16_t)(sc[0] | (sc[1] << 8));
+  }
+}
+
+inline int grid_for(int64_t slots) {
+  int64_t g = (slots + kThreads - 1) / kThreads;
+  if (g < 1) g = 1;
+  return (int)(g < kMaxGrid ? g : kMaxGrid);
+}
+
+}  // namespace
+
+namespace fp4impl {
+
+hipError_t launch_hadamard_amax(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                uint32_t* partials, int* npart, hipStream_t stream) {
+  const int64_t nslots = rows * cols / kPer;
+  int g = grid_for(nslots);
+  if (g > kAmaxPartials) g = kAmaxPartials;
+  *npart = g;
+  if (bf16)
+    hipLaunchKernelGGL(k_had_amax<true>, dim3(g), dim3(kThreads), 0, stream, x, nslots, partials);
+  else
+    hipLaunchKernelGGL(k_had_amax<false>, dim3(g), dim3(kThreads), 0, stream, x, nslots, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard_quant(const void* x, bool bf16, int64_t rows, int64_t cols, bool sr,
+                                 uint64_t seed, uint8_t* q, uint8_t* scales, const float* amax_in,
+                                 const uint32_t* partials, int npart, float* amax_out,
+                                 float* scale_out, hipStream_t stream) {
+  const int64_t nslots = rows * cols / kPer;
+  const int g = grid_for(nslots);
+#define FP4_HAD_LAUNCH(B, S)                                                                  \
+  hipLaunchKernelGGL((k_had_quant<B, S>), dim3(g), dim3(kThreads), 0, stream, x, nslots, seed, q, \
+                     scales, amax_in, partials, npart, amax_out, scale_out)
+  if (bf16) {
+    if (sr) FP4_HAD_LAUNCH(true, true); else FP4_HAD_LAUNCH(true, false);
+  } else {
+    if (sr) FP4_HAD_LAUNCH(false, true); else FP4_HAD_LAUNCH(false, false);
+  }
+#undef FP4_HAD_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace fp4impl

@@ -372,17 +372,23 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
     return c0, c1, c2, c3
 
 
-def sr_bits(rows: int, cols: int, seed: int) -> np.ndarray:
-    """16 random bits per element of a row-major [rows, cols] tensor: element with
-    flat index i uses Philox4x32-10 with counter (i//8 low word, i//8 high word,
-    0, 0) and key (seed low word, seed high word); output word (i%8)//2, low 16
-    bits for even i%8, high 16 bits for odd."""
-    n = rows * cols
-    g = np.arange((n + 7) // 8, dtype=np.uint64)
+def sr_bits_at(flat_index: np.ndarray, seed: int) -> np.ndarray:
+    """16 random bits for each given flat element index i of a row-major tensor:
+    Philox4x32-10 with counter (i//8 low word, i//8 high word, 0, 0) and key
+    (seed low word, seed high word); output word (i%8)//2, its low 16 bits for
+    even i%8 and high 16 bits for odd."""
+    i = np.asarray(flat_index, dtype=np.uint64)
+    g = i // np.uint64(8)
     w = philox4x32_10(g & np.uint64(MASK32), g >> np.uint64(32), 0, 0, seed & MASK32, (seed >> 32) & MASK32)
-    words = np.stack(w, axis=1)                       # [groups, 4]
-    halves = np.stack([words & np.uint64(0xFFFF), words >> np.uint64(16)], axis=2)   # [groups, 4, 2]
-    return halves.reshape(-1)[:n].astype(np.uint16).reshape(rows, cols)
+    words = np.stack(w, axis=-1)
+    j = (i % np.uint64(8)).astype(np.int64)
+    word = np.take_along_axis(words, (j // 2)[..., None], axis=-1)[..., 0]
+    return np.where(j % 2 == 0, word & np.uint64(0xFFFF), word >> np.uint64(16)).astype(np.uint16)
+
+
+def sr_bits(rows: int, cols: int, seed: int) -> np.ndarray:
+    """sr_bits_at for every element of a [rows, cols] tensor."""
+    return sr_bits_at(np.arange(rows * cols, dtype=np.uint64), seed).reshape(rows, cols)
 
 
 def sr_round(q: np.ndarray, bits: np.ndarray) -> np.ndarray:

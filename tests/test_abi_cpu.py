@@ -1,0 +1,90 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point that include/fp4.h declares,
+and reject bad arguments on the host (before any HIP call) with the documented
+status codes.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import micro_scaled_fp4_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(m.LIB_PATH), reason="libfp4.so not built")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ARCH, WORKSPACE, HIP = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:fp4_status|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_six_calls():
+    names = declared_functions()
+    for fn in ("nvfp4_quantize", "mxfp4_quantize", "fp4_dequantize", "fp4_scaled_gemm",
+               "fp4_gemv_batched", "hadamard_quantize"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) <= set(m.SIGNATURES)
+
+
+def test_status_strings():
+    lib = m.load_library()
+    for s in range(8):
+        assert lib.fp4_status_string(s)
+    assert b"gfx950" in lib.fp4_status_string(ARCH)
+
+
+P = ctypes.c_void_p(4096)       # a non-NULL, aligned stand-in pointer (never dereferenced)
+
+
+def test_quantize_argument_errors():
+    lib = m.load_library()
+    q = lib.nvfp4_quantize
+    assert q(P, 9, 4, 16, P, P, P, 0, P, P, 4096, None) == DTYPE
+    assert q(P, 1, -1, 16, P, P, P, 0, P, P, 4096, None) == SHAPE
+    assert q(P, 1, 4, 16, P, P, P, 0, None, P, 4096, None) == NULL
+    assert q(None, 1, 4, 16, P, P, P, 0, P, P, 4096, None) == NULL
+    assert q(P, 1, 4, 16, P, P, None, 1, P, None, 0, None) == NULL      # static amax missing
+    assert q(P, 1, 4, 16, P, P, P, 0, P, None, 0, None) == WORKSPACE
+    assert q(P, 1, 4, 16, P, P, P, 0, P, P, 100, None) == WORKSPACE
+    assert q(ctypes.c_void_p(4097), 1, 4, 16, P, P, P, 0, P, P, 4096, None) == ALIGN
+    mx = lib.mxfp4_quantize
+    assert mx(P, 3, 4, 32, P, P, None) == DTYPE
+    assert mx(None, 1, 4, 32, P, P, None) == NULL
+    assert mx(P, 0, 4, -2, P, P, None) == SHAPE
+
+
+def test_dequant_gemm_gemv_hadamard_argument_errors():
+    lib = m.load_library()
+    assert lib.fp4_dequantize(7, P, P, P, 4, 16, P, 0, None) == DTYPE
+    assert lib.fp4_dequantize(1, P, P, P, 4, 32, P, 0, None) == DTYPE     # MX takes no tensor scale
+    assert lib.fp4_dequantize(0, P, P, None, 4, 16, P, 0, None) == NULL
+    g = lib.fp4_scaled_gemm
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 48, P, 1, None) == SHAPE     # K % 32
+    assert g(1, P, P, P, P, P, P, 1.0, 8, 8, 64, P, 1, None) == DTYPE     # MX: g_a/g_b must be NULL
+    assert g(0, P, P, None, P, P, P, 1.0, 8, 8, 64, P, 1, None) == NULL
+    assert g(0, ctypes.c_void_p(4104), P, P, P, P, P, 1.0, 8, 8, 64, P, 1, None) == ALIGN
+    v = lib.fp4_gemv_batched
+    need = lib.fp4_gemv_workspace_bytes(4, 512)
+    assert need >= 4 * 256 + 4 * 32
+    assert v(P, 1, 0, P, P, P, 8, 512, 1.0, P, 1, P, need, None) == SHAPE   # B < 1
+    assert v(P, 1, 17, P, P, P, 8, 512, 1.0, P, 1, P, 1 << 20, None) == SHAPE
+    assert v(P, 1, 4, P, P, P, 8, 500, 1.0, P, 1, P, need, None) == SHAPE   # K % 32
+    assert v(P, 1, 4, P, P, P, 8, 512, 1.0, P, 1, P, need - 1, None) == WORKSPACE
+    h = lib.hadamard_quantize
+    assert h(P, 1, 4, 256, 64, 0, 0, P, P, P, 0, P, P, 4096, None) == SHAPE
+    assert h(P, 1, 4, 200, 128, 0, 0, P, P, P, 0, P, P, 4096, None) == SHAPE
+    assert h(P, 1, 4, 256, 128, 5, 0, P, P, P, 0, P, P, 4096, None) == DTYPE

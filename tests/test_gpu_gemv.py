@@ -1,0 +1,53 @@
+"""GPU parity: batched NVFP4 GEMV against the float64 oracle.
+
+y = g_d * NVFP4(x) @ W_hat^T.  Pass rule: |y - y_ref| <= 1e-5 * |g_d| *
+sum_k |x_hat_k * W_hat_nk| (float32 output), plus one bf16 rounding of y_ref
+for bf16 output.  W operands come from the oracle's quantizer (small cases)
+or are uniformly random valid NVFP4 codes and scales (full decode shape).
+"""
+import numpy as np
+import pytest
+import torch
+
+import micro_scaled_fp4_amd as fp4
+import workloads
+from oracle import fp4_oracle as o
+from gpu_util import announce, to_gpu_bf16, to_gpu_f32, to_gpu_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(xbits_or_f32, x_is_bf16, Wq, Ws, g_w, N, K, g_d, out_dtype):
+    xf = o.bf16_bits_to_f32(xbits_or_f32) if x_is_bf16 else xbits_or_f32
+    xg = to_gpu_bf16(xbits_or_f32) if x_is_bf16 else to_gpu_f32(xbits_or_f32)
+    gw = torch.tensor([g_w], dtype=torch.float32, device="cuda:0")
+    y = fp4.fp4_gemv_batched(xg, to_gpu_u8(Wq), to_gpu_u8(Ws), gw, K, g_d, out_dtype)
+    y_ref, mag = o.gemv_ref(xf, Wq, Ws, np.float32(g_w), g_d, K)
+    ok, err, bound = o.gemm_within_tolerance(y.float().cpu().numpy(), y_ref, mag,
+                                             out_bf16=out_dtype == torch.bfloat16)
+    assert ok, f"max err/bound = {np.max(err / np.maximum(bound, 1e-300))}"
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 7, 16])
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 512), (256, 1056), (300, 5120)])
+def test_gemv_small_matches_oracle(B, N, K):
+    announce(f"gemv B={B} N={N} K={K}")
+    Wb = workloads.gemv_weight(N, K, seed=40 + N)
+    Wq, Ws, _, g_w = o.nvfp4_quantize(o.bf16_bits_to_f32(Wb))
+    x = workloads.gemv_x(B, K, seed=50 + K)
+    _run_and_check(x, True, Wq, Ws, float(g_w), N, K, 1.0, torch.float32)
+    _run_and_check(x, True, Wq, Ws, float(g_w), N, K, 0.5, torch.bfloat16)
+    _run_and_check(o.bf16_bits_to_f32(x), False, Wq, Ws, float(g_w), N, K, 2.0, torch.float32)
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_gemv_decode_shape_all_outputs(B):
+    """W 27648x5120 (the decode GEMV shape) with random valid NVFP4 codes and
+    E4M3 scale bytes in [0x18, 0x58]; every one of the B x 27648 outputs checked."""
+    announce(f"gemv decode shape B={B}")
+    N, K = 27648, 5120
+    Wq = workloads.random_codes((N, K // 2), seed=61)
+    Ws = workloads.random_bytes((N, K // 16), 0x18, 0x58, seed=62)
+    x = workloads.gemv_x(B, K)
+    _run_and_check(x, True, Wq, Ws, 0.013, N, K, 1.0, torch.float32)
+    _run_and_check(x, True, Wq, Ws, 0.013, N, K, 1.0, torch.bfloat16)
