@@ -1,0 +1,392 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 / MXFP4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step runs every call of the hot path once per input copy, each at its
+workload's shape:
+  activation   8192x8192 bf16, N(0,1), 8 outlier channels x40:
+               nvfp4_quantize (dynamic amax), nvfp4_quantize (static amax),
+               mxfp4_quantize, NVFP4 and MXFP4 dequantize to bf16
+  decode GEMV  W 27648x5120 NVFP4, x bf16 [B, 5120] quantized on the fly, B = 1, 4, 16
+  prefill GEMM 8192 x 28672 x 8192, NVFP4 and MXFP4 operands, bf16 output
+  rotate       16384x8192 bf16, 16 outlier channels x60: FWHT-128 + NVFP4, RNE and SR
+Each call kind is captured in its own HIP graph of R back-to-back calls that
+cycle through input copies totalling >= 1 GiB (more than the 256 MiB Infinity
+Cache), so consecutive calls never find their inputs in cache and no host
+launch overhead is timed.  HIP events on the capture/replay stream bracket
+every replay.
+
+The printed JSON line's `value` is the NVFP4 quantize throughput (dynamic
+amax) on the activation workload in GB/s of algorithmic bytes (input read
+once + codes + scales); every other call is reported under `components`.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}
+GiB = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--only", default="", help="comma list of call names to run (profiling)")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ helpers --
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "micro_scaled_fp4_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM traffic per launch measured by rocprofv3 counters (profiles/traffic.json),
+    used only while the kernel source it was measured on is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        return json.load(f)
+
+
+class Op:
+    """One call kind: R calls captured in a graph, cycling over input copies."""
+
+    def __init__(self, name, launch, n_copies, unit, per_call, peak, bound, kernel, src):
+        self.name, self.launch, self.n = name, launch, n_copies
+        self.unit, self.per_call, self.peak, self.bound = unit, per_call, peak, bound
+        self.kernel, self.src = kernel, src
+        self.graph = None
+        self.times_ms = []
+
+    def capture(self, torch):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(self.n):          # eager warm-up (first-call setup outside capture)
+                self.launch(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for i in range(self.n):
+                self.launch(i)
+        torch.cuda.synchronize()
+
+    def replay_timed(self, torch):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.graph.replay()
+        e1.record()
+        return e0, e1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "part of it (see the sharding notes in DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import micro_scaled_fp4_amd as fp4
+    import workloads
+
+    lib = fp4.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    only = set(filter(None, args.only.split(",")))
+    stream_of = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def bf16_from_bits(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def copies(t, total_bytes=GiB):
+        n = max(2, -(-total_bytes // (t.numel() * t.element_size())))
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    ops = []
+    t_setup = time.time()
+
+    # ---------------------------------------------------------- activation --
+    R_A, C_A = 8192, 8192
+    xa = bf16_from_bits(workloads.activation(R_A, C_A))
+    xa_c = copies(xa)
+    nA = len(xa_c)
+    q_nv = [torch.empty((R_A, C_A // 2), dtype=torch.uint8, device=dev) for _ in range(nA)]
+    s_nv = [torch.empty((R_A, C_A // 16), dtype=torch.uint8, device=dev) for _ in range(nA)]
+    amax = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nA)]
+    gsc = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nA)]
+    wsp = [torch.empty(fp4.AMAX_WORKSPACE_BYTES, dtype=torch.uint8, device=dev) for _ in range(nA)]
+    static_amax = torch.tensor([float(xa.float().abs().max())], dtype=torch.float32, device=dev)
+    q_mx = [torch.empty((R_A, C_A // 2), dtype=torch.uint8, device=dev) for _ in range(nA)]
+    s_mx = [torch.empty((R_A, C_A // 32), dtype=torch.uint8, device=dev) for _ in range(nA)]
+    y_bf = torch.empty((R_A, C_A), dtype=torch.bfloat16, device=dev)
+    elems = R_A * C_A
+    b_nv = elems * 2 + elems // 2 + elems // 16 + 8
+    b_mx = elems * 2 + elems // 2 + elems // 32
+
+    def nv_dyn(i):
+        st = lib.nvfp4_quantize(P(xa_c[i]), fp4.FP4_BF16, R_A, C_A, P(q_nv[i]), P(s_nv[i]), P(amax[i]),
+                                0, P(gsc[i]), P(wsp[i]), fp4.AMAX_WORKSPACE_BYTES, stream_of())
+        assert st == 0, st
+
+    def nv_static(i):
+        st = lib.nvfp4_quantize(P(xa_c[i]), fp4.FP4_BF16, R_A, C_A, P(q_nv[i]), P(s_nv[i]),
+                                P(static_amax), 1, P(gsc[i]), None, 0, stream_of())
+        assert st == 0, st
+
+    def mx_q(i):
+        st = lib.mxfp4_quantize(P(xa_c[i]), fp4.FP4_BF16, R_A, C_A, P(q_mx[i]), P(s_mx[i]), stream_of())
+        assert st == 0, st
+
+    def nv_deq(i):
+        st = lib.fp4_dequantize(fp4.FP4_NVFP4, P(q_nv[i]), P(s_nv[i]), P(gsc[i]), R_A, C_A, P(y_bf),
+                                fp4.FP4_BF16, stream_of())
+        assert st == 0, st
+
+    def mx_deq(i):
+        st = lib.fp4_dequantize(fp4.FP4_MXFP4, P(q_mx[i]), P(s_mx[i]), None, R_A, C_A, P(y_bf),
+                                fp4.FP4_BF16, stream_of())
+        assert st == 0, st
+
+    qsrc = _src_hash("quantize.hip", "fp4_device.h")
+    ops += [
+        Op("nvfp4_quantize_dynamic", nv_dyn, nA, "GB/s", b_nv, HBM_PEAK_GBS, "hbm",
+           "k_amax + k_nv_quant_fast", qsrc),
+        Op("nvfp4_quantize_static", nv_static, nA, "GB/s", b_nv, HBM_PEAK_GBS, "hbm",
+           "k_nv_quant_fast", qsrc),
+        Op("mxfp4_quantize", mx_q, nA, "GB/s", b_mx, HBM_PEAK_GBS, "hbm", "k_mx_quant_fast", qsrc),
+        Op("nvfp4_dequantize_bf16", nv_deq, nA, "GB/s", b_nv - 4, HBM_PEAK_GBS, "hbm",
+           "k_nv_dequant_fast", qsrc),
+        Op("mxfp4_dequantize_bf16", mx_deq, nA, "GB/s", b_mx, HBM_PEAK_GBS, "hbm",
+           "k_mx_dequant_fast", qsrc),
+    ]
+
+    # --------------------------------------------------------- decode GEMV --
+    Nv, Kv = 27648, 5120
+    wv = bf16_from_bits(workloads.gemv_weight(Nv, Kv))
+    wq0, ws0, _, gw0 = fp4.nvfp4_quantize(wv)
+    del wv
+    w_bytes = wq0.numel() + ws0.numel() + 4
+    nG = max(2, -(-GiB // w_bytes))
+    Wq = [wq0] + [wq0.clone() for _ in range(nG - 1)]
+    Wsc = [ws0] + [ws0.clone() for _ in range(nG - 1)]
+    gsrc = _src_hash("gemv.hip", "fp4_device.h")
+    for B in (1, 4, 16):
+        xv = bf16_from_bits(workloads.gemv_x(B, Kv))
+        yv = torch.empty((B, Nv), dtype=torch.bfloat16, device=dev)
+        wsz = fp4.gemv_workspace_bytes(B, Kv)
+        wsv = torch.empty(wsz, dtype=torch.uint8, device=dev)
+
+        def gemv(i, xv=xv, yv=yv, wsv=wsv, wsz=wsz, B=B):
+            st = lib.fp4_gemv_batched(P(xv), fp4.FP4_BF16, B, P(Wq[i]), P(Wsc[i]), P(gw0), Nv, Kv,
+                                      1.0, P(yv), fp4.FP4_BF16, P(wsv), wsz, stream_of())
+            assert st == 0, st
+
+        ops.append(Op(f"gemv_b{B}", gemv, nG, "GB/s", w_bytes + B * Kv * 2 + B * Nv * 2,
+                      HBM_PEAK_GBS, "hbm", "k_gemv_xquant + k_gemv", gsrc))
+
+    # -------------------------------------------------------- prefill GEMM --
+    Mg, Ng, Kg = 8192, 28672, 8192
+    ga_bits = workloads.gemm_a(Mg, Kg)
+    aq_nv, as_nv, _, ga_nv = fp4.nvfp4_quantize(bf16_from_bits(ga_bits))
+    aq_mx, as_mx = fp4.mxfp4_quantize(bf16_from_bits(ga_bits))
+    del ga_bits
+    gw_bits = workloads.gemm_w(Ng, Kg)
+    wt = bf16_from_bits(gw_bits)
+    del gw_bits
+    wq_nv, wsc_nv, _, gw_nv = fp4.nvfp4_quantize(wt)
+    wq_mx, wsc_mx = fp4.mxfp4_quantize(wt)
+    del wt
+    Dg = torch.empty((Mg, Ng), dtype=torch.bfloat16, device=dev)
+    flops = 2 * Mg * Ng * Kg
+    msrc = _src_hash("gemm.hip", "fp4_device.h")
+
+    def gemm_nv(i):
+        st = lib.fp4_scaled_gemm(fp4.FP4_NVFP4, P(aq_nv), P(as_nv), P(ga_nv), P(wq_nv), P(wsc_nv),
+                                 P(gw_nv), 1.0, Mg, Ng, Kg, P(Dg), fp4.FP4_BF16, stream_of())
+        assert st == 0, st
+
+    def gemm_mx(i):
+        st = lib.fp4_scaled_gemm(fp4.FP4_MXFP4, P(aq_mx), P(as_mx), None, P(wq_mx), P(wsc_mx), None,
+                                 1.0, Mg, Ng, Kg, P(Dg), fp4.FP4_BF16, stream_of())
+        assert st == 0, st
+
+    ops += [
+        Op("gemm_nvfp4", gemm_nv, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp16"], "mfma",
+           "k_gemm<NV> (fp16 MFMA after exact in-register dequant)", msrc),
+        Op("gemm_mxfp4", gemm_mx, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp4"], "mfma",
+           "k_gemm<MX> (scaled FP4 MFMA)", msrc),
+    ]
+
+    # -------------------------------------------------------------- rotate --
+    R_H, C_H = 16384, 8192
+    xh = bf16_from_bits(workloads.rotate_input(R_H, C_H))
+    xh_c = copies(xh)
+    nH = len(xh_c)
+    qh = torch.empty((R_H, C_H // 2), dtype=torch.uint8, device=dev)
+    sh = torch.empty((R_H, C_H // 16), dtype=torch.uint8, device=dev)
+    ah = torch.empty(1, dtype=torch.float32, device=dev)
+    gh = torch.empty(1, dtype=torch.float32, device=dev)
+    wh = torch.empty(fp4.AMAX_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    eh = R_H * C_H
+    b_h = eh * 2 + eh // 2 + eh // 16 + 8
+    hsrc = _src_hash("hadamard.hip", "fp4_device.h")
+    for mode, nm in ((fp4.FP4_RNE, "rne"), (fp4.FP4_SR, "sr")):
+        def had(i, mode=mode):
+            st = lib.hadamard_quantize(P(xh_c[i]), fp4.FP4_BF16, R_H, C_H, 128, mode,
+                                       ctypes.c_uint64(workloads.SEED_SR), P(qh), P(sh), P(ah), 0,
+                                       P(gh), P(wh), fp4.AMAX_WORKSPACE_BYTES, stream_of())
+            assert st == 0, st
+        ops.append(Op(f"hadamard_quantize_{nm}", had, nH, "GB/s", b_h, HBM_PEAK_GBS, "hbm",
+                      "k_had_amax + k_had_quant", hsrc))
+
+    if only:
+        ops = [op for op in ops if op.name in only]
+    setup_s = time.time() - t_setup
+
+    # ------------------------------------------------------------- capture --
+    for op in ops:
+        op.capture(torch)
+    # graph replays reproduce the eager result (checked on the dynamic quantize)
+    if any(op.name == "nvfp4_quantize_dynamic" for op in ops):
+        ref = [t.clone() for t in (q_nv[0], s_nv[0], amax[0], gsc[0])]
+        q_nv[0].zero_()
+        next(op for op in ops if op.name == "nvfp4_quantize_dynamic").graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (q_nv[0], s_nv[0], amax[0], gsc[0])):
+            assert torch.equal(a, b), "graph replay differs from eager result"
+
+    # ------------------------------------------------------------- warm-up --
+    for _ in range(args.warmup):
+        for op in ops:
+            op.graph.replay()
+    torch.cuda.synchronize()
+
+    # --------------------------------------------------------- timed steps --
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for op in ops:
+            events.append((op, *op.replay_timed(torch)))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for op, e0, e1 in events:
+        op.times_ms.append(e0.elapsed_time(e1) / op.n)
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+
+    traffic = load_traffic()
+    comps = {}
+    for op in ops:
+        t_ms = float(np.mean(op.times_ms))
+        if op.unit == "GB/s":
+            achieved = op.per_call / (t_ms * 1e-3) / 1e9
+        else:
+            achieved = op.per_call / (t_ms * 1e-3) / 1e12
+        tr = traffic.get(op.name)
+        tr_bytes = tr["bytes_per_call"] if tr and tr.get("src") == op.src else None
+        comps[op.name] = {
+            "us_per_call": round(t_ms * 1e3, 2),
+            "us_p10": round(float(np.percentile(op.times_ms, 10)) * 1e3, 2),
+            "us_p90": round(float(np.percentile(op.times_ms, 90)) * 1e3, 2),
+            "achieved": round(achieved, 1), "unit": op.unit, "peak": op.peak,
+            "frac": round(achieved / op.peak, 4), "bound": op.bound,
+            ("bytes_per_call" if op.unit == "GB/s" else "flop_per_call"): op.per_call,
+            "kernels": op.kernel, "calls_per_replay": op.n, "traffic": tr_bytes,
+        }
+        if op.name == "gemm_nvfp4":
+            comps[op.name]["frac_of_fp4_peak"] = round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4)
+
+    head = comps.get("nvfp4_quantize_dynamic") or next(iter(comps.values()))
+    enc = comps.get("nvfp4_quantize_static", head)
+    result = {
+        "metric": "NVFP4 quantize GB/s; FP4 scaled-GEMM TFLOPS; GEMV GB/s (% roofline)",
+        "value": head["achieved"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, e2m1+e4m3 out",
+        "data": "synthetic (seeded)",
+        "config": {
+            "workload": "activation quantization: bf16 8192x8192, N(0,1), 8 outlier channels x40, "
+                        "nvfp4_quantize with dynamic (computed) amax",
+            "rows": R_A, "cols": C_A,
+            "value_bytes_per_call": b_nv,
+            "step_also_runs": "mxfp4_quantize, NV/MX dequantize (8192x8192); GEMV W 27648x5120 "
+                              "B=1,4,16; GEMM 8192x28672x8192 NVFP4 and MXFP4; FWHT+NVFP4 "
+                              "16384x8192 RNE and SR",
+        },
+        "roofline": {
+            "kernel": "k_nv_quant_fast (NVFP4 encode pass; timed alone as the static-amax call)",
+            "bound": "hbm", "achieved": enc["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(enc["achieved"] / HBM_PEAK_GBS, 4), "traffic": enc["traffic"],
+            "algorithmic_bytes_per_launch": b_nv,
+            "avg_launch_us": enc["us_per_call"],
+        },
+        "components": comps,
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu_baseline and (not only or "nvfp4_quantize_dynamic" in only):
+        result["cpu_baseline"] = cpu_baseline(xa, args.cpu_seconds, b_nv / elems)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(xa, seconds, bytes_per_elem):
+    """The CPU oracle's nvfp4_quantize (plain NumPy, single thread for the
+    element-wise work) on 256-row slices of the activation tensor, at the full
+    tensor's amax, repeated for about `seconds`."""
+    import torch
+    from oracle import fp4_oracle as o
+
+    bits = xa[:2048].cpu().view(torch.int16).numpy().view(np.uint16)
+    G = float(xa.float().abs().max())
+    xf = o.bf16_bits_to_f32(bits)
+    n_el = 0
+    t0 = time.perf_counter()
+    r = 0
+    while time.perf_counter() - t0 < seconds:
+        o.nvfp4_quantize(xf[r:r + 256], amax=G)
+        n_el += 256 * xf.shape[1]
+        r = (r + 256) % 2048
+    dt = time.perf_counter() - t0
+    return {"value": round(n_el * bytes_per_elem / dt / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{n_el // xf.shape[1]} rows (256-row slices of the first 2048 rows) of the "
+                      f"8192x8192 activation, nvfp4_quantize at the full tensor's amax, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+"""GPU parity: block-scaled FP4 GEMM (NVFP4 and MXFP4) against the float64 oracle.
+
+Pass rule: |D - D_ref| <= 1e-5 * |g_d| * sum_k |A_hat_mk * W_hat_nk| for float32
+output, plus one bf16 rounding of D_ref for bf16 output.  Small shapes span
+several 256x256 tiles with ragged M/N edges and K tails; the prefill shape
+(8192 x 28672 x 8192) is checked on sampled entries, two full rows, two full
+columns and one 128x128 tile.
+"""
+import numpy as np
+import pytest
+import torch
+
+import micro_scaled_fp4_amd as fp4
+import workloads
+from oracle import fp4_oracle as o
+from gpu_util import announce, to_gpu_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(fmt, M, N, K, seed, quantized_from=None):
+    """Oracle-made operands: NVFP4/MXFP4 quantization of seeded bf16 data, or
+    (for the big shape) uniformly random valid codes and scale bytes."""
+    if quantized_from is not None:
+        Af, Wf = quantized_from
+        if fmt == "nv":
+            qa, sa, _, ga = o.nvfp4_quantize(Af)
+            qw, sw, _, gw = o.nvfp4_quantize(Wf)
+            return qa, sa, np.float32(ga), qw, sw, np.float32(gw)
+        qa, sa = o.mxfp4_quantize(Af)
+        qw, sw = o.mxfp4_quantize(Wf)
+        return qa, sa, None, qw, sw, None
+    qa = workloads.random_codes((M, K // 2), seed)
+    qw = workloads.random_codes((N, K // 2), seed + 1)
+    if fmt == "nv":
+        sa = workloads.random_bytes((M, K // 16), 0x20, 0x50, seed + 2)
+        sw = workloads.random_bytes((N, K // 16), 0x20, 0x50, seed + 3)
+        return qa, sa, np.float32(0.75), qw, sw, np.float32(0.0625)
+    sa = workloads.random_bytes((M, K // 32), 120, 134, seed + 2)
+    sw = workloads.random_bytes((N, K // 32), 120, 134, seed + 3)
+    return qa, sa, None, qw, sw, None
+
+
+def _hat(fmt, q, s, g, K, rows=None):
+    if rows is not None:
+        q, s = q[rows], s[rows]
+    return o.nv_operand_f64(q, s, g, K) if fmt == "nv" else o.mx_operand_f64(q, s, K)
+
+
+def _gpu_gemm(fmt, ops, K, g_d, out_dtype):
+    qa, sa, ga, qw, sw, gw = ops
+    f = fp4.FP4_NVFP4 if fmt == "nv" else fp4.FP4_MXFP4
+    tga = None if ga is None else torch.tensor([ga], dtype=torch.float32, device="cuda:0")
+    tgw = None if gw is None else torch.tensor([gw], dtype=torch.float32, device="cuda:0")
+    return fp4.fp4_scaled_gemm(f, to_gpu_u8(qa), to_gpu_u8(sa), tga, to_gpu_u8(qw), to_gpu_u8(sw),
+                               tgw, K, g_d, out_dtype)
+
+
+def _check(D, fmt, ops, K, g_d, out_bf16, rows=None, cols=None):
+    qa, sa, ga, qw, sw, gw = ops
+    Ah = _hat(fmt, qa, sa, 1.0 if ga is None else ga, K, rows)
+    Wh = _hat(fmt, qw, sw, 1.0 if gw is None else gw, K, cols)
+    ref, mag = o.scaled_gemm_ref(Ah, Wh, g_d)
+    ok, err, bound = o.gemm_within_tolerance(D, ref, mag, out_bf16)
+    assert ok, f"max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
+def test_gemm_tiny_reference_config(fmt):
+    """A, W fp32 64x256 ~ N(0,1) with 1% of entries x50, quantized (NVFP4 or
+    MXFP4), D = A_hat @ W_hat^T (64x64)."""
+    announce(f"gemm tiny {fmt}")
+    A, W = workloads.tiny_pair()
+    ops = _operands(fmt, 64, 64, 256, 0, quantized_from=(A, W))
+    for out in (torch.float32, torch.bfloat16):
+        D = _gpu_gemm(fmt, ops, 256, 1.0, out)
+        _check(D.float().cpu().numpy(), fmt, ops, 256, 1.0, out == torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (17, 33, 96), (256, 256, 128), (100, 300, 384),
+                                   (300, 520, 4096), (513, 257, 1056)])
+def test_gemm_small_shapes(fmt, M, N, K):
+    announce(f"gemm {fmt} {M}x{N}x{K}")
+    A = o.bf16_bits_to_f32(workloads.gemm_a(M, K, seed=70 + M))
+    W = o.bf16_bits_to_f32(workloads.gemm_w(N, K, seed=71 + N))
+    ops = _operands(fmt, M, N, K, 0, quantized_from=(A, W))
+    D = _gpu_gemm(fmt, ops, K, 1.0, torch.float32)
+    _check(D.cpu().numpy(), fmt, ops, K, 1.0, False)
+    D = _gpu_gemm(fmt, ops, K, -2.5, torch.bfloat16)
+    _check(D.float().cpu().numpy(), fmt, ops, K, -2.5, True)
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
+def test_gemm_unit_scales_exact(fmt):
+    """All block scales 1 and g = 1: every product is a multiple of 1/4 and the
+    float32 sums stay exact, so D must equal the integer matmul exactly."""
+    announce(f"gemm exact {fmt}")
+    M, N, K = 300, 200, 2048
+    qa = workloads.random_codes((M, K // 2), 81)
+    qw = workloads.random_codes((N, K // 2), 82)
+    one = 0x38 if fmt == "nv" else 127
+    bs = 16 if fmt == "nv" else 32
+    sa = np.full((M, K // bs), one, np.uint8)
+    sw = np.full((N, K // bs), one, np.uint8)
+    g = np.float32(1.0) if fmt == "nv" else None
+    ops = (qa, sa, g, qw, sw, g)
+    D = _gpu_gemm(fmt, ops, K, 1.0, torch.float32).cpu().numpy()
+    ref, _ = o.scaled_gemm_ref(_hat(fmt, qa, sa, 1.0, K), _hat(fmt, qw, sw, 1.0, K), 1.0)
+    assert np.array_equal(D.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
+def test_gemm_prefill_shape_sampled(fmt):
+    """8192 x 28672 x 8192 with random valid codes and scale bytes; bf16 output
+    (the timed configuration) checked on 4096 random entries, 2 full rows, 2 full
+    columns and one 128x128 tile."""
+    announce(f"gemm prefill {fmt}")
+    M, N, K = 8192, 28672, 8192
+    ops = _operands(fmt, M, N, K, 91 if fmt == "nv" else 92)
+    D = _gpu_gemm(fmt, ops, K, 1.0, torch.bfloat16)
+    rng = np.random.default_rng(93)
+    ii = rng.integers(0, M, 4096)
+    jj = rng.integers(0, N, 4096)
+    Dn = D[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()].float().cpu().numpy()
+    qa, sa, ga, qw, sw, gw = ops
+    Ah = _hat(fmt, qa, sa, 1.0 if ga is None else ga, K, ii)
+    Wh = _hat(fmt, qw, sw, 1.0 if gw is None else gw, K, jj)
+    ref = np.sum(Ah * Wh, axis=1)
+    mag = np.sum(np.abs(Ah * Wh), axis=1)
+    ok, err, bound = o.gemm_within_tolerance(Dn, ref, mag, True)
+    assert ok, f"sampled entries: max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
+    rows = np.array([0, 5003])
+    cols = np.array([7, 28671])
+    _check(D[torch.from_numpy(rows).cuda()].float().cpu().numpy(), fmt, ops, K, 1.0, True, rows=rows)
+    _check(D[:, torch.from_numpy(cols).cuda()].float().cpu().numpy(), fmt, ops, K, 1.0, True, cols=cols)
+    r0, c0 = 4096 + 64, 20480 + 96
+    tr, tc = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
+    _check(D[r0:r0 + 128, c0:c0 + 128].float().cpu().numpy(), fmt, ops, K, 1.0, True, rows=tr, cols=tc)
