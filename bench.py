@@ -302,6 +302,19 @@ def main():
         op.times_ms.append(e0.elapsed_time(e1) / op.n)
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
 
+    # context: a plain device copy of 1 GiB (read + write) on the same GPU
+    src = torch.empty(GiB // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
     traffic = load_traffic()
     comps = {}
     for op in ops:
@@ -356,6 +369,8 @@ def main():
             "avg_launch_us": enc["us_per_call"],
         },
         "components": comps,
+        "context": {"device_copy_GBs_read_plus_write": round(copy_gbs, 1),
+                    "note": "torch copy_ of 512 MiB, for reference against the 8 TB/s peak"},
         "setup_s": round(setup_s, 1),
     }
 

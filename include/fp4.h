@@ -145,6 +145,7 @@ size_t fp4_gemv_workspace_bytes(int64_t B, int64_t K);
  *   W   NVFP4 [N, K/2] + w_scales [N, K/16] + g_w (device float);
  *   y   out [B, N] float32 or bf16.  1 <= B <= 16, K % 32 == 0.
  *   workspace  >= fp4_gemv_workspace_bytes(B, K) bytes (holds quantized x).
+ * x, W and workspace must be 16-byte aligned, w_scales 2-byte aligned (FP4_ERR_ALIGN).
  * Accuracy as for fp4_scaled_gemm.
  */
 fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_t* W,
@@ -168,7 +169,8 @@ fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_
  *     Philox4x32-10 (Salmon et al., SC'11) with key (seed low, seed high) and
  *     counter (i/8 low, i/8 high, 0, 0) for flat element index i, taking word
  *     (i%8)/2, low half for even i%8, high half for odd.
- *   cols % group == 0; group must be 128.
+ *   cols % group == 0; group must be 128.  x and q must be 16-byte aligned,
+ *   scales 2-byte aligned (FP4_ERR_ALIGN).
  * Outputs and workspace as nvfp4_quantize.
  */
 fp4_status hadamard_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, int group,

@@ -189,7 +189,7 @@ fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_
     return FP4_ERR_NULL;
   if (workspace == nullptr || workspace_bytes < fp4impl::gemv_workspace_bytes(B, K))
     return FP4_ERR_WORKSPACE;
-  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(workspace, 16) ||
+  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(w_scales, 2) ||
       !aligned(y, yt == FP4_BF16 ? 2 : 4))
     return FP4_ERR_ALIGN;
   fp4_status st = check_arch();
@@ -210,7 +210,7 @@ fp4_status hadamard_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t 
   fp4_status st = check_quant_args(x, xt, rows, cols, q, scales, global_amax, amax_given,
                                    global_scale, workspace, workspace_bytes);
   if (st != FP4_OK) return st;
-  if (rows != 0 && cols != 0 && (!aligned(x, 16) || !aligned(q, 16)))
+  if (rows != 0 && cols != 0 && (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 2)))
     return FP4_ERR_ALIGN;
   if ((st = check_arch()) != FP4_OK) return st;
   const bool bf16 = xt == FP4_BF16;

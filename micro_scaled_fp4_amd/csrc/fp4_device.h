@@ -40,6 +40,26 @@ __device__ __forceinline__ uint32_t e2m1_code(float q) {
   return c | ((u >> 28) & 8u);
 }
 
+// The gfx950 conversion v_cvt_scalef32_pk_fp4_f32 with scale 1.0 encodes two
+// float32 values with exactly the rounding of e2m1_code (nearest, ties to the
+// even code, saturating at 6, sign kept, denormals included); it writes the
+// byte (first value in the low nibble) selected by SEL of `old`.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float q0, float q1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, 1.0f, SEL);
+}
+
+// Eight float32 values -> one dword of packed codes (value 2j in the low
+// nibble of byte j).
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* q) {
+  uint32_t d = 0;
+  d = e2m1_pack2<0>(d, q[0], q[1]);
+  d = e2m1_pack2<1>(d, q[2], q[3]);
+  d = e2m1_pack2<2>(d, q[4], q[5]);
+  d = e2m1_pack2<3>(d, q[6], q[7]);
+  return d;
+}
+
 // Value of a 4-bit code as float32.
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
   uint32_t e = (c >> 1) & 3u, m = c & 1u;
@@ -97,6 +117,31 @@ __device__ __forceinline__ uint32_t e8m0_code(uint32_t abits) {
 __device__ __forceinline__ float e8m0_inv(uint32_t code) { return __uint_as_float((254u - code) << 23); }
 __device__ __forceinline__ float e8m0_value(uint32_t code) {
   return code ? __uint_as_float(code << 23) : 0x1p-127f;
+}
+
+// ------------------------------------------------------------ LDS staging --
+// Loads the VPB 16-byte vectors of each of the nb (<= NT) blocks starting at
+// block `base` (each block VPB consecutive vectors) with coalesced 128-bit
+// loads (lane i of a wave reads bytes [16i, 16i+16) of a contiguous run), and
+// hands thread t the vectors of block base + t.  Array k of the LDS buffer
+// (VPB * (NT + 1) vectors) holds vector k of every block; the arrays are skewed
+// by one vector so the writes of a 16-lane group hit distinct banks.  Every
+// thread of the workgroup must call it.
+template <int VPB, int NT>
+__device__ __forceinline__ void stage_blocks(const u32x4* __restrict__ src, int64_t base, int nb,
+                                             u32x4* lds, u32x4 (&out)[VPB]) {
+#pragma unroll
+  for (int k = 0; k < VPB; ++k) {
+    const int i = threadIdx.x + NT * k;
+    if (i < VPB * nb)
+      lds[(i % VPB) * (NT + 1) + i / VPB] = __builtin_nontemporal_load(src + base * VPB + i);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nb) {
+#pragma unroll
+    for (int k = 0; k < VPB; ++k) out[k] = lds[k * (NT + 1) + threadIdx.x];
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------- wave reductions --

@@ -41,29 +41,26 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
   return r;
 }
 
+// 16-byte vectors of one slot (32 channels) -> float32
 template <bool BF16>
-__device__ __forceinline__ void load32(const void* __restrict__ x, int64_t s, float (&v)[kPer]) {
+__device__ __forceinline__ void unpack32(const u32x4* w, float (&v)[kPer]) {
   if (BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(x) + 4 * s;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const u32x4 a = p[k];
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+      const uint32_t a[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[8 * k + 2 * j] = bf16_lo(w[j]);
-        v[8 * k + 2 * j + 1] = bf16_hi(w[j]);
+        v[8 * k + 2 * j] = bf16_lo(a[j]);
+        v[8 * k + 2 * j + 1] = bf16_hi(a[j]);
       }
     }
   } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(x) + 8 * s;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const f32x4 a = p[k];
-      v[4 * k] = a.x;
-      v[4 * k + 1] = a.y;
-      v[4 * k + 2] = a.z;
-      v[4 * k + 3] = a.w;
+      v[4 * k] = __uint_as_float(w[k].x);
+      v[4 * k + 1] = __uint_as_float(w[k].y);
+      v[4 * k + 2] = __uint_as_float(w[k].z);
+      v[4 * k + 3] = __uint_as_float(w[k].w);
     }
   }
 }
@@ -168,14 +165,21 @@ __device__ __forceinline__ uint32_t pack8(const uint32_t (&c)[8]) {
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
     k_had_amax(const void* __restrict__ x, int64_t nslots, uint32_t* __restrict__ partials) {
+  constexpr int VPB = BF16 ? 4 : 8;
+  __shared__ u32x4 lds[VPB * (kThreads + 1)];
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   const int p = threadIdx.x & 3;
   uint32_t m = 0;
-  // nslots and the slot stride are multiples of 4, so a quad enters and leaves
-  // the loop together (DPP partners are always active).
-  for (int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x; s < nslots;
-       s += (int64_t)gridDim.x * kThreads) {
+  // nslots and the chunk bases are multiples of 4, so the lanes of a quad are
+  // all active or all idle (DPP partners are always active).
+  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nslots;
+       base += (int64_t)gridDim.x * kThreads) {
+    const int nb = (int)(nslots - base < kThreads ? nslots - base : kThreads);
+    u32x4 w[VPB];
+    stage_blocks<VPB, kThreads>(xv, base, nb, lds, w);
+    if ((int)threadIdx.x >= nb) continue;
     float v[kPer];
-    load32<BF16>(x, s, v);
+    unpack32<BF16>(w, v);
     fwht128(v, p);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) m = umax(m, __float_as_uint(v[j]) & 0x7fffffffu);
@@ -203,12 +207,20 @@ __global__ void __launch_bounds__(kThreads)
     if (amax_out) *amax_out = G;
     *scale_out = s_global;
   }
+  constexpr int VPB = BF16 ? 4 : 8;
+  __shared__ u32x4 lds[VPB * (kThreads + 1)];
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   const int p = threadIdx.x & 3;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  for (int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x; s < nslots;
-       s += (int64_t)gridDim.x * kThreads) {
+  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nslots;
+       base += (int64_t)gridDim.x * kThreads) {
+    const int nb = (int)(nslots - base < kThreads ? nslots - base : kThreads);
+    u32x4 wv[VPB];
+    stage_blocks<VPB, kThreads>(xv, base, nb, lds, wv);
+    if ((int)threadIdx.x >= nb) continue;
+    const int64_t s = base + threadIdx.x;
     float v[kPer];
-    load32<BF16>(x, s, v);
+    unpack32<BF16>(wv, v);
     fwht128(v, p);
     uint32_t w[4];
     uint32_t sc[2];
@@ -221,9 +233,9 @@ __global__ void __launch_bounds__(kThreads)
       nv_block_scale(__uint_as_float(am), s_global, sc[blk], r);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        uint32_t c[8];
         const int base = 16 * blk + 8 * half;
         if (SR) {
+          uint32_t c[8];
           // elements 32s + base .. +7 share Philox counter (32s + base) / 8
           const uint64_t g = (uint64_t)(4 * s + 2 * blk + half);
           uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), 0u, 0u};
@@ -233,11 +245,13 @@ __global__ void __launch_bounds__(kThreads)
             const uint32_t u = (j & 1) ? (ctr[j >> 1] >> 16) : (ctr[j >> 1] & 0xffffu);
             c[j] = e2m1_code_sr(v[base + j] * r, u);
           }
+          w[2 * blk + half] = pack8(c);
         } else {
+          float qv[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) c[j] = e2m1_code(v[base + j] * r);
+          for (int j = 0; j < 8; ++j) qv[j] = v[base + j] * r;
+          w[2 * blk + half] = e2m1_pack8(qv);
         }
-        w[2 * blk + half] = pack8(c);
       }
     }
     reinterpret_cast<u32x4*>(q)[s] = u32x4{w[0], w[1], w[2], w[3]};

@@ -1,10 +1,14 @@
 // NVFP4 / MXFP4 quantization and dequantization kernels for gfx950.
 //
-// Layout: one lane owns one whole scale block (16 values for NVFP4, 32 for
-// MXFP4), so the block amax, the scale and the element codes need no cross-lane
-// traffic; a wave covers 64 consecutive blocks, i.e. 2 KiB (NV, bf16) of
-// contiguous input per pass, read with 128-bit loads, and writes 512 contiguous
-// code bytes with 64-bit stores.
+// Encode: one lane owns one whole scale block (16 values for NVFP4, 32 for
+// MXFP4), so the block amax, the scale and the codes need no cross-lane
+// traffic.  A workgroup stages 256 consecutive blocks through LDS: every global
+// load instruction is fully coalesced (lane i reads bytes [16i, 16i+16) of a
+// contiguous run), then each lane reads its own block back from LDS.  Codes are
+// written with 64/128-bit stores at consecutive lane addresses.
+//
+// Decode: one lane owns 8 output values (bf16: one 16-byte store) or 4 (float32:
+// one 16-byte store), so stores are fully coalesced too.
 //
 // The "fast" kernels treat the tensor as one flat run of blocks; they need
 // cols to be a multiple of the block and 16-byte aligned pointers.  The
@@ -18,20 +22,26 @@ using namespace fp4dev;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxGrid = 2048;  // 256 CUs x 8 workgroups, grid-stride beyond
+constexpr int kMaxGrid = 2048;      // 256 CUs x 8 workgroups, grid-stride beyond
+constexpr int kAmaxThreads = 512;   // amax pass: 1024 workgroups x 8 waves fill every CU
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 // Workgroup max of a u32 (every thread gets the result).
+template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
-  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t red[NT / 64];
   v = wave_max_u32(v);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
   uint32_t r = red[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = umax(r, red[i]);
+  for (int i = 1; i < NT / 64; ++i) r = umax(r, red[i]);
   __syncthreads();
   return r;
 }
@@ -42,64 +52,95 @@ __device__ __forceinline__ float resolve_amax(const float* amax_in, const uint32
   if (partials == nullptr) return *amax_in;
   uint32_t m = 0;
   for (int i = threadIdx.x; i < npart; i += kThreads) m = umax(m, partials[i]);
-  return __uint_as_float(block_max_u32(m));
+  return __uint_as_float(block_max_u32<>(m));
+}
+
+__device__ __forceinline__ u16x2 pkmax_abs(u16x2 m, uint32_t w) {
+  const uint32_t a = w & 0x7fff7fffu;
+  u16x2 av;
+  __builtin_memcpy(&av, &a, 4);
+  return __builtin_elementwise_max(m, av);
+}
+
+template <int N>
+__device__ __forceinline__ void unpack_bf16(const u32x4* w, float (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N / 8; ++k) {
+    const uint32_t a[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * k + 2 * j] = bf16_lo(a[j]);
+      v[8 * k + 2 * j + 1] = bf16_hi(a[j]);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void unpack_f32(const u32x4* w, float (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N / 4; ++k) {
+    v[4 * k] = __uint_as_float(w[k].x);
+    v[4 * k + 1] = __uint_as_float(w[k].y);
+    v[4 * k + 2] = __uint_as_float(w[k].z);
+    v[4 * k + 3] = __uint_as_float(w[k].w);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ float amax_of(const float (&v)[N]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) m = umax(m, __float_as_uint(v[j]) & 0x7fffffffu);
+  return __uint_as_float(m);
 }
 
 // ------------------------------------------------------------------ amax --
+// Per-workgroup max|x| over a contiguous range of 16-byte vectors, four
+// vectors in flight per thread; bf16 pairs are reduced with packed u16 max on
+// their magnitude bits (same order as the values).
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, int64_t n,
-                                                   uint32_t* __restrict__ partials) {
+__global__ void __launch_bounds__(kAmaxThreads) k_amax(const void* __restrict__ x, int64_t n,
+                                                       uint32_t* __restrict__ partials) {
   constexpr int kPer = BF16 ? 8 : 4;  // elements per 16-byte vector
   const int64_t nvec = n / kPer;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  uint32_t m0 = 0, m1 = 0;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < nvec; i += 4 * stride) {
+  const int64_t chunk = ((nvec + gridDim.x - 1) / gridDim.x + 4 * kAmaxThreads - 1) /
+                        (4 * kAmaxThreads) * (4 * kAmaxThreads);
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < nvec ? lo + chunk : nvec;
+  u16x2 mh = {0, 0};
+  uint32_t mf = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 4 * kAmaxThreads) {
     u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = xv[i + u * stride];
+    for (int u = 0; u < 4; ++u)
+      v[u] = (i + u * kAmaxThreads < hi) ? __builtin_nontemporal_load(xv + i + u * kAmaxThreads)
+                                         : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (BF16) {
-          const uint32_t a = w[j] & 0x7fff7fffu;
-          m0 = umax(m0, a & 0xffffu);
-          m1 = umax(m1, a >> 16);
-        } else {
-          m0 = umax(m0, w[j] & 0x7fffffffu);
-        }
-      }
-    }
-  }
-  for (; i < nvec; i += stride) {
-    const u32x4 v = xv[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
       if (BF16) {
-        const uint32_t a = w[j] & 0x7fff7fffu;
-        m0 = umax(m0, a & 0xffffu);
-        m1 = umax(m1, a >> 16);
+        mh = pkmax_abs(mh, v[u].x);
+        mh = pkmax_abs(mh, v[u].y);
+        mh = pkmax_abs(mh, v[u].z);
+        mh = pkmax_abs(mh, v[u].w);
       } else {
-        m0 = umax(m0, w[j] & 0x7fffffffu);
+        mf = umax(mf, umax(umax(v[u].x & 0x7fffffffu, v[u].y & 0x7fffffffu),
+                           umax(v[u].z & 0x7fffffffu, v[u].w & 0x7fffffffu)));
       }
     }
   }
+  uint32_t m0 = BF16 ? (uint32_t)(mh.x > mh.y ? mh.x : mh.y) : 0u;
   // tail elements (n not a multiple of the vector)
   if (blockIdx.x == 0) {
-    for (int64_t t = nvec * kPer + threadIdx.x; t < n; t += kThreads) {
-      if (BF16) {
+    for (int64_t t = nvec * kPer + threadIdx.x; t < n; t += kAmaxThreads) {
+      if (BF16)
         m0 = umax(m0, (uint32_t)(reinterpret_cast<const uint16_t*>(x)[t] & 0x7fffu));
-      } else {
-        m0 = umax(m0, reinterpret_cast<const uint32_t*>(x)[t] & 0x7fffffffu);
-      }
+      else
+        mf = umax(mf, reinterpret_cast<const uint32_t*>(x)[t] & 0x7fffffffu);
     }
   }
-  uint32_t m = BF16 ? (umax(m0, m1) << 16) : m0;
-  m = block_max_u32(m);
+  uint32_t m = BF16 ? (m0 << 16) : mf;
+  m = block_max_u32<kAmaxThreads>(m);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
@@ -115,82 +156,47 @@ __global__ void __launch_bounds__(kThreads) k_amax_scalar(const void* __restrict
     else
       m = umax(m, reinterpret_cast<const uint32_t*>(x)[t] & 0x7fffffffu);
   }
-  m = block_max_u32(m);
+  m = block_max_u32<>(m);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
 // ------------------------------------------------------------ NV quantize --
-// Loads the 16 values of block b as float32.
-template <bool BF16>
-__device__ __forceinline__ void load16(const void* __restrict__ x, int64_t b, float (&v)[16]) {
-  if (BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(x) + 2 * b;
-    const u32x4 a = p[0], c = p[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[2 * j] = bf16_lo(w[j]);
-      v[2 * j + 1] = bf16_hi(w[j]);
-    }
-  } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(x) + 4 * b;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 a = p[j];
-      v[4 * j] = a.x;
-      v[4 * j + 1] = a.y;
-      v[4 * j + 2] = a.z;
-      v[4 * j + 3] = a.w;
-    }
-  }
-}
-
-template <int N>
-__device__ __forceinline__ float amax_of(const float (&v)[N]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < N; ++j) m = umax(m, __float_as_uint(v[j]) & 0x7fffffffu);
-  return __uint_as_float(m);
-}
-
-// Packs 8 codes (element 2j low nibble of byte j).
-__device__ __forceinline__ uint32_t pack8(const uint32_t (&c)[8]) {
-  return c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) | (c[5] << 20) |
-         (c[6] << 24) | (c[7] << 28);
-}
-
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
     k_nv_quant_fast(const void* __restrict__ x, int64_t nblk, uint8_t* __restrict__ q,
                     uint8_t* __restrict__ scales, const float* __restrict__ amax_in,
                     const uint32_t* __restrict__ partials, int npart, float* __restrict__ amax_out,
                     float* __restrict__ scale_out) {
+  constexpr int VPB = BF16 ? 2 : 4;
+  __shared__ u32x4 lds[VPB * (kThreads + 1)];
   const float G = resolve_amax(amax_in, partials, npart);
   const float s_global = nv_global_scale(G);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (amax_out) *amax_out = G;
     *scale_out = s_global;
   }
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
-       b += (int64_t)gridDim.x * kThreads) {
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblk;
+       base += (int64_t)gridDim.x * kThreads) {
+    const int nb = (int)(nblk - base < kThreads ? nblk - base : kThreads);
+    u32x4 w[VPB];
+    stage_blocks<VPB, kThreads>(xv, base, nb, lds, w);
+    if ((int)threadIdx.x >= nb) continue;
     float v[16];
-    load16<BF16>(x, b, v);
+    if (BF16) unpack_bf16<16>(w, v); else unpack_f32<16>(w, v);
     uint32_t sc;
     float r;
     nv_block_scale(amax_of(v), s_global, sc, r);
-    uint32_t c[8], d[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      c[j] = e2m1_code(v[j] * r);
-      d[j] = e2m1_code(v[8 + j] * r);
-    }
-    reinterpret_cast<u32x2*>(q)[b] = u32x2{pack8(c), pack8(d)};
+    for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
+    const int64_t b = base + threadIdx.x;
+    reinterpret_cast<u32x2*>(q)[b] = u32x2{e2m1_pack8(v), e2m1_pack8(v + 8)};
     scales[b] = (uint8_t)sc;
   }
 }
 
 // Any shape / alignment: one thread per (row, block).
-template <bool BF16, int BS>
+template <bool BF16>
 __device__ __forceinline__ float load_elem(const void* x, int64_t idx) {
   if (BF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[idx] << 16);
   return reinterpret_cast<const float*>(x)[idx];
@@ -217,14 +223,14 @@ __global__ void __launch_bounds__(kThreads)
     const int len = (int)((cols - c0) < 16 ? (cols - c0) : 16);
     float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = i < len ? load_elem<BF16, 16>(x, r * cols + c0 + i) : 0.0f;
+    for (int i = 0; i < 16; ++i) v[i] = i < len ? load_elem<BF16>(x, r * cols + c0 + i) : 0.0f;
     uint32_t sc;
     float rr;
     nv_block_scale(amax_of(v), s_global, sc, rr);
     uint8_t* qrow = q + r * qstride + c0 / 2;
     for (int i = 0; i < len; i += 2) {
-      uint32_t lo = e2m1_code(v[i] * rr);
-      uint32_t hi = (i + 1 < len) ? e2m1_code(v[i + 1] * rr) : 0u;
+      const uint32_t lo = e2m1_code(v[i] * rr);
+      const uint32_t hi = (i + 1 < len) ? e2m1_code(v[i + 1] * rr) : 0u;
       qrow[i / 2] = (uint8_t)(lo | (hi << 4));
     }
     scales[r * bpr + j] = (uint8_t)sc;
@@ -232,52 +238,64 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // ------------------------------------------------------------ MX quantize --
-template <bool BF16>
-__device__ __forceinline__ void load32(const void* __restrict__ x, int64_t b, float (&v)[32]) {
-  if (BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(x) + 4 * b;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const u32x4 a = p[k];
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * k + 2 * j] = bf16_lo(w[j]);
-        v[8 * k + 2 * j + 1] = bf16_hi(w[j]);
-      }
-    }
-  } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(x) + 8 * b;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const f32x4 a = p[j];
-      v[4 * j] = a.x;
-      v[4 * j + 1] = a.y;
-      v[4 * j + 2] = a.z;
-      v[4 * j + 3] = a.w;
-    }
-  }
+// bf16 input: v_cvt_scalef32_pk_fp4_bf16 divides a bf16 pair by the power of
+// two 2^(byte-127) and encodes it with the E2M1 rounding (identical to
+// E2M1(x * 2^-e) for every finite bf16 and every exponent), so the encode is
+// one instruction per two values.
+template <int SEL>
+__device__ __forceinline__ uint32_t mx_pack2_bf16(uint32_t old, uint32_t w, float scale) {
+  bf16x2 v;
+  __builtin_memcpy(&v, &w, 4);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, v, scale, SEL);
 }
 
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
     k_mx_quant_fast(const void* __restrict__ x, int64_t nblk, uint8_t* __restrict__ q,
                     uint8_t* __restrict__ scales) {
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
-       b += (int64_t)gridDim.x * kThreads) {
-    float v[32];
-    load32<BF16>(x, b, v);
-    const uint32_t sc = e8m0_code(__float_as_uint(amax_of(v)));
-    const float inv = e8m0_inv(sc);
-    uint32_t w[4];
+  constexpr int VPB = BF16 ? 4 : 8;
+  __shared__ u32x4 lds[VPB * (kThreads + 1)];
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblk;
+       base += (int64_t)gridDim.x * kThreads) {
+    const int nb = (int)(nblk - base < kThreads ? nblk - base : kThreads);
+    u32x4 w[VPB];
+    stage_blocks<VPB, kThreads>(xv, base, nb, lds, w);
+    if ((int)threadIdx.x >= nb) continue;
+    uint32_t w4[4];
+    uint32_t sc;
+    if (BF16) {
+      u16x2 m = {0, 0};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t c[8];
+      for (int k = 0; k < 4; ++k) {
+        m = pkmax_abs(m, w[k].x);
+        m = pkmax_abs(m, w[k].y);
+        m = pkmax_abs(m, w[k].z);
+        m = pkmax_abs(m, w[k].w);
+      }
+      sc = e8m0_code((uint32_t)(m.x > m.y ? m.x : m.y) << 16);
+      const float scale = e8m0_value(sc);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = e2m1_code(v[8 * k + j] * inv);
-      w[k] = pack8(c);
+      for (int k = 0; k < 4; ++k) {
+        uint32_t d = 0;
+        d = mx_pack2_bf16<0>(d, w[k].x, scale);
+        d = mx_pack2_bf16<1>(d, w[k].y, scale);
+        d = mx_pack2_bf16<2>(d, w[k].z, scale);
+        d = mx_pack2_bf16<3>(d, w[k].w, scale);
+        w4[k] = d;
+      }
+    } else {
+      float v[32];
+      unpack_f32<32>(w, v);
+      sc = e8m0_code(__float_as_uint(amax_of(v)));
+      const float inv = e8m0_inv(sc);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = v[j] * inv;     // exact power-of-two multiply
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w4[k] = e2m1_pack8(v + 8 * k);
     }
-    reinterpret_cast<u32x4*>(q)[b] = u32x4{w[0], w[1], w[2], w[3]};
+    const int64_t b = base + threadIdx.x;
+    reinterpret_cast<u32x4*>(q)[b] = u32x4{w4[0], w4[1], w4[2], w4[3]};
     scales[b] = (uint8_t)sc;
   }
 }
@@ -295,13 +313,13 @@ __global__ void __launch_bounds__(kThreads)
     const int len = (int)((cols - c0) < 32 ? (cols - c0) : 32);
     float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = i < len ? load_elem<BF16, 32>(x, r * cols + c0 + i) : 0.0f;
+    for (int i = 0; i < 32; ++i) v[i] = i < len ? load_elem<BF16>(x, r * cols + c0 + i) : 0.0f;
     const uint32_t sc = e8m0_code(__float_as_uint(amax_of(v)));
     const float inv = e8m0_inv(sc);
     uint8_t* qrow = q + r * qstride + c0 / 2;
     for (int i = 0; i < len; i += 2) {
-      uint32_t lo = e2m1_code(v[i] * inv);
-      uint32_t hi = (i + 1 < len) ? e2m1_code(v[i + 1] * inv) : 0u;
+      const uint32_t lo = e2m1_code(v[i] * inv);
+      const uint32_t hi = (i + 1 < len) ? e2m1_code(v[i + 1] * inv) : 0u;
       qrow[i / 2] = (uint8_t)(lo | (hi << 4));
     }
     scales[r * bpr + j] = (uint8_t)sc;
@@ -309,60 +327,70 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // ------------------------------------------------------------- dequantize --
-template <bool BF16OUT, int N>
-__device__ __forceinline__ void store_vals(void* __restrict__ y, int64_t b, const float (&v)[N]) {
-  if (BF16OUT) {
-    u32x4* p = reinterpret_cast<u32x4*>(y) + (N / 8) * b;
-#pragma unroll
-    for (int k = 0; k < N / 8; ++k) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = f32_to_bf16(v[8 * k + 2 * j]) | (f32_to_bf16(v[8 * k + 2 * j + 1]) << 16);
-      p[k] = u32x4{w[0], w[1], w[2], w[3]};
-    }
-  } else {
-    f32x4* p = reinterpret_cast<f32x4*>(y) + (N / 4) * b;
-#pragma unroll
-    for (int k = 0; k < N / 4; ++k)
-      p[k] = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
-  }
+// Codes -> float32 values v * scale for a power-of-two scale (the gfx950
+// conversion applies only the exponent of its scale operand; with a power of
+// two the products are exact).  Byte SEL of d holds two codes.
+template <int SEL>
+__device__ __forceinline__ f32x2 decode2(uint32_t d, float pow2) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, pow2, SEL);
 }
 
-template <bool BF16OUT>
-__global__ void __launch_bounds__(kThreads)
-    k_nv_dequant_fast(const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
-                      const float* __restrict__ global_scale, int64_t nblk, void* __restrict__ y) {
-  const float s_global = *global_scale;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
-       b += (int64_t)gridDim.x * kThreads) {
-    const u32x2 c = reinterpret_cast<const u32x2*>(q)[b];
-    const float sb = s_global * e4m3_value(scales[b]);
-    float v[16];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[j] = sb * e2m1_value((c.x >> (4 * j)) & 15u);
-      v[8 + j] = sb * e2m1_value((c.y >> (4 * j)) & 15u);
-    }
-    store_vals<BF16OUT, 16>(y, b, v);
-  }
+template <int SEL>
+__device__ __forceinline__ uint32_t decode2_bf16(uint32_t d, float pow2) {
+  const bf16x2 h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, pow2, SEL);
+  uint32_t r;
+  __builtin_memcpy(&r, &h, 4);
+  return r;
 }
 
-template <bool BF16OUT>
+// float32 pair -> packed bf16, nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 h = {(__bf16)a, (__bf16)b};
+  uint32_t r;
+  __builtin_memcpy(&r, &h, 4);
+  return r;
+}
+
+// One lane per 8 values (bf16 out, 16-byte store) or 4 values (float32 out,
+// 16-byte store).  `unit` indexes those groups over the flat tensor.
+template <bool MX, bool BF16OUT>
 __global__ void __launch_bounds__(kThreads)
-    k_mx_dequant_fast(const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
-                      int64_t nblk, void* __restrict__ y) {
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
-       b += (int64_t)gridDim.x * kThreads) {
-    const u32x4 c = reinterpret_cast<const u32x4*>(q)[b];
-    const float s = e8m0_value(scales[b]);
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float v[32];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[8 * k + j] = e2m1_value((w[k] >> (4 * j)) & 15u) * s;
-    store_vals<BF16OUT, 32>(y, b, v);
+    k_dequant_fast(const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
+                   const float* __restrict__ global_scale, int64_t nunits, void* __restrict__ y) {
+  constexpr int kVals = BF16OUT ? 8 : 4;
+  constexpr int kBlock = MX ? 32 : 16;
+  const float s_global = MX ? 1.0f : *global_scale;
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < nunits;
+       u += (int64_t)gridDim.x * kThreads) {
+    const uint32_t d =
+        BF16OUT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q) + u)
+                : (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(q) + u);
+    const uint32_t sb = scales[u * kVals / kBlock];
+    u32x4 out;
+    if (MX) {
+      const float s = e8m0_value(sb);
+      if (BF16OUT) {
+        // v * 2^e is exact in bf16 (2 significant bits)
+        out = u32x4{decode2_bf16<0>(d, s), decode2_bf16<1>(d, s), decode2_bf16<2>(d, s),
+                    decode2_bf16<3>(d, s)};
+      } else {
+        const f32x2 a = decode2<0>(d, s), b = decode2<1>(d, s);
+        out = u32x4{__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(b.x),
+                    __float_as_uint(b.y)};
+      }
+    } else {
+      const float s = s_global * e4m3_value(sb);        // s_b, as the quantizer computes it
+      const f32x2 a = decode2<0>(d, 1.0f), b = decode2<1>(d, 1.0f);
+      if (BF16OUT) {
+        const f32x2 c = decode2<2>(d, 1.0f), e = decode2<3>(d, 1.0f);
+        out = u32x4{pack_bf16(s * a.x, s * a.y), pack_bf16(s * b.x, s * b.y),
+                    pack_bf16(s * c.x, s * c.y), pack_bf16(s * e.x, s * e.y)};
+      } else {
+        out = u32x4{__float_as_uint(s * a.x), __float_as_uint(s * a.y), __float_as_uint(s * b.x),
+                    __float_as_uint(s * b.y)};
+      }
+    }
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(y) + u);
   }
 }
 
@@ -381,7 +409,8 @@ __global__ void __launch_bounds__(kThreads)
     const uint32_t byte = q[r * qstride + c / 2];
     const uint32_t code = (c & 1) ? (byte >> 4) : (byte & 15u);
     const uint32_t sb = scales[r * bpr + c / bs];
-    const float v = mx ? e2m1_value(code) * e8m0_value(sb) : (s_global * e4m3_value(sb)) * e2m1_value(code);
+    const float v = mx ? e2m1_value(code) * e8m0_value(sb)
+                       : (s_global * e4m3_value(sb)) * e2m1_value(code);
     if (BF16OUT)
       reinterpret_cast<uint16_t*>(y)[t] = (uint16_t)f32_to_bf16(v);
     else
@@ -411,17 +440,20 @@ namespace fp4impl {
 hipError_t launch_amax(const void* x, bool bf16, int64_t n, uint32_t* partials, int* npart,
                        hipStream_t stream) {
   const int per = bf16 ? 8 : 4;
-  int64_t nvec = n / per;
-  // 4 vectors in flight per thread on the unrolled path
-  int g = grid_for((nvec + 3) / 4);
-  if (g > kAmaxPartials) g = kAmaxPartials;
-  *npart = g;
+  const int64_t nvec = n / per;
   if (aligned16(x)) {
+    // 4 vectors in flight per thread
+    const int64_t g64 = (nvec + 4 * kAmaxThreads - 1) / (4 * kAmaxThreads);
+    const int g = (int)(g64 < 1 ? 1 : (g64 > kAmaxPartials ? kAmaxPartials : g64));
+    *npart = g;
     if (bf16)
-      hipLaunchKernelGGL(k_amax<true>, dim3(g), dim3(kThreads), 0, stream, x, n, partials);
+      hipLaunchKernelGGL(k_amax<true>, dim3(g), dim3(kAmaxThreads), 0, stream, x, n, partials);
     else
-      hipLaunchKernelGGL(k_amax<false>, dim3(g), dim3(kThreads), 0, stream, x, n, partials);
+      hipLaunchKernelGGL(k_amax<false>, dim3(g), dim3(kAmaxThreads), 0, stream, x, n, partials);
   } else {
+    int g = grid_for((n + 3) / 4);
+    if (g > kAmaxPartials) g = kAmaxPartials;
+    *npart = g;
     if (bf16)
       hipLaunchKernelGGL(k_amax_scalar<true>, dim3(g), dim3(kThreads), 0, stream, x, n, partials);
     else
@@ -485,23 +517,17 @@ hipError_t launch_dequant(bool mx, const uint8_t* q, const uint8_t* scales,
   const int bs = mx ? 32 : 16;
   const bool fast = (cols % bs == 0) && aligned16(q) && aligned16(y);
   if (fast) {
-    const int64_t nblk = rows * (cols / bs);
-    const int g = grid_for(nblk);
+    const int64_t nunits = rows * cols / (bf16_out ? 8 : 4);
+    const int g = grid_for(nunits);
+#define FP4_DEQ_LAUNCH(M, B)                                                                    \
+  hipLaunchKernelGGL((k_dequant_fast<M, B>), dim3(g), dim3(kThreads), 0, stream, q, scales,     \
+                     global_scale, nunits, y)
     if (mx) {
-      if (bf16_out)
-        hipLaunchKernelGGL(k_mx_dequant_fast<true>, dim3(g), dim3(kThreads), 0, stream, q, scales,
-                           nblk, y);
-      else
-        hipLaunchKernelGGL(k_mx_dequant_fast<false>, dim3(g), dim3(kThreads), 0, stream, q,
-                           scales, nblk, y);
+      if (bf16_out) FP4_DEQ_LAUNCH(true, true); else FP4_DEQ_LAUNCH(true, false);
     } else {
-      if (bf16_out)
-        hipLaunchKernelGGL(k_nv_dequant_fast<true>, dim3(g), dim3(kThreads), 0, stream, q, scales,
-                           global_scale, nblk, y);
-      else
-        hipLaunchKernelGGL(k_nv_dequant_fast<false>, dim3(g), dim3(kThreads), 0, stream, q,
-                           scales, global_scale, nblk, y);
+      if (bf16_out) FP4_DEQ_LAUNCH(false, true); else FP4_DEQ_LAUNCH(false, false);
     }
+#undef FP4_DEQ_LAUNCH
   } else {
     const int g = grid_for(rows * cols);
     if (bf16_out)
