@@ -127,6 +127,7 @@ fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* q, const uint8_t* scale
  * float32; |D - D_ref| <= 1e-5 * |g_d| * sum_k |A_hat_mk W_hat_nk| (+ one bf16
  * rounding for bf16 output).  K must be a multiple of bs (FP4_ERR_SHAPE);
  * A, W must be 16-byte aligned and K a multiple of 32 (FP4_ERR_ALIGN / SHAPE).
+ * M == 0 or N == 0 is a no-op; K == 0 writes D = 0 without reading the operands.
  */
 fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
                            const float* g_a, const uint8_t* W, const uint8_t* w_scales,
@@ -145,6 +146,7 @@ size_t fp4_gemv_workspace_bytes(int64_t B, int64_t K);
  *   W   NVFP4 [N, K/2] + w_scales [N, K/16] + g_w (device float);
  *   y   out [B, N] float32 or bf16.  1 <= B <= 16, K % 32 == 0.
  *   workspace  >= fp4_gemv_workspace_bytes(B, K) bytes (holds quantized x).
+ * N == 0 is a no-op; K == 0 writes y = 0 without reading x, W or the workspace.
  * x, W and workspace must be 16-byte aligned, w_scales 2-byte aligned (FP4_ERR_ALIGN).
  * Accuracy as for fp4_scaled_gemm.
  */

@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfp4.so")
+# FP4_LIBRARY may name another build of the same library (A/B timing of kernel variants).
+LIB_PATH = os.environ.get("FP4_LIBRARY") or os.path.join(_PKG, "libfp4.so")
 
 # enums of include/fp4.h
 FP4_OK = 0

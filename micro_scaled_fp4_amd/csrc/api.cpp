@@ -160,6 +160,14 @@ fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_sc
   if (K % 32 != 0) return FP4_ERR_SHAPE;
   if (fmt == FP4_MXFP4 && (g_a != nullptr || g_b != nullptr)) return FP4_ERR_DTYPE;
   if (M == 0 || N == 0) return FP4_OK;
+  if (K == 0) {   // empty contraction: D = 0, operands are not read
+    if (D == nullptr) return FP4_ERR_NULL;
+    if (!aligned(D, dt == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+    fp4_status st = check_arch();
+    if (st != FP4_OK) return st;
+    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(D, M * N, dt == FP4_BF16, stream), "fp4_scaled_gemm");
+    return FP4_OK;
+  }
   if (A == nullptr || a_scales == nullptr || W == nullptr || w_scales == nullptr || D == nullptr)
     return FP4_ERR_NULL;
   if (fmt == FP4_NVFP4 && (g_a == nullptr || g_b == nullptr)) return FP4_ERR_NULL;
@@ -185,6 +193,14 @@ fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_
   if (!valid_dtype(xt) || !valid_dtype(yt)) return FP4_ERR_DTYPE;
   if (B < 1 || B > 16 || N < 0 || K < 0 || K % 32 != 0) return FP4_ERR_SHAPE;
   if (N == 0) return FP4_OK;
+  if (K == 0) {   // empty contraction: y = 0, x, W and the workspace are not read
+    if (y == nullptr) return FP4_ERR_NULL;
+    if (!aligned(y, yt == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+    fp4_status st = check_arch();
+    if (st != FP4_OK) return st;
+    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(y, B * N, yt == FP4_BF16, stream), "fp4_gemv_batched");
+    return FP4_OK;
+  }
   if (x == nullptr || W == nullptr || w_scales == nullptr || g_w == nullptr || y == nullptr)
     return FP4_ERR_NULL;
   if (workspace == nullptr || workspace_bytes < fp4impl::gemv_workspace_bytes(B, K))

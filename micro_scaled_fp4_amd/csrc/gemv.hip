@@ -31,13 +31,14 @@ using namespace fp4dev;
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kPrepThreads = 256;
 constexpr size_t kHeader = 256;        // workspace header: [0] s_global of x
 constexpr int kMaxWaves = 16;
-constexpr int kMaxSteps = 4;           // 128-value steps per wave kept in registers
+constexpr int kMaxSteps = 3;           // 128-value steps per wave kept in registers
 
 inline int64_t kpad(int64_t K) { return (K + 127) / 128 * 128; }
 
@@ -145,6 +146,60 @@ __device__ __forceinline__ v8h dequant8(uint32_t codes, float pow2, v2h mant) {
   return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// One 128-value step of a 16-row strip: this lane's 16 code bytes (32 values)
+// and 2 scale bytes; zeros past K.
+__device__ __forceinline__ void load_step(const uint8_t* __restrict__ wr,
+                                          const uint8_t* __restrict__ sr, int kc, int K,
+                                          u32x4& codes, uint32_t& sbytes) {
+  if (kc < K) {
+    codes = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + kc / 2));
+    sbytes = *reinterpret_cast<const uint16_t*>(sr + kc / 16);
+  } else {
+    codes = u32x4{0, 0, 0, 0};
+    sbytes = 0;
+  }
+}
+
+__device__ __forceinline__ v4f mfma_step(v4f acc, const v8h (&xv)[4], const u32x4& codes,
+                                         uint32_t sbytes) {
+  float p0, p1;
+  v2h m0, m1;
+  e4m3_split(sbytes & 0xffu, p0, m0);
+  e4m3_split(sbytes >> 8, p1, m1);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[0], dequant8(codes.x, p0, m0), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[1], dequant8(codes.y, p0, m0), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[2], dequant8(codes.z, p1, m1), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[3], dequant8(codes.w, p1, m1), acc, 0, 0, 0);
+  return acc;
+}
+
+// Sums the waves' partial 16x16 tiles (fixed order) and writes y for strip n0.
+template <bool YBF16>
+__device__ __forceinline__ void reduce_store(v4f* red, v4f acc, int nwaves, int n0, int N, int B,
+                                             float gscale, float g_d, void* __restrict__ y) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  // output (b, n0 + c) sits in lane (b/4)*16 + c, element b%4, of every wave
+  for (int o = threadIdx.x; o < 256; o += blockDim.x) {
+    const int ob = o >> 4, oc = o & 15;
+    const int src = (ob >> 2) * 16 + oc, el = ob & 3;
+    float sum = red[src][el];
+    for (int w = 1; w < nwaves; ++w) sum = sum + red[w * 64 + src][el];
+    if (ob < B && n0 + oc < N) {
+      const float v = (sum * gscale) * g_d;
+      if (YBF16)
+        reinterpret_cast<uint16_t*>(y)[(int64_t)ob * N + n0 + oc] = (uint16_t)f32_to_bf16(v);
+      else
+        reinterpret_cast<float*>(y)[(int64_t)ob * N + n0 + oc] = v;
+    }
+  }
+  __syncthreads();
+}
+
+// RESIDENT: the wave's x' fragments (spw <= kMaxSteps steps) stay in registers
+// and the next strip's W bytes are loaded while the current strip computes.
+// Otherwise x' is re-read from the workspace (L2) for every step.
 template <bool YBF16, bool RESIDENT>
 __global__ void __launch_bounds__(kMaxWaves * 64)
     k_gemv_mfma(const uint8_t* __restrict__ W, const uint8_t* __restrict__ w_scales,
@@ -158,86 +213,305 @@ __global__ void __launch_bounds__(kMaxWaves * 64)
   const int t0 = wave * spw;
   const _Float16* xp = reinterpret_cast<const _Float16*>(ws + kHeader);
   const int64_t wrow_bytes = K / 2, srow_bytes = K / 16;
+  const float gscale = reinterpret_cast<const float*>(ws)[0] * (*g_w);
+  const int nstrips = (N + 15) / 16;
+  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
-  // x' fragments of this wave's K range: step i, MFMA sub-step s -> 8 fp16
-  v8h xf[kMaxSteps][4];
   if (RESIDENT) {
+    // x' fragments of this wave's K range: step i, MFMA sub-step s -> 8 fp16
+    v8h xf[kMaxSteps][4];
 #pragma unroll
     for (int i = 0; i < kMaxSteps; ++i) {
       const int t = t0 + i;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (i < spw && t < T && b < B)
-          xf[i][s] = *reinterpret_cast<const v8h*>(xp + (int64_t)b * Kp + 128 * t + 32 * g + 8 * s);
-        else
-          xf[i][s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int s = 0; s < 4; ++s)
+        xf[i][s] = (i < spw && t < T && b < B)
+                       ? *reinterpret_cast<const v8h*>(xp + (int64_t)b * Kp + 128 * t + 32 * g + 8 * s)
+                       : zero8;
+    }
+    u32x4 nc[kMaxSteps];
+    uint32_t ns[kMaxSteps];
+    auto load_strip = [&](int strip) {
+      const int row = min(strip * 16 + b, N - 1);
+      const uint8_t* wr = W + (int64_t)row * wrow_bytes;
+      const uint8_t* sr = w_scales + (int64_t)row * srow_bytes;
+#pragma unroll
+      for (int i = 0; i < kMaxSteps; ++i) {
+        const int t = t0 + i;
+        if (i < spw && t < T) {
+          load_step(wr, sr, 128 * t + 32 * g, K, nc[i], ns[i]);
+        } else {
+          nc[i] = u32x4{0, 0, 0, 0};
+          ns[i] = 0;
+        }
+      }
+    };
+    int strip = blockIdx.x;
+    if (strip < nstrips) load_strip(strip);
+    for (; strip < nstrips; strip += gridDim.x) {
+      u32x4 cc[kMaxSteps];
+      uint32_t cs[kMaxSteps];
+#pragma unroll
+      for (int i = 0; i < kMaxSteps; ++i) {
+        cc[i] = nc[i];
+        cs[i] = ns[i];
+      }
+      if (strip + (int)gridDim.x < nstrips) load_strip(strip + gridDim.x);
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < kMaxSteps; ++i)
+        if (i < spw) acc = mfma_step(acc, xf[i], cc[i], cs[i]);
+      reduce_store<YBF16>(red, acc, nwaves, strip * 16, N, B, gscale, g_d, y);
+    }
+  } else {
+    for (int strip = blockIdx.x; strip < nstrips; strip += gridDim.x) {
+      const int row = min(strip * 16 + b, N - 1);
+      const uint8_t* wr = W + (int64_t)row * wrow_bytes;
+      const uint8_t* sr = w_scales + (int64_t)row * srow_bytes;
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int i = 0; i < spw; ++i) {
+        const int t = t0 + i;
+        if (t >= T) break;
+        u32x4 codes;
+        uint32_t sbytes;
+        load_step(wr, sr, 128 * t + 32 * g, K, codes, sbytes);
+        v8h xv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          xv[s] = b < B ? *reinterpret_cast<const v8h*>(xp + (int64_t)b * Kp + 128 * t + 32 * g + 8 * s)
+                        : zero8;
+        acc = mfma_step(acc, xv, codes, sbytes);
+      }
+      reduce_store<YBF16>(red, acc, nwaves, strip * 16, N, B, gscale, g_d, y);
+    }
+  }
+}
+
+// ------------------------------------------------------ fused streaming GEMV --
+// One workgroup per CU.  Every workgroup first quantizes all of x itself (global
+// amax, then per-block NVFP4 exactly as nvfp4_quantize) into LDS -- as exact
+// fp16 x' when it fits (XF16), else as codes + scale bytes that are dequantized
+// per use -- while its first W loads are already in flight.  Then each wave
+// streams whole 16-row strips of W over all of K (no cross-wave reduction) with
+// kPairs pairs of 128-value steps in flight.  A decode GEMV moves so few bytes
+// per wave that the loads in flight, not the wave count, set the rate, so the
+// ring is as deep as the register file allows.
+constexpr int kStreamThreads = 1024;
+constexpr int kPairs = 4;     // pairs of 128-value steps in flight per wave
+
+__device__ __forceinline__ uint32_t block_max_1024(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < kStreamThreads / 64; ++i) r = umax(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+template <bool XBF16, bool XF16, bool YBF16>
+__global__ void __launch_bounds__(kStreamThreads, 1)
+    k_gemv_stream(const void* __restrict__ x, int B, const uint8_t* __restrict__ W,
+                  const uint8_t* __restrict__ w_scales, const float* __restrict__ g_w, int N,
+                  int K, int Kq, int lds_x_bytes, float g_d, void* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ uint32_t red[kStreamThreads / 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = lane & 15, g = lane >> 4;
+  const int nstrips = (N + 15) / 16;
+  const int64_t wrow_bytes = K / 2, srow_bytes = K / 16;
+  // LDS layout of the quantized x (zero past K up to Kq, a multiple of 256)
+  const int xf_row = Kq * 2 + 16;                // XF16: fp16 row stride (bytes)
+  const int xc_row = Kq / 2 + 16;                // codes row stride
+  uint8_t* xs_base = lds + B * xc_row;           // scale bytes [B][Kq/16]
+
+  // A wave's work is a sequence of elements (strip si, pair pp): pair pp holds
+  // the two 128-value steps 2pp, 2pp+1 of strip gw + si * nwt, pp < Pq.  Strips
+  // are dealt wave-major so every CU gets the same number of streaming waves.
+  // HBM is read as 8 rows x 128 contiguous bytes per instruction (lane l: row
+  // l/8, 16-byte chunk l%8), two instructions per pair.  Loads are branch-free
+  // and their results used unmodified, so kPairs pairs stay in flight: past K
+  // the addresses are clamped to the row's last 32 values, which are finite
+  // (E2M1 codes, E4M3 scales of real blocks) and meet x' = 0 there, so they add
+  // exact zeros; rows past N (and loads past the wave's last element) are
+  // clamped into the matrix and their results never stored.
+  const int Pq = Kq / 256;
+  const int nwt = gridDim.x * (kStreamThreads / 64);
+  const int gw = wave * gridDim.x + blockIdx.x;
+  const int nmine = gw < nstrips ? (nstrips - gw + nwt - 1) / nwt : 0;
+  const int J = nmine * Pq;
+  const int r8 = lane >> 3, c8 = lane & 7;
+  u32x4 ra[kPairs], rb[kPairs];
+  uint32_t rs0[kPairs], rs1[kPairs];
+  auto load_pair = [&](int si, int pp, u32x4& a, u32x4& bb, uint32_t& s0, uint32_t& s1) {
+    const int strip = gw + si * nwt;
+    const int vidx = 256 * pp + 32 * c8;
+    const int vcl = min(vidx, K - 32);
+    const int ra_ = min(strip * 16 + r8, N - 1), rb_ = min(strip * 16 + 8 + r8, N - 1);
+    a = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(W + (int64_t)ra_ * wrow_bytes + vcl / 2));
+    bb = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(W + (int64_t)rb_ * wrow_bytes + vcl / 2));
+    // scale bytes for this lane's MFMA position (W row b, values [32g, 32g+32) of each step)
+    const int row = min(strip * 16 + b, N - 1);
+    const int v0 = 256 * pp + 32 * g, v1 = v0 + 128;
+    const uint8_t* sr = w_scales + (int64_t)row * srow_bytes;
+    s0 = *reinterpret_cast<const uint16_t*>(sr + min(v0, K - 32) / 16);
+    s1 = *reinterpret_cast<const uint16_t*>(sr + min(v1, K - 32) / 16);
+  };
+  int lsi = 0, lpp = 0;   // next element to load
+#pragma unroll
+  for (int i = 0; i < kPairs; ++i) {
+    load_pair(lsi, lpp, ra[i], rb[i], rs0[i], rs1[i]);
+    if (++lpp == Pq) { lpp = 0; ++lsi; }
+  }
+
+  // ---- x -> NVFP4 (global amax over all of [B, K], then per 16-value block)
+  const int64_t n = (int64_t)B * K;
+  uint32_t m = 0;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  for (int64_t i = threadIdx.x; i < n / (XBF16 ? 8 : 4); i += kStreamThreads) {
+    const u32x4 v = xv[i];
+    if (XBF16) {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = w4[j] & 0x7fff7fffu;
+        m = umax(m, umax(a << 16, a & 0xffff0000u));
+      }
+    } else {
+      m = umax(umax(m, v.x & 0x7fffffffu),
+               umax(v.y & 0x7fffffffu, umax(v.z & 0x7fffffffu, v.w & 0x7fffffffu)));
+    }
+  }
+  const float s_gx = nv_global_scale(__uint_as_float(block_max_1024(m, red)));
+  const int bpr = Kq / 16;
+  for (int blk = threadIdx.x; blk < B * bpr; blk += kStreamThreads) {
+    const int row = blk / bpr, c0 = (blk - row * bpr) * 16;
+    uint32_t c[2] = {0u, 0u}, sc = 0u;
+    if (c0 < K) {
+      float v[16];
+      const int64_t base = (int64_t)row * K + c0;
+      if (XBF16) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + base);
+        const u32x4 a = p[0], e = p[1];
+        const uint32_t w8[8] = {a.x, a.y, a.z, a.w, e.x, e.y, e.z, e.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          v[2 * j] = bf16_lo(w8[j]);
+          v[2 * j + 1] = bf16_hi(w8[j]);
+        }
+      } else {
+        const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + base);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 a = p[j];
+          v[4 * j] = a.x;
+          v[4 * j + 1] = a.y;
+          v[4 * j + 2] = a.z;
+          v[4 * j + 3] = a.w;
+        }
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
+      float r;
+      nv_block_scale(__uint_as_float(am), s_gx, sc, r);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
+      c[0] = e2m1_pack8(v);
+      c[1] = e2m1_pack8(v + 8);
+    }
+    if (XF16) {
+      float p2;
+      v2h mt;
+      e4m3_split(sc, p2, mt);
+      const v8h h0 = dequant8(c[0], p2, mt), h1 = dequant8(c[1], p2, mt);    // exact x'
+      v8h* dst = reinterpret_cast<v8h*>(lds + row * xf_row + c0 * 2);
+      dst[0] = h0;
+      dst[1] = h1;
+    } else {
+      *reinterpret_cast<u32x2*>(lds + row * xc_row + c0 / 2) = u32x2{c[0], c[1]};
+      xs_base[row * bpr + c0 / 16] = (uint8_t)sc;
+    }
+  }
+  __syncthreads();
+  const float gscale = s_gx * (*g_w);
+  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  // ---- stream W
+  // wave-private transpose buffer: row r's 128 bytes at r*128, 16-byte chunk c
+  // stored at position c ^ (r & 7) so both the row-wise writes and the
+  // MFMA-layout reads hit distinct banks
+  uint8_t* tb = lds + lds_x_bytes + wave * 2048;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int csi = 0, cpp = 0;   // element being computed
+  for (int j0 = 0; j0 < J; j0 += kPairs) {
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const u32x4 a = ra[i], bb = rb[i];
+      const uint32_t s0 = rs0[i], s1 = rs1[i];
+      load_pair(lsi, lpp, ra[i], rb[i], rs0[i], rs1[i]);
+      if (++lpp == Pq) { lpp = 0; ++lsi; }
+      if (j0 + i < J) {
+        *reinterpret_cast<u32x4*>(tb + r8 * 128 + ((c8 ^ r8) << 4)) = a;
+        *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + ((c8 ^ r8) << 4)) = bb;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const u32x4 codes =
+              *reinterpret_cast<const u32x4*>(tb + b * 128 + (((4 * st + g) ^ (b & 7)) << 4));
+          const int t = 2 * cpp + st;
+          v8h xq[4];
+          if (XF16) {
+            const v8h* src = reinterpret_cast<const v8h*>(lds + min(b, B - 1) * xf_row + (128 * t + 32 * g) * 2);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) xq[s4] = b < B ? src[s4] : zero8;
+          } else {
+            const int bc = min(b, B - 1);
+            const u32x4 xc = *reinterpret_cast<const u32x4*>(lds + bc * xc_row + 64 * t + 16 * g);
+            const uint32_t xsb = b < B ? *reinterpret_cast<const uint16_t*>(xs_base + bc * bpr + 8 * t + 2 * g) : 0u;
+            float q0, q1;
+            v2h m0, m1;
+            e4m3_split(xsb & 0xffu, q0, m0);
+            e4m3_split(xsb >> 8, q1, m1);
+            xq[0] = dequant8(xc.x, q0, m0);
+            xq[1] = dequant8(xc.y, q0, m0);
+            xq[2] = dequant8(xc.z, q1, m1);
+            xq[3] = dequant8(xc.w, q1, m1);
+          }
+          acc = mfma_step(acc, xq, codes, st ? s1 : s0);
+        }
+        if (cpp == Pq - 1) {   // end of a strip: D[4g + r][b] of this 16-row strip
+          const int nn = (gw + csi * nwt) * 16 + b;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int ob = 4 * g + r;
+            if (ob < B && nn < N) {
+              const float v = (acc[r] * gscale) * g_d;
+              if (YBF16)
+                reinterpret_cast<uint16_t*>(y)[(int64_t)ob * N + nn] = (uint16_t)f32_to_bf16(v);
+              else
+                reinterpret_cast<float*>(y)[(int64_t)ob * N + nn] = v;
+            }
+          }
+          acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (++cpp == Pq) { cpp = 0; ++csi; }
       }
     }
   }
-  const float gscale = reinterpret_cast<const float*>(ws)[0] * (*g_w);
-  const int nstrips = (N + 15) / 16;
-  for (int strip = blockIdx.x; strip < nstrips; strip += gridDim.x) {
-    const int n0 = strip * 16;
-    const int row = min(n0 + b, N - 1);
-    const uint8_t* wr = W + (int64_t)row * wrow_bytes;
-    const uint8_t* sr = w_scales + (int64_t)row * srow_bytes;
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int i0 = 0; i0 < spw; i0 += kMaxSteps) {
-      u32x4 codes[kMaxSteps];
-      uint32_t sbytes[kMaxSteps];
-#pragma unroll
-      for (int i = 0; i < kMaxSteps; ++i) {
-        const int t = t0 + i0 + i;
-        const int kc = 128 * t + 32 * g;
-        if (i0 + i < spw && t < T && kc < K) {
-          codes[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + kc / 2));
-          sbytes[i] = *reinterpret_cast<const uint16_t*>(sr + kc / 16);
-        } else {
-          codes[i] = u32x4{0, 0, 0, 0};
-          sbytes[i] = 0;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kMaxSteps; ++i) {
-        if (i0 + i >= spw) break;
-        const int t = t0 + i0 + i;
-        v8h xv[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (RESIDENT) {
-            xv[s] = xf[i][s];
-          } else {
-            xv[s] = (t < T && b < B) ? *reinterpret_cast<const v8h*>(xp + (int64_t)b * Kp + 128 * t + 32 * g + 8 * s)
-                                     : v8h{0, 0, 0, 0, 0, 0, 0, 0};
-          }
-        }
-        float p0, p1;
-        v2h m0, m1;
-        e4m3_split(sbytes[i] & 0xffu, p0, m0);
-        e4m3_split(sbytes[i] >> 8, p1, m1);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[0], dequant8(codes[i].x, p0, m0), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[1], dequant8(codes[i].y, p0, m0), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[2], dequant8(codes[i].z, p1, m1), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[3], dequant8(codes[i].w, p1, m1), acc, 0, 0, 0);
-      }
-    }
-    red[wave * 64 + lane] = acc;
-    __syncthreads();
-    // output (b, n0 + c) sits in lane (b/4)*16 + c, element b%4, of every wave
-    for (int o = threadIdx.x; o < 256; o += blockDim.x) {
-      const int ob = o >> 4, oc = o & 15;
-      const int src = (ob >> 2) * 16 + oc, el = ob & 3;
-      float sum = red[src][el];
-      for (int w = 1; w < nwaves; ++w) sum = sum + red[w * 64 + src][el];
-      if (ob < B && n0 + oc < N) {
-        const float v = (sum * gscale) * g_d;
-        if (YBF16)
-          reinterpret_cast<uint16_t*>(y)[(int64_t)ob * N + n0 + oc] = (uint16_t)f32_to_bf16(v);
-        else
-          reinterpret_cast<float*>(y)[(int64_t)ob * N + n0 + oc] = v;
-      }
-    }
-    __syncthreads();
+}
+
+// K = 0: every output is an empty sum.
+template <bool YBF16>
+__global__ void __launch_bounds__(256) k_zero_fill(int64_t n, void* __restrict__ y) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    if (YBF16)
+      reinterpret_cast<uint16_t*>(y)[i] = 0;
+    else
+      reinterpret_cast<float*>(y)[i] = 0.0f;
   }
 }
 
@@ -247,6 +521,17 @@ int g_num_cus = 0;
 
 namespace fp4impl {
 
+hipError_t launch_zero_fill(void* y, int64_t n, bool y_bf16, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t nb = (n + 255) / 256;
+  const dim3 g0((unsigned)(nb < 4096 ? nb : 4096));
+  if (y_bf16)
+    hipLaunchKernelGGL(k_zero_fill<true>, g0, dim3(256), 0, stream, n, y);
+  else
+    hipLaunchKernelGGL(k_zero_fill<false>, g0, dim3(256), 0, stream, n, y);
+  return hipGetLastError();
+}
+
 size_t gemv_workspace_bytes(int64_t B, int64_t K) {
   return kHeader + (size_t)(B * kpad(K) * 2);
 }
@@ -255,6 +540,45 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
                        const uint8_t* w_scales, const float* g_w, int64_t N, int64_t K, float g_d,
                        void* y, bool y_bf16, void* workspace, hipStream_t stream) {
   if (N > (1 << 30) || K > (1 << 30)) return hipErrorInvalidValue;
+  if (g_num_cus == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      g_num_cus = cus;
+    else
+      g_num_cus = 256;
+  }
+  if (K == 0) return launch_zero_fill(y, B * N, y_bf16, stream);
+  const int nstrips = (int)((N + 15) / 16);
+  // fused streaming kernel when the quantized x fits in LDS
+  const int64_t Kq = (K + 255) / 256 * 256;
+  const int64_t lds_f16 = B * (Kq * 2 + 16);
+  const int64_t lds_fp4 = B * (Kq / 2 + 16) + B * (Kq / 16);
+  const bool xf16 = lds_f16 <= 96 * 1024;
+  if (xf16 || lds_fp4 <= 120 * 1024) {
+    const int lds_x = (int)(((xf16 ? lds_f16 : lds_fp4) + 15) / 16 * 16);
+    const int lds = lds_x + (kStreamThreads / 64) * 2048;
+    const int grid = nstrips < g_num_cus ? nstrips : g_num_cus;
+#define FP4_GEMV_STREAM(XB, XF, YB)                                                              \
+  do {                                                                                           \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<XB, XF, YB>), \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);        \
+    if (e != hipSuccess) return e;                                                               \
+    hipLaunchKernelGGL((k_gemv_stream<XB, XF, YB>), dim3(grid), dim3(kStreamThreads), lds,       \
+                       stream, x, (int)B, W, w_scales, g_w, (int)N, (int)K, (int)Kq, lds_x, g_d, y);    \
+  } while (0)
+    if (x_bf16) {
+      if (xf16) { if (y_bf16) FP4_GEMV_STREAM(true, true, true); else FP4_GEMV_STREAM(true, true, false); }
+      else { if (y_bf16) FP4_GEMV_STREAM(true, false, true); else FP4_GEMV_STREAM(true, false, false); }
+    } else {
+      if (xf16) { if (y_bf16) FP4_GEMV_STREAM(false, true, true); else FP4_GEMV_STREAM(false, true, false); }
+      else { if (y_bf16) FP4_GEMV_STREAM(false, false, true); else FP4_GEMV_STREAM(false, false, false); }
+    }
+#undef FP4_GEMV_STREAM
+    return hipGetLastError();
+  }
+
+  // very long K: x' through the workspace, waves split K
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int64_t Kp = kpad(K);
   const int64_t nblk = B * (Kp / 16);
@@ -265,21 +589,11 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
     hipLaunchKernelGGL(k_gemv_xprep<false>, g1, dim3(kPrepThreads), 0, stream, x, B, K, Kp, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-
-  if (g_num_cus == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      g_num_cus = cus;
-    else
-      g_num_cus = 256;
-  }
   const int T = (int)(Kp / 128);
   int spw = (T + kMaxWaves - 1) / kMaxWaves;
   if (spw < 1) spw = 1;
   const int nwaves = (T + spw - 1) / spw;
   const bool resident = spw <= kMaxSteps;
-  const int nstrips = (int)((N + 15) / 16);
   const int grid = nstrips < g_num_cus ? nstrips : g_num_cus;
   const dim3 blk(64 * nwaves);
 #define FP4_GEMV_LAUNCH(YB, RES)                                                               \

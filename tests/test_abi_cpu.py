@@ -84,6 +84,10 @@ def test_dequant_gemm_gemv_hadamard_argument_errors():
     assert v(P, 1, 17, P, P, P, 8, 512, 1.0, P, 1, P, 1 << 20, None) == SHAPE
     assert v(P, 1, 4, P, P, P, 8, 500, 1.0, P, 1, P, need, None) == SHAPE   # K % 32
     assert v(P, 1, 4, P, P, P, 8, 512, 1.0, P, 1, P, need - 1, None) == WORKSPACE
+    # K = 0 needs only y; a missing or misaligned y is reported before any HIP call
+    assert v(None, 1, 4, None, None, None, 8, 0, 1.0, None, 1, None, 0, None) == NULL
+    assert v(None, 1, 4, None, None, None, 8, 0, 1.0, ctypes.c_void_p(4099), 1, None, 0, None) == ALIGN
+    assert g(0, None, None, None, None, None, None, 1.0, 8, 8, 0, None, 1, None) == NULL
     h = lib.hadamard_quantize
     assert h(P, 1, 4, 256, 64, 0, 0, P, P, P, 0, P, P, 4096, None) == SHAPE
     assert h(P, 1, 4, 200, 128, 0, 0, P, P, P, 0, P, P, 4096, None) == SHAPE

@@ -92,6 +92,22 @@ def test_gemm_small_shapes(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["nv", "mx"])
+def test_gemm_empty_k_writes_zeros(fmt):
+    """K = 0: D is the empty sum, exactly 0; M = 0 or N = 0 writes nothing."""
+    announce(f"gemm K=0 {fmt}")
+    dev = "cuda:0"
+    e = torch.empty((5, 0), dtype=torch.uint8, device=dev)
+    g = torch.ones(1, dtype=torch.float32, device=dev) if fmt == "nv" else None
+    f = fp4.FP4_NVFP4 if fmt == "nv" else fp4.FP4_MXFP4
+    for out in (torch.float32, torch.bfloat16):
+        D = torch.full((5, 5), 3.0, dtype=out, device=dev)
+        fp4.fp4_scaled_gemm(f, e, e, g, e, e, g, 0, 1.0, out, out=D)
+        assert torch.count_nonzero(D).item() == 0
+    z = torch.empty((0, 16), dtype=torch.uint8, device=dev)
+    assert fp4.fp4_scaled_gemm(f, z, z, g, z, z, g, 32).shape == (0, 0)
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
 def test_gemm_unit_scales_exact(fmt):
     """All block scales 1 and g = 1: every product is a multiple of 1/4 and the
     float32 sums stay exact, so D must equal the integer matmul exactly."""

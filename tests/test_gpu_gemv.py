@@ -40,6 +40,18 @@ def test_gemv_small_matches_oracle(B, N, K):
     _run_and_check(o.bf16_bits_to_f32(x), False, Wq, Ws, float(g_w), N, K, 2.0, torch.float32)
 
 
+@pytest.mark.parametrize("B,N,K", [(16, 64, 20480), (2, 100, 32768), (12, 70, 5120), (9, 33, 4096)])
+def test_gemv_long_k_and_wide_batch(B, N, K):
+    """Shapes that take the other kernel paths: x kept in LDS as codes + scales
+    (wide batch or long K) and the split-K path for K too long for LDS."""
+    announce(f"gemv path B={B} N={N} K={K}")
+    Wq = workloads.random_codes((N, K // 2), seed=K + 1)
+    Ws = workloads.random_bytes((N, K // 16), 0x18, 0x58, seed=K + 2)
+    x = workloads.gemv_x(B, K, seed=K + 3)
+    _run_and_check(x, True, Wq, Ws, 0.02, N, K, 1.0, torch.float32)
+    _run_and_check(o.bf16_bits_to_f32(x), False, Wq, Ws, 0.02, N, K, 0.5, torch.bfloat16)
+
+
 @pytest.mark.parametrize("B", [1, 4, 16])
 def test_gemv_decode_shape_all_outputs(B):
     """W 27648x5120 (the decode GEMV shape) with random valid NVFP4 codes and
@@ -51,3 +63,20 @@ def test_gemv_decode_shape_all_outputs(B):
     x = workloads.gemv_x(B, K)
     _run_and_check(x, True, Wq, Ws, 0.013, N, K, 1.0, torch.float32)
     _run_and_check(x, True, Wq, Ws, 0.013, N, K, 1.0, torch.bfloat16)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gemv_empty_k_writes_zeros(out_dtype):
+    """K = 0: every output is an empty sum, so y = 0 exactly; N = 0 is a no-op."""
+    announce(f"gemv K=0 {out_dtype}")
+    x = torch.empty((3, 0), dtype=torch.bfloat16, device="cuda:0")
+    W = torch.empty((40, 0), dtype=torch.uint8, device="cuda:0")
+    Ws = torch.empty((40, 0), dtype=torch.uint8, device="cuda:0")
+    gw = torch.ones(1, dtype=torch.float32, device="cuda:0")
+    y = torch.full((3, 40), 7.0, dtype=out_dtype, device="cuda:0")
+    fp4.fp4_gemv_batched(x, W, Ws, gw, 0, 1.0, out_dtype, out=y)
+    assert torch.count_nonzero(y).item() == 0
+    y0 = fp4.fp4_gemv_batched(torch.zeros((2, 64), dtype=torch.bfloat16, device="cuda:0"),
+                              torch.empty((0, 32), dtype=torch.uint8, device="cuda:0"),
+                              torch.empty((0, 4), dtype=torch.uint8, device="cuda:0"), gw, 64)
+    assert y0.shape == (2, 0)
