@@ -288,16 +288,23 @@ __global__ void __launch_bounds__(kMaxWaves * 64)
 }
 
 // ------------------------------------------------------ fused streaming GEMV --
-// One workgroup per CU.  Every workgroup first quantizes all of x itself (global
-// amax, then per-block NVFP4 exactly as nvfp4_quantize) into LDS -- as exact
-// fp16 x' when it fits (XF16), else as codes + scale bytes that are dequantized
-// per use -- while its first W loads are already in flight.  Then each wave
-// streams whole 16-row strips of W over all of K (no cross-wave reduction) with
-// kPairs pairs of 128-value steps in flight.  A decode GEMV moves so few bytes
-// per wave that the loads in flight, not the wave count, set the rate, so the
-// ring is as deep as the register file allows.
+// One workgroup of 16 waves per CU, persistent over rounds of strips.
+// Prologue: every workgroup quantizes all of x itself (global amax, then
+// per-block NVFP4 exactly as nvfp4_quantize) into LDS -- as exact fp16 x' when
+// it fits (XF16), else as codes + scale bytes dequantized per use.  Its first x
+// loads are issued before the first W loads so they do not queue behind them.
+// Streaming: a round gives each of the kSlots wave pairs one 16-row strip; the
+// two waves of a pair stream the two halves of K, kPairs pairs of 128-value
+// steps in flight per wave.  At the round's end the upper half's partial tile
+// goes through LDS (double-buffered by round parity, one barrier per round) to
+// the lower half's wave, which adds it (fixed order) and writes y.
 constexpr int kStreamThreads = 1024;
-constexpr int kPairs = 4;     // pairs of 128-value steps in flight per wave
+constexpr int kStreamWaves = kStreamThreads / 64;
+constexpr int kSplit = 2;                       // waves per strip (K parts)
+constexpr int kSlots = kStreamWaves / kSplit;   // strips per workgroup and round
+constexpr int kPairs = 4;                       // pairs of steps in flight per wave
+constexpr int kXRegVecs = 4;                    // 16-byte x vectors per thread held in registers
+constexpr int kRedBytes = 2 * kSlots * 64 * 16; // double-buffered partial tiles
 
 __device__ __forceinline__ uint32_t block_max_1024(uint32_t v, uint32_t* red) {
   v = wave_max_u32(v);
@@ -305,203 +312,335 @@ __device__ __forceinline__ uint32_t block_max_1024(uint32_t v, uint32_t* red) {
   __syncthreads();
   uint32_t r = 0;
 #pragma unroll
-  for (int i = 0; i < kStreamThreads / 64; ++i) r = umax(r, red[i]);
+  for (int i = 0; i < kStreamWaves; ++i) r = umax(r, red[i]);
   __syncthreads();
   return r;
 }
 
-template <bool XBF16, bool XF16, bool YBF16>
+// f16 pair (h, h) for one E4M3 byte, h = E4M3 value * 2^-8 exactly: the byte's
+// exponent and mantissa fields drop into the f16 fields (bias 7 against 15
+// gives the 2^-8, E4M3 subnormals land on f16 subnormals) and its sign bit on
+// the sign.  Bytes 0x7f / 0xff (NaN) read as +-480; quantizers never emit them.
+__device__ __forceinline__ v2h e4m3_h2(uint32_t byte) {
+  const uint32_t h = ((byte & 0x80u) << 8) | ((byte & 0x7fu) << 7);
+  return __builtin_bit_cast(v2h, h | (h << 16));
+}
+
+// The 8 values E2M1(code) * E4M3 of one dword of codes: the conversion scales
+// by 2^8 (exact), and the f16 product with E4M3 * 2^-8 is exact (at most 6
+// significant bits, magnitude in [2^-10, 2688]).
+__device__ __forceinline__ v8h dq8(uint32_t codes, v2h s) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s;
+  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// K order inside a pair (256 values of a 16-row strip): lane (b = l % 16,
+// g = l / 16) feeds W row b and batch row b with values [64g + 32st, +32) in
+// step st, 8 per MFMA; x' and W use the same order, so each MFMA sums the same
+// products.  A lane's W scales for a pair are then 4 contiguous bytes.
+//
+// W scale bytes (SCM):
+//   kScaleBlock  K % 256 == 0, 16-aligned scales, kPairs <= E pairs per part and
+//                at most kSB KB of scales per part: at
+//                a round's first element a wave loads its part of the strip's
+//                scales, 16 rows x E * 16 bytes, with fully coalesced 16-byte
+//                loads into registers, then stores them to its LDS area at the
+//                first compute of the round; each pair reads its dword there.
+//   kScaleDword  K % 64 == 0, 4-aligned: one dword load per pair.
+//   kScaleHalf   otherwise: two 16-bit loads per pair.
+constexpr int kScaleHalf = 0, kScaleDword = 1, kScaleBlock = 2;
+constexpr int kSB = 3;                          // scale-block 16-byte loads per lane (max)
+
+template <bool XBF16, bool XF16, int SCM>
 __global__ void __launch_bounds__(kStreamThreads, 1)
     k_gemv_stream(const void* __restrict__ x, int B, const uint8_t* __restrict__ W,
                   const uint8_t* __restrict__ w_scales, const float* __restrict__ g_w, int N,
-                  int K, int Kq, int lds_x_bytes, float g_d, void* __restrict__ y) {
+                  int K, int Kq, int lds_x_bytes, float g_d, void* __restrict__ y, bool YBF16) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ uint32_t red[kStreamThreads / 64];
+  __shared__ uint32_t red_max[kStreamWaves];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = lane & 15, g = lane >> 4;
+  const int r8 = lane >> 3, c8 = lane & 7;
   const int nstrips = (N + 15) / 16;
-  const int64_t wrow_bytes = K / 2, srow_bytes = K / 16;
-  // LDS layout of the quantized x (zero past K up to Kq, a multiple of 256)
+  const int wrow = K / 2, srow = K / 16;
+  // LDS: x' (zero past K up to Kq, a multiple of 256) | transpose tiles | partial tiles
   const int xf_row = Kq * 2 + 16;                // XF16: fp16 row stride (bytes)
   const int xc_row = Kq / 2 + 16;                // codes row stride
-  uint8_t* xs_base = lds + B * xc_row;           // scale bytes [B][Kq/16]
+  const int bpr = Kq / 16;                       // x blocks per padded row
+  uint8_t* xs_base = lds + B * xc_row;           // scale bytes [B][bpr]
+  uint8_t* tb = lds + lds_x_bytes + wave * 2048;
+  v4f* red = reinterpret_cast<v4f*>(lds + lds_x_bytes + kStreamWaves * 2048);
 
-  // A wave's work is a sequence of elements (strip si, pair pp): pair pp holds
-  // the two 128-value steps 2pp, 2pp+1 of strip gw + si * nwt, pp < Pq.  Strips
-  // are dealt wave-major so every CU gets the same number of streaming waves.
-  // HBM is read as 8 rows x 128 contiguous bytes per instruction (lane l: row
-  // l/8, 16-byte chunk l%8), two instructions per pair.  Loads are branch-free
-  // and their results used unmodified, so kPairs pairs stay in flight: past K
-  // the addresses are clamped to the row's last 32 values, which are finite
-  // (E2M1 codes, E4M3 scales of real blocks) and meet x' = 0 there, so they add
-  // exact zeros; rows past N (and loads past the wave's last element) are
-  // clamped into the matrix and their results never stored.
-  const int Pq = Kq / 256;
-  const int nwt = gridDim.x * (kStreamThreads / 64);
-  const int gw = wave * gridDim.x + blockIdx.x;
-  const int nmine = gw < nstrips ? (nstrips - gw + nwt - 1) / nwt : 0;
-  const int J = nmine * Pq;
-  const int r8 = lane >> 3, c8 = lane & 7;
-  u32x4 ra[kPairs], rb[kPairs];
-  uint32_t rs0[kPairs], rs1[kPairs];
-  auto load_pair = [&](int si, int pp, u32x4& a, u32x4& bb, uint32_t& s0, uint32_t& s1) {
-    const int strip = gw + si * nwt;
-    const int vidx = 256 * pp + 32 * c8;
-    const int vcl = min(vidx, K - 32);
-    const int ra_ = min(strip * 16 + r8, N - 1), rb_ = min(strip * 16 + 8 + r8, N - 1);
-    a = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(W + (int64_t)ra_ * wrow_bytes + vcl / 2));
-    bb = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(W + (int64_t)rb_ * wrow_bytes + vcl / 2));
-    // scale bytes for this lane's MFMA position (W row b, values [32g, 32g+32) of each step)
-    const int row = min(strip * 16 + b, N - 1);
-    const int v0 = 256 * pp + 32 * g, v1 = v0 + 128;
-    const uint8_t* sr = w_scales + (int64_t)row * srow_bytes;
-    s0 = *reinterpret_cast<const uint16_t*>(sr + min(v0, K - 32) / 16);
-    s1 = *reinterpret_cast<const uint16_t*>(sr + min(v1, K - 32) / 16);
+  // ---- x: first blocks into registers (thread t owns blocks t + i * 1024)
+  constexpr int VPB = XBF16 ? 2 : 4;             // 16-byte vectors per 16-value block
+  constexpr int kXB = kXRegVecs / VPB;
+  const int nblk = B * bpr;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  auto block_src = [&](int blk, bool& ok) {
+    const int row = blk / bpr, c0 = (blk - row * bpr) * 16;
+    ok = blk < nblk && c0 < K;
+    return xv + (ok ? ((int64_t)row * K + c0) / (16 / VPB) : 0);
   };
-  int lsi = 0, lpp = 0;   // next element to load
+  u32x4 xr[kXB][VPB];
 #pragma unroll
-  for (int i = 0; i < kPairs; ++i) {
-    load_pair(lsi, lpp, ra[i], rb[i], rs0[i], rs1[i]);
-    if (++lpp == Pq) { lpp = 0; ++lsi; }
+  for (int i = 0; i < kXB; ++i) {
+    bool ok;
+    const u32x4* src = block_src(threadIdx.x + i * kStreamThreads, ok);
+#pragma unroll
+    for (int v = 0; v < VPB; ++v) xr[i][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // ---- x -> NVFP4 (global amax over all of [B, K], then per 16-value block)
-  const int64_t n = (int64_t)B * K;
-  uint32_t m = 0;
-  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-  for (int64_t i = threadIdx.x; i < n / (XBF16 ? 8 : 4); i += kStreamThreads) {
-    const u32x4 v = xv[i];
-    if (XBF16) {
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  // ---- W ring: a wave's elements are (round r, pair pp) for pp in its part
+  const int part = wave / kSlots, slot = wave - part * kSlots;
+  const int Pq = Kq / 256;
+  const int Ph = (Pq + kSplit - 1) / kSplit;
+  const int pbeg = min(part * Ph, Pq), pend = min(pbeg + Ph, Pq);
+  const int E = pend - pbeg;
+  const int G = gridDim.x * kSlots;              // strips per round
+  const int s_first = slot * gridDim.x + blockIdx.x;
+  const int R = (nstrips + G - 1) / G;
+  const int nmine = s_first < nstrips ? (nstrips - s_first + G - 1) / G : 0;
+  const int J = nmine * E;
+  // Loads are branch-free and their results used unmodified, so kPairs pairs
+  // stay in flight.  Past K the offsets are clamped onto the row (K % 32 == 0:
+  // a 32-value chunk is wholly inside or outside, and with SC4 so is a lane's
+  // 64-value scale dword); those values are finite and meet x' = 0, so they add
+  // exact zeros.  Rows past N, and loads past the wave's last element, are
+  // clamped into the matrix and their results never stored.
+  u32x4 ra[kPairs], rb[kPairs];
+  uint32_t rs[kPairs];
+  // scale block: lane l's k-th load takes 16-byte chunk q = 64k + l of the
+  // part's [16 rows][E chunks] block (clamped to the last chunk)
+  u32x4 sbv[kSB];
+  int sb_row[kSB], sb_col[kSB];
+  const int nsb = (16 * E + 63) / 64;
+  uint8_t* sa = lds + lds_x_bytes + kStreamWaves * 2048 + kRedBytes + wave * nsb * 1024;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t a = w4[j] & 0x7fff7fffu;
-        m = umax(m, umax(a << 16, a & 0xffff0000u));
+  for (int k = 0; k < kSB; ++k) {
+    const int q = min(64 * k + lane, max(16 * E - 1, 0));
+    const int rq = E > 0 ? q / E : 0;
+    sb_row[k] = rq;
+    sb_col[k] = 16 * (pbeg + q - rq * E);
+  }
+  int lr = 0, lpp = pbeg;
+  auto load_elem = [&](u32x4& a, u32x4& bb, uint32_t& sc) {
+    const int r0 = (s_first + lr * G) * 16;
+    const int off = min(128 * lpp + 16 * c8, wrow - 16);
+    a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        W + (int64_t)min(r0 + r8, N - 1) * wrow + off));
+    bb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        W + (int64_t)min(r0 + 8 + r8, N - 1) * wrow + off));
+    if (SCM == kScaleBlock) {
+      if (lpp == pbeg) {
+#pragma unroll
+        for (int k = 0; k < kSB; ++k)
+          if (k < nsb)
+            sbv[k] = *reinterpret_cast<const u32x4*>(
+                w_scales + (int64_t)min(r0 + sb_row[k], N - 1) * srow + sb_col[k]);
       }
     } else {
-      m = umax(umax(m, v.x & 0x7fffffffu),
-               umax(v.y & 0x7fffffffu, umax(v.z & 0x7fffffffu, v.w & 0x7fffffffu)));
-    }
-  }
-  const float s_gx = nv_global_scale(__uint_as_float(block_max_1024(m, red)));
-  const int bpr = Kq / 16;
-  for (int blk = threadIdx.x; blk < B * bpr; blk += kStreamThreads) {
-    const int row = blk / bpr, c0 = (blk - row * bpr) * 16;
-    uint32_t c[2] = {0u, 0u}, sc = 0u;
-    if (c0 < K) {
-      float v[16];
-      const int64_t base = (int64_t)row * K + c0;
-      if (XBF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + base);
-        const u32x4 a = p[0], e = p[1];
-        const uint32_t w8[8] = {a.x, a.y, a.z, a.w, e.x, e.y, e.z, e.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          v[2 * j] = bf16_lo(w8[j]);
-          v[2 * j + 1] = bf16_hi(w8[j]);
-        }
+      const uint8_t* sr = w_scales + (int64_t)min(r0 + b, N - 1) * srow;
+      if (SCM == kScaleDword) {
+        sc = *reinterpret_cast<const uint32_t*>(sr + min(16 * lpp + 4 * g, srow - 4));
       } else {
-        const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + base);
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(sr + min(16 * lpp + 4 * g, srow - 2));
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(sr + min(16 * lpp + 4 * g + 2, srow - 2));
+        sc = lo | (hi << 16);
+      }
+    }
+    if (++lpp >= pend) { lpp = pbeg; ++lr; }
+  };
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 a = p[j];
-          v[4 * j] = a.x;
-          v[4 * j + 1] = a.y;
-          v[4 * j + 2] = a.z;
-          v[4 * j + 3] = a.w;
+  for (int i = 0; i < kPairs; ++i) load_elem(ra[i], rb[i], rs[i]);
+
+  // ---- x -> NVFP4 (global amax over all of [B, K], then per 16-value block)
+  auto vec_absmax = [&](const u32x4& v) {
+    if (XBF16) {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t t = w4[j] & 0x7fff7fffu;
+        m = umax(m, umax(t << 16, t & 0xffff0000u));
+      }
+      return m;
+    }
+    return umax(umax(v.x & 0x7fffffffu, v.y & 0x7fffffffu),
+                umax(v.z & 0x7fffffffu, v.w & 0x7fffffffu));
+  };
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kXB; ++i)
+#pragma unroll
+    for (int v = 0; v < VPB; ++v) m = umax(m, vec_absmax(xr[i][v]));
+  for (int blk0 = threadIdx.x + kXB * kStreamThreads; blk0 < nblk; blk0 += 2 * kStreamThreads) {
+    u32x4 t[2][VPB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bool ok;
+      const u32x4* src = block_src(blk0 + h * kStreamThreads, ok);
+#pragma unroll
+      for (int v = 0; v < VPB; ++v) t[h][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < VPB; ++v) m = umax(m, vec_absmax(t[h][v]));
+  }
+  const float s_gx = nv_global_scale(__uint_as_float(block_max_1024(m, red_max)));
+  auto quant_block = [&](int blk, const u32x4 (&vv)[VPB]) {
+    const int row = blk / bpr, c0 = (blk - row * bpr) * 16;
+    float v[16];
+    if (XBF16) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w4[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[8 * j + 2 * q] = bf16_lo(w4[q]);
+          v[8 * j + 2 * q + 1] = bf16_hi(w4[q]);
         }
       }
-      uint32_t am = 0;
+    } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
-      float r;
-      nv_block_scale(__uint_as_float(am), s_gx, sc, r);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
-      c[0] = e2m1_pack8(v);
-      c[1] = e2m1_pack8(v + 8);
+      for (int j = 0; j < 4; ++j) {
+        v[4 * j] = __uint_as_float(vv[j].x);
+        v[4 * j + 1] = __uint_as_float(vv[j].y);
+        v[4 * j + 2] = __uint_as_float(vv[j].z);
+        v[4 * j + 3] = __uint_as_float(vv[j].w);
+      }
     }
+    uint32_t am = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
+    uint32_t sc;
+    float r;
+    nv_block_scale(__uint_as_float(am), s_gx, sc, r);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
+    uint32_t c[2] = {e2m1_pack8(v), e2m1_pack8(v + 8)};
+    if (c0 >= K) c[0] = c[1] = sc = 0u;        // padding past K: x' = 0
     if (XF16) {
-      float p2;
-      v2h mt;
-      e4m3_split(sc, p2, mt);
-      const v8h h0 = dequant8(c[0], p2, mt), h1 = dequant8(c[1], p2, mt);    // exact x'
+      const v2h h = e4m3_h2(sc);
       v8h* dst = reinterpret_cast<v8h*>(lds + row * xf_row + c0 * 2);
-      dst[0] = h0;
-      dst[1] = h1;
+      dst[0] = dq8(c[0], h);
+      dst[1] = dq8(c[1], h);
     } else {
       *reinterpret_cast<u32x2*>(lds + row * xc_row + c0 / 2) = u32x2{c[0], c[1]};
       xs_base[row * bpr + c0 / 16] = (uint8_t)sc;
     }
+  };
+#pragma unroll
+  for (int i = 0; i < kXB; ++i) {
+    const int blk = threadIdx.x + i * kStreamThreads;
+    if (blk < nblk) quant_block(blk, xr[i]);
+  }
+  for (int blk = threadIdx.x + kXB * kStreamThreads; blk < nblk; blk += kStreamThreads) {
+    bool ok;
+    const u32x4* src = block_src(blk, ok);
+    u32x4 t[VPB];
+#pragma unroll
+    for (int v = 0; v < VPB; ++v) t[v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+    quant_block(blk, t);
   }
   __syncthreads();
   const float gscale = s_gx * (*g_w);
-  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
   // ---- stream W
-  // wave-private transpose buffer: row r's 128 bytes at r*128, 16-byte chunk c
-  // stored at position c ^ (r & 7) so both the row-wise writes and the
-  // MFMA-layout reads hit distinct banks
-  uint8_t* tb = lds + lds_x_bytes + wave * 2048;
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int csi = 0, cpp = 0;   // element being computed
+  // Transpose tile (wave-private, 16 rows x 128 bytes): 16-byte chunk c of row
+  // r sits at chunk position c ^ (r & 7) ^ 4 (r >> 3), so the row-wise writes
+  // and the MFMA-layout reads (rows b and b + 8 apart by 4 chunks) spread over
+  // the banks.
+  const int xrow = min(b, B - 1);               // batch rows >= B: any finite x, never stored
+  auto finish = [&](int r, v4f a, bool valid) {
+    if (kSplit > 1) {
+      v4f* rp = red + ((r & 1) * kSlots + slot) * 64;
+      if (part != 0) rp[lane] = a;
+      __syncthreads();
+      if (part != 0) return;
+      a += rp[lane];
+    }
+    if (!valid) return;
+    const int nn = (s_first + r * G) * 16 + b;   // D[4g + q][b] of this strip
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ob = 4 * g + q;
+      if (ob < B && nn < N) {
+        const float v = (a[q] * gscale) * g_d;
+        if (YBF16)
+          reinterpret_cast<uint16_t*>(y)[(int64_t)ob * N + nn] = (uint16_t)f32_to_bf16(v);
+        else
+          reinterpret_cast<float*>(y)[(int64_t)ob * N + nn] = v;
+      }
+    }
+  };
+  v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+  int cr = 0, cpp = pbeg;
+  const int wsw = (r8 ^ c8) << 4;
   for (int j0 = 0; j0 < J; j0 += kPairs) {
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
-      const u32x4 a = ra[i], bb = rb[i];
-      const uint32_t s0 = rs0[i], s1 = rs1[i];
-      load_pair(lsi, lpp, ra[i], rb[i], rs0[i], rs1[i]);
-      if (++lpp == Pq) { lpp = 0; ++lsi; }
-      if (j0 + i < J) {
-        *reinterpret_cast<u32x4*>(tb + r8 * 128 + ((c8 ^ r8) << 4)) = a;
-        *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + ((c8 ^ r8) << 4)) = bb;
+      const bool live = j0 + i < J;
+      uint32_t sw = rs[i];
+      if (live) {
+        if (SCM == kScaleBlock) {
+          if (cpp == pbeg) {
+#pragma unroll
+            for (int k = 0; k < kSB; ++k)
+              if (k < nsb) *reinterpret_cast<u32x4*>(sa + k * 1024 + lane * 16) = sbv[k];
+          }
+          sw = *reinterpret_cast<const uint32_t*>(sa + b * (16 * E) + 16 * (cpp - pbeg) + 4 * g);
+        }
+        *reinterpret_cast<u32x4*>(tb + r8 * 128 + wsw) = ra[i];
+        *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + (wsw ^ 64)) = rb[i];
+      }
+      load_elem(ra[i], rb[i], rs[i]);
+      if (live) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const u32x4 codes =
-              *reinterpret_cast<const u32x4*>(tb + b * 128 + (((4 * st + g) ^ (b & 7)) << 4));
-          const int t = 2 * cpp + st;
+          const int c = 2 * g + st;
+          const u32x4 codes = *reinterpret_cast<const u32x4*>(
+              tb + b * 128 + ((c ^ (b & 7) ^ ((b >> 3) << 2)) << 4));
+          const int v0 = 256 * cpp + 64 * g + 32 * st;   // first of this lane's 32 values
           v8h xq[4];
           if (XF16) {
-            const v8h* src = reinterpret_cast<const v8h*>(lds + min(b, B - 1) * xf_row + (128 * t + 32 * g) * 2);
+            const v8h* src = reinterpret_cast<const v8h*>(lds + xrow * xf_row + v0 * 2);
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) xq[s4] = b < B ? src[s4] : zero8;
+            for (int s4 = 0; s4 < 4; ++s4) xq[s4] = src[s4];
           } else {
-            const int bc = min(b, B - 1);
-            const u32x4 xc = *reinterpret_cast<const u32x4*>(lds + bc * xc_row + 64 * t + 16 * g);
-            const uint32_t xsb = b < B ? *reinterpret_cast<const uint16_t*>(xs_base + bc * bpr + 8 * t + 2 * g) : 0u;
-            float q0, q1;
-            v2h m0, m1;
-            e4m3_split(xsb & 0xffu, q0, m0);
-            e4m3_split(xsb >> 8, q1, m1);
-            xq[0] = dequant8(xc.x, q0, m0);
-            xq[1] = dequant8(xc.y, q0, m0);
-            xq[2] = dequant8(xc.z, q1, m1);
-            xq[3] = dequant8(xc.w, q1, m1);
+            const u32x4 xc = *reinterpret_cast<const u32x4*>(lds + xrow * xc_row + v0 / 2);
+            const uint32_t xsb = *reinterpret_cast<const uint16_t*>(xs_base + xrow * bpr + v0 / 16);
+            const v2h h0 = e4m3_h2(xsb & 0xffu), h1 = e4m3_h2(xsb >> 8);
+            xq[0] = dq8(xc.x, h0);
+            xq[1] = dq8(xc.y, h0);
+            xq[2] = dq8(xc.z, h1);
+            xq[3] = dq8(xc.w, h1);
           }
-          acc = mfma_step(acc, xq, codes, st ? s1 : s0);
+          const v2h w0 = e4m3_h2((sw >> (16 * st)) & 0xffu);
+          const v2h w1 = e4m3_h2((sw >> (16 * st + 8)) & 0xffu);
+          v4f& acc = st ? acc1 : acc0;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[0], dq8(codes.x, w0), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[1], dq8(codes.y, w0), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[2], dq8(codes.z, w1), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[3], dq8(codes.w, w1), acc, 0, 0, 0);
         }
-        if (cpp == Pq - 1) {   // end of a strip: D[4g + r][b] of this 16-row strip
-          const int nn = (gw + csi * nwt) * 16 + b;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ob = 4 * g + r;
-            if (ob < B && nn < N) {
-              const float v = (acc[r] * gscale) * g_d;
-              if (YBF16)
-                reinterpret_cast<uint16_t*>(y)[(int64_t)ob * N + nn] = (uint16_t)f32_to_bf16(v);
-              else
-                reinterpret_cast<float*>(y)[(int64_t)ob * N + nn] = v;
-            }
-          }
-          acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        if (cpp == pend - 1) {
+          finish(cr, acc0 + acc1, true);
+          acc0 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          acc1 = acc0;
         }
-        if (++cpp == Pq) { cpp = 0; ++csi; }
+        if (++cpp == pend) { cpp = pbeg; ++cr; }
       }
     }
   }
+  // Every wave takes part in all R rounds' exchanges: a wave whose part of K is
+  // empty (E == 0) contributes zeros for its valid rounds, and rounds without a
+  // strip for this slot exchange nothing that is stored.
+  for (int r = E > 0 ? nmine : 0; r < R; ++r) finish(r, acc0, r < nmine);
 }
 
 // K = 0: every output is an empty sum.
@@ -516,6 +655,28 @@ __global__ void __launch_bounds__(256) k_zero_fill(int64_t n, void* __restrict__
 }
 
 int g_num_cus = 0;
+
+struct StreamArgs {
+  const void* x;
+  int B;
+  const uint8_t* W;
+  const uint8_t* w_scales;
+  const float* g_w;
+  int N, K, Kq, lds_x;
+  float g_d;
+  void* y;
+  bool y_bf16;
+};
+
+template <bool XB, bool XF, int SCM>
+hipError_t launch_stream(const StreamArgs& a, int grid, int lds, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&k_gemv_stream<XB, XF, SCM>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gemv_stream<XB, XF, SCM>), dim3(grid), dim3(kStreamThreads), lds, stream,
+                     a.x, a.B, a.W, a.w_scales, a.g_w, a.N, a.K, a.Kq, a.lds_x, a.g_d, a.y, a.y_bf16);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -554,28 +715,40 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   const int64_t Kq = (K + 255) / 256 * 256;
   const int64_t lds_f16 = B * (Kq * 2 + 16);
   const int64_t lds_fp4 = B * (Kq / 2 + 16) + B * (Kq / 16);
-  const bool xf16 = lds_f16 <= 96 * 1024;
-  if (xf16 || lds_fp4 <= 120 * 1024) {
+  const int Pq = (int)(Kq / 256);
+  const int E = (Pq + kSplit - 1) / kSplit;
+  const int nsb = (16 * E + 63) / 64;
+  int scm = kScaleHalf;
+  if (K % 64 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 4 == 0) scm = kScaleDword;
+  // scale blocks: one register copy, so the next round's block (loaded kPairs
+  // elements ahead) must not arrive before this round's first compute: E >= kPairs
+  if (K % 256 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 16 == 0 && nsb <= kSB &&
+      E >= kPairs)
+    scm = kScaleBlock;
+  const int64_t lds_fixed =
+      kStreamWaves * 2048 + kRedBytes + (scm == kScaleBlock ? kStreamWaves * nsb * 1024 : 0);
+  const int64_t lds_max = 160 * 1024 - 256;
+  const bool xf16 = lds_f16 + lds_fixed <= lds_max;
+  if (xf16 || lds_fp4 + lds_fixed <= lds_max) {
     const int lds_x = (int)(((xf16 ? lds_f16 : lds_fp4) + 15) / 16 * 16);
-    const int lds = lds_x + (kStreamThreads / 64) * 2048;
+    const int lds = lds_x + (int)lds_fixed;
     const int grid = nstrips < g_num_cus ? nstrips : g_num_cus;
-#define FP4_GEMV_STREAM(XB, XF, YB)                                                              \
-  do {                                                                                           \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<XB, XF, YB>), \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);        \
-    if (e != hipSuccess) return e;                                                               \
-    hipLaunchKernelGGL((k_gemv_stream<XB, XF, YB>), dim3(grid), dim3(kStreamThreads), lds,       \
-                       stream, x, (int)B, W, w_scales, g_w, (int)N, (int)K, (int)Kq, lds_x, g_d, y);    \
-  } while (0)
-    if (x_bf16) {
-      if (xf16) { if (y_bf16) FP4_GEMV_STREAM(true, true, true); else FP4_GEMV_STREAM(true, true, false); }
-      else { if (y_bf16) FP4_GEMV_STREAM(true, false, true); else FP4_GEMV_STREAM(true, false, false); }
-    } else {
-      if (xf16) { if (y_bf16) FP4_GEMV_STREAM(false, true, true); else FP4_GEMV_STREAM(false, true, false); }
-      else { if (y_bf16) FP4_GEMV_STREAM(false, false, true); else FP4_GEMV_STREAM(false, false, false); }
+    const StreamArgs sa{x, (int)B, W, w_scales, g_w, (int)N, (int)K, (int)Kq, lds_x, g_d, y, y_bf16};
+    const int sel = (x_bf16 ? 4 : 0) | (xf16 ? 2 : 0);
+    switch (sel * 3 + scm) {
+      case 0: return launch_stream<false, false, kScaleHalf>(sa, grid, lds, stream);
+      case 1: return launch_stream<false, false, kScaleDword>(sa, grid, lds, stream);
+      case 2: return launch_stream<false, false, kScaleBlock>(sa, grid, lds, stream);
+      case 6: return launch_stream<false, true, kScaleHalf>(sa, grid, lds, stream);
+      case 7: return launch_stream<false, true, kScaleDword>(sa, grid, lds, stream);
+      case 8: return launch_stream<false, true, kScaleBlock>(sa, grid, lds, stream);
+      case 12: return launch_stream<true, false, kScaleHalf>(sa, grid, lds, stream);
+      case 13: return launch_stream<true, false, kScaleDword>(sa, grid, lds, stream);
+      case 14: return launch_stream<true, false, kScaleBlock>(sa, grid, lds, stream);
+      case 18: return launch_stream<true, true, kScaleHalf>(sa, grid, lds, stream);
+      case 19: return launch_stream<true, true, kScaleDword>(sa, grid, lds, stream);
+      default: return launch_stream<true, true, kScaleBlock>(sa, grid, lds, stream);
     }
-#undef FP4_GEMV_STREAM
-    return hipGetLastError();
   }
 
   // very long K: x' through the workspace, waves split K

@@ -52,6 +52,20 @@ def test_gemv_long_k_and_wide_batch(B, N, K):
     _run_and_check(o.bf16_bits_to_f32(x), False, Wq, Ws, 0.02, N, K, 0.5, torch.bfloat16)
 
 
+@pytest.mark.parametrize("B,N,K", [(2, 40000, 2048), (3, 33000, 1056), (1, 36000, 4096),
+                                   (5, 2100, 1024)])
+def test_gemv_several_rounds(B, N, K):
+    """More 16-row strips than one pass of the workgroups takes (2048 per round
+    on 256 CUs), so strips come in rounds; covers the per-round exchange of the
+    two K halves, per-pair scale loads (K = 1056) and per-round scale blocks
+    with exactly as many pairs per half as the prefetch depth (K = 2048)."""
+    announce(f"gemv rounds B={B} N={N} K={K}")
+    Wq = workloads.random_codes((N, K // 2), seed=N + 1)
+    Ws = workloads.random_bytes((N, K // 16), 0x18, 0x58, seed=N + 2)
+    x = workloads.gemv_x(B, K, seed=N + 3)
+    _run_and_check(x, True, Wq, Ws, 0.02, N, K, 1.0, torch.float32)
+
+
 @pytest.mark.parametrize("B", [1, 4, 16])
 def test_gemv_decode_shape_all_outputs(B):
     """W 27648x5120 (the decode GEMV shape) with random valid NVFP4 codes and
