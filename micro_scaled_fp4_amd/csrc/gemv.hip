@@ -352,6 +352,8 @@ __device__ __forceinline__ v8h dq8(uint32_t codes, v2h s) {
 //   kScaleDword  K % 64 == 0, 4-aligned: one dword load per pair.
 //   kScaleHalf   otherwise: two 16-bit loads per pair.
 constexpr int kScaleHalf = 0, kScaleDword = 1, kScaleBlock = 2;
+constexpr int kBufferWord3 = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
+constexpr int kLoadNT = 2;                      // buffer load cache policy: nontemporal
 constexpr int kSB = 3;                          // scale-block 16-byte loads per lane (max)
 
 template <bool XBF16, bool XF16, int SCM>
@@ -427,30 +429,40 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     sb_col[k] = 16 * (pbeg + q - rq * E);
   }
   int lr = 0, lpp = pbeg;
+  // All W and W-scale reads are buffer loads through a per-strip descriptor
+  // whose range is the strip's rows that exist (N may end inside a strip).  A
+  // read outside the range returns zeros without touching memory, so the ring
+  // stays branch-free: look-ahead past the wave's last element gets an empty
+  // range, and reads past K run into the next row's codes (finite, against
+  // x' = 0) or off the range.  The lane's offset inside the strip is fixed; the
+  // pair's offset is a scalar.
+  const int w_lane = r8 * wrow + 16 * c8;
+  const int s_lane = b * srow + 4 * g;
+  int sb_off[kSB];
+#pragma unroll
+  for (int k = 0; k < kSB; ++k) sb_off[k] = sb_row[k] * srow + sb_col[k];
   auto load_elem = [&](u32x4& a, u32x4& bb, uint32_t& sc) {
-    const int r0 = (s_first + lr * G) * 16;
-    const int off = min(128 * lpp + 16 * c8, wrow - 16);
-    a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        W + (int64_t)min(r0 + r8, N - 1) * wrow + off));
-    bb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        W + (int64_t)min(r0 + 8 + r8, N - 1) * wrow + off));
+    const bool beyond = lr >= nmine;
+    const int r0 = beyond ? 0 : (s_first + lr * G) * 16;
+    const int rows = beyond ? 0 : min(16, N - r0);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W) + (int64_t)r0 * wrow, 0, rows * wrow, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, rows * srow, kBufferWord3);
+    a = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, 128 * lpp, kLoadNT);
+    bb = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + 8 * wrow, 128 * lpp, kLoadNT);
     if (SCM == kScaleBlock) {
       if (lpp == pbeg) {
 #pragma unroll
         for (int k = 0; k < kSB; ++k)
-          if (k < nsb)
-            sbv[k] = *reinterpret_cast<const u32x4*>(
-                w_scales + (int64_t)min(r0 + sb_row[k], N - 1) * srow + sb_col[k]);
+          if (k < nsb) sbv[k] = __builtin_amdgcn_raw_buffer_load_b128(rsc, sb_off[k], 0, 0);
       }
+    } else if (SCM == kScaleDword) {
+      sc = __builtin_amdgcn_raw_buffer_load_b32(rsc, s_lane, 16 * lpp, 0);
     } else {
-      const uint8_t* sr = w_scales + (int64_t)min(r0 + b, N - 1) * srow;
-      if (SCM == kScaleDword) {
-        sc = *reinterpret_cast<const uint32_t*>(sr + min(16 * lpp + 4 * g, srow - 4));
-      } else {
-        const uint32_t lo = *reinterpret_cast<const uint16_t*>(sr + min(16 * lpp + 4 * g, srow - 2));
-        const uint32_t hi = *reinterpret_cast<const uint16_t*>(sr + min(16 * lpp + 4 * g + 2, srow - 2));
-        sc = lo | (hi << 16);
-      }
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_lane, 16 * lpp, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_lane + 2, 16 * lpp, 0);
+      sc = lo | (hi << 16);
     }
     if (++lpp >= pend) { lpp = pbeg; ++lr; }
   };
@@ -581,61 +593,62 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
   int cr = 0, cpp = pbeg;
   const int wsw = (r8 ^ c8) << 4;
+  // One element from ring slot i: stage its W codes (and at a round's first
+  // element its scale block) in LDS, refill the slot with the element kPairs
+  // ahead, then dequantize and accumulate.
+  auto elem = [&](u32x4& ra_i, u32x4& rb_i, uint32_t& rs_i) {
+    uint32_t sw = rs_i;
+    if (SCM == kScaleBlock) {
+      if (cpp == pbeg) {
+#pragma unroll
+        for (int k = 0; k < kSB; ++k)
+          if (k < nsb) *reinterpret_cast<u32x4*>(sa + k * 1024 + lane * 16) = sbv[k];
+      }
+      sw = *reinterpret_cast<const uint32_t*>(sa + b * (16 * E) + 16 * (cpp - pbeg) + 4 * g);
+    }
+    *reinterpret_cast<u32x4*>(tb + r8 * 128 + wsw) = ra_i;
+    *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + (wsw ^ 64)) = rb_i;
+    load_elem(ra_i, rb_i, rs_i);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int c = 2 * g + st;
+      const u32x4 codes = *reinterpret_cast<const u32x4*>(
+          tb + b * 128 + ((c ^ (b & 7) ^ ((b >> 3) << 2)) << 4));
+      const int v0 = 256 * cpp + 64 * g + 32 * st;   // first of this lane's 32 values
+      v8h xq[4];
+      if (XF16) {
+        const v8h* src = reinterpret_cast<const v8h*>(lds + xrow * xf_row + v0 * 2);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) xq[s4] = src[s4];
+      } else {
+        const u32x4 xc = *reinterpret_cast<const u32x4*>(lds + xrow * xc_row + v0 / 2);
+        const uint32_t xsb = *reinterpret_cast<const uint16_t*>(xs_base + xrow * bpr + v0 / 16);
+        const v2h h0 = e4m3_h2(xsb & 0xffu), h1 = e4m3_h2(xsb >> 8);
+        xq[0] = dq8(xc.x, h0);
+        xq[1] = dq8(xc.y, h0);
+        xq[2] = dq8(xc.z, h1);
+        xq[3] = dq8(xc.w, h1);
+      }
+      const v2h w0 = e4m3_h2((sw >> (16 * st)) & 0xffu);
+      const v2h w1 = e4m3_h2((sw >> (16 * st + 8)) & 0xffu);
+      v4f& acc = st ? acc1 : acc0;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[0], dq8(codes.x, w0), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[1], dq8(codes.y, w0), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[2], dq8(codes.z, w1), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[3], dq8(codes.w, w1), acc, 0, 0, 0);
+    }
+    if (cpp == pend - 1) {
+      finish(cr, acc0 + acc1, true);
+      acc0 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      acc1 = acc0;
+    }
+    if (++cpp == pend) { cpp = pbeg; ++cr; }
+  };
+  // element j lives in slot j % kPairs and is refilled with element j + kPairs
   for (int j0 = 0; j0 < J; j0 += kPairs) {
 #pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const bool live = j0 + i < J;
-      uint32_t sw = rs[i];
-      if (live) {
-        if (SCM == kScaleBlock) {
-          if (cpp == pbeg) {
-#pragma unroll
-            for (int k = 0; k < kSB; ++k)
-              if (k < nsb) *reinterpret_cast<u32x4*>(sa + k * 1024 + lane * 16) = sbv[k];
-          }
-          sw = *reinterpret_cast<const uint32_t*>(sa + b * (16 * E) + 16 * (cpp - pbeg) + 4 * g);
-        }
-        *reinterpret_cast<u32x4*>(tb + r8 * 128 + wsw) = ra[i];
-        *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + (wsw ^ 64)) = rb[i];
-      }
-      load_elem(ra[i], rb[i], rs[i]);
-      if (live) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int c = 2 * g + st;
-          const u32x4 codes = *reinterpret_cast<const u32x4*>(
-              tb + b * 128 + ((c ^ (b & 7) ^ ((b >> 3) << 2)) << 4));
-          const int v0 = 256 * cpp + 64 * g + 32 * st;   // first of this lane's 32 values
-          v8h xq[4];
-          if (XF16) {
-            const v8h* src = reinterpret_cast<const v8h*>(lds + xrow * xf_row + v0 * 2);
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) xq[s4] = src[s4];
-          } else {
-            const u32x4 xc = *reinterpret_cast<const u32x4*>(lds + xrow * xc_row + v0 / 2);
-            const uint32_t xsb = *reinterpret_cast<const uint16_t*>(xs_base + xrow * bpr + v0 / 16);
-            const v2h h0 = e4m3_h2(xsb & 0xffu), h1 = e4m3_h2(xsb >> 8);
-            xq[0] = dq8(xc.x, h0);
-            xq[1] = dq8(xc.y, h0);
-            xq[2] = dq8(xc.z, h1);
-            xq[3] = dq8(xc.w, h1);
-          }
-          const v2h w0 = e4m3_h2((sw >> (16 * st)) & 0xffu);
-          const v2h w1 = e4m3_h2((sw >> (16 * st + 8)) & 0xffu);
-          v4f& acc = st ? acc1 : acc0;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[0], dq8(codes.x, w0), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[1], dq8(codes.y, w0), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[2], dq8(codes.z, w1), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[3], dq8(codes.w, w1), acc, 0, 0, 0);
-        }
-        if (cpp == pend - 1) {
-          finish(cr, acc0 + acc1, true);
-          acc0 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-          acc1 = acc0;
-        }
-        if (++cpp == pend) { cpp = pbeg; ++cr; }
-      }
-    }
+    for (int i = 0; i < kPairs; ++i)
+      if (j0 + i < J) elem(ra[i], rb[i], rs[i]);
   }
   // Every wave takes part in all R rounds' exchanges: a wave whose part of K is
   // empty (E == 0) contributes zeros for its valid rounds, and rounds without a
@@ -729,7 +742,9 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
       kStreamWaves * 2048 + kRedBytes + (scm == kScaleBlock ? kStreamWaves * nsb * 1024 : 0);
   const int64_t lds_max = 160 * 1024 - 256;
   const bool xf16 = lds_f16 + lds_fixed <= lds_max;
-  if (xf16 || lds_fp4 + lds_fixed <= lds_max) {
+  // (the strip-relative buffer offsets need 16 rows of W to span < 2^31 bytes;
+  // the x' sizes above already keep K far below that)
+  if ((xf16 || lds_fp4 + lds_fixed <= lds_max) && K < (1 << 27)) {
     const int lds_x = (int)(((xf16 ? lds_f16 : lds_fp4) + 15) / 16 * 16);
     const int lds = lds_x + (int)lds_fixed;
     const int grid = nstrips < g_num_cus ? nstrips : g_num_cus;
