@@ -306,6 +306,11 @@ constexpr int kPairs = 4;                       // pairs of steps in flight per 
 constexpr int kXRegVecs = 4;                    // 16-byte x vectors per thread held in registers
 constexpr int kRedBytes = 2 * kSlots * 64 * 16; // double-buffered partial tiles
 
+__host__ __device__ inline int xf16_row_bytes(int Kq) {
+  const int base = Kq * 2 + Kq / 4;
+  return base + ((64 - base % 256) & 255);
+}
+
 __device__ __forceinline__ uint32_t block_max_1024(uint32_t v, uint32_t* red) {
   v = wave_max_u32(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
@@ -343,18 +348,15 @@ __device__ __forceinline__ v8h dq8(uint32_t codes, v2h s) {
 // products.  A lane's W scales for a pair are then 4 contiguous bytes.
 //
 // W scale bytes (SCM):
-//   kScaleBlock  K % 256 == 0, 16-aligned scales, kPairs <= E pairs per part and
-//                at most kSB KB of scales per part: at
-//                a round's first element a wave loads its part of the strip's
-//                scales, 16 rows x E * 16 bytes, with fully coalesced 16-byte
-//                loads into registers, then stores them to its LDS area at the
-//                first compute of the round; each pair reads its dword there.
+//   kScaleGroup  K % 256 == 0 and 16-aligned scales: the group's scales, 16 rows x
+//                kPairs * 16 bytes, arrive with one 16-byte load per lane issued
+//                with the group before (ring slot 0), pass through a 1 KB LDS
+//                area per wave, and each pair reads its dword there.
 //   kScaleDword  K % 64 == 0, 4-aligned: one dword load per pair.
 //   kScaleHalf   otherwise: two 16-bit loads per pair.
-constexpr int kScaleHalf = 0, kScaleDword = 1, kScaleBlock = 2;
+constexpr int kScaleHalf = 0, kScaleDword = 1, kScaleGroup = 2;
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
 constexpr int kLoadNT = 2;                      // buffer load cache policy: nontemporal
-constexpr int kSB = 3;                          // scale-block 16-byte loads per lane (max)
 
 template <bool XBF16, bool XF16, int SCM>
 __global__ void __launch_bounds__(kStreamThreads, 1)
@@ -370,7 +372,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   const int nstrips = (N + 15) / 16;
   const int wrow = K / 2, srow = K / 16;
   // LDS: x' (zero past K up to Kq, a multiple of 256) | transpose tiles | partial tiles
-  const int xf_row = Kq * 2 + 16;                // XF16: fp16 row stride (bytes)
+  // XF16 x' row: value v at byte 2v + 16 (v / 64), rows 64 bytes apart modulo
+  // 256, so the four lane groups' 32-value reads (and up to 4 batch rows) fall
+  // on distinct LDS banks
+  const int xf_row = xf16_row_bytes(Kq);
   const int xc_row = Kq / 2 + 16;                // codes row stride
   const int bpr = Kq / 16;                       // x blocks per padded row
   uint8_t* xs_base = lds + B * xc_row;           // scale bytes [B][bpr]
@@ -396,78 +401,68 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     for (int v = 0; v < VPB; ++v) xr[i][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // ---- W ring: a wave's elements are (round r, pair pp) for pp in its part
+  // ---- W ring: a wave's elements are (round r, pair pbeg + e), e < Ep
   const int part = wave / kSlots, slot = wave - part * kSlots;
   const int Pq = Kq / 256;
   const int Ph = (Pq + kSplit - 1) / kSplit;
   const int pbeg = min(part * Ph, Pq), pend = min(pbeg + Ph, Pq);
   const int E = pend - pbeg;
+  // a round is padded to whole groups of kPairs elements, so every loop
+  // iteration below runs all kPairs ring slots; padding elements read nothing
+  // (empty range) and are not computed
+  const int Ep = (E + kPairs - 1) / kPairs * kPairs;
   const int G = gridDim.x * kSlots;              // strips per round
   const int s_first = slot * gridDim.x + blockIdx.x;
   const int R = (nstrips + G - 1) / G;
   const int nmine = s_first < nstrips ? (nstrips - s_first + G - 1) / G : 0;
-  const int J = nmine * E;
-  // Loads are branch-free and their results used unmodified, so kPairs pairs
-  // stay in flight.  Past K the offsets are clamped onto the row (K % 32 == 0:
-  // a 32-value chunk is wholly inside or outside, and with SC4 so is a lane's
-  // 64-value scale dword); those values are finite and meet x' = 0, so they add
-  // exact zeros.  Rows past N, and loads past the wave's last element, are
-  // clamped into the matrix and their results never stored.
-  u32x4 ra[kPairs], rb[kPairs];
-  uint32_t rs[kPairs];
-  // scale block: lane l's k-th load takes 16-byte chunk q = 64k + l of the
-  // part's [16 rows][E chunks] block (clamped to the last chunk)
-  u32x4 sbv[kSB];
-  int sb_row[kSB], sb_col[kSB];
-  const int nsb = (16 * E + 63) / 64;
-  uint8_t* sa = lds + lds_x_bytes + kStreamWaves * 2048 + kRedBytes + wave * nsb * 1024;
-#pragma unroll
-  for (int k = 0; k < kSB; ++k) {
-    const int q = min(64 * k + lane, max(16 * E - 1, 0));
-    const int rq = E > 0 ? q / E : 0;
-    sb_row[k] = rq;
-    sb_col[k] = 16 * (pbeg + q - rq * E);
-  }
-  int lr = 0, lpp = pbeg;
+  const int J = nmine * Ep;
   // All W and W-scale reads are buffer loads through a per-strip descriptor
   // whose range is the strip's rows that exist (N may end inside a strip).  A
-  // read outside the range returns zeros without touching memory, so the ring
-  // stays branch-free: look-ahead past the wave's last element gets an empty
-  // range, and reads past K run into the next row's codes (finite, against
-  // x' = 0) or off the range.  The lane's offset inside the strip is fixed; the
-  // pair's offset is a scalar.
+  // read outside the range returns zeros without touching memory, so every
+  // loop iteration issues the same loads with no branch around them (which
+  // keeps kPairs elements in flight): look-ahead past the wave's last element
+  // and padding elements get an empty range, and reads past K run into the
+  // next row's codes (finite, against x' = 0) or off the range.  The lane's
+  // offset inside the strip is fixed; the pair's offset is a scalar.
+  u32x4 ra[kPairs], rb[kPairs];
+  uint32_t rs[kPairs];
+  u32x4 sg;                                      // scale group in flight
   const int w_lane = r8 * wrow + 16 * c8;
   const int s_lane = b * srow + 4 * g;
-  int sb_off[kSB];
-#pragma unroll
-  for (int k = 0; k < kSB; ++k) sb_off[k] = sb_row[k] * srow + sb_col[k];
-  auto load_elem = [&](u32x4& a, u32x4& bb, uint32_t& sc) {
-    const bool beyond = lr >= nmine;
-    const int r0 = beyond ? 0 : (s_first + lr * G) * 16;
-    const int rows = beyond ? 0 : min(16, N - r0);
+  const int g_lane = b * srow + 16 * g;          // group load: row b, pair g of the group
+  uint8_t* sa = lds + lds_x_bytes + kStreamWaves * 2048 + kRedBytes + wave * 1024;
+  int lr = 0, le = 0;                            // next element to load
+  auto load_elem = [&](u32x4& a, u32x4& bb, uint32_t& sc, bool group) {
+    const bool live = lr < nmine && le < E;
+    const int r0 = lr < nmine ? (s_first + lr * G) * 16 : 0;
+    const int rows = live ? min(16, N - r0) : 0;
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(W) + (int64_t)r0 * wrow, 0, rows * wrow, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, rows * srow, kBufferWord3);
-    a = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, 128 * lpp, kLoadNT);
-    bb = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + 8 * wrow, 128 * lpp, kLoadNT);
-    if (SCM == kScaleBlock) {
-      if (lpp == pbeg) {
-#pragma unroll
-        for (int k = 0; k < kSB; ++k)
-          if (k < nsb) sbv[k] = __builtin_amdgcn_raw_buffer_load_b128(rsc, sb_off[k], 0, 0);
+    const int pp = pbeg + le;
+    a = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, 128 * pp, kLoadNT);
+    bb = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + 8 * wrow, 128 * pp, kLoadNT);
+    if (SCM == kScaleGroup) {
+      if (group) {   // the group's first element (le % kPairs == 0): its kPairs pairs
+        const int grows = lr < nmine ? min(16, N - r0) : 0;
+        const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, grows * srow, kBufferWord3);
+        sg = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane, 16 * pp, 0);
       }
-    } else if (SCM == kScaleDword) {
-      sc = __builtin_amdgcn_raw_buffer_load_b32(rsc, s_lane, 16 * lpp, 0);
     } else {
-      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_lane, 16 * lpp, 0);
-      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_lane + 2, 16 * lpp, 0);
-      sc = lo | (hi << 16);
+      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, rows * srow, kBufferWord3);
+      if (SCM == kScaleDword) {
+        sc = __builtin_amdgcn_raw_buffer_load_b32(rsc, s_lane, 16 * pp, 0);
+      } else {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_lane, 16 * pp, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_lane + 2, 16 * pp, 0);
+        sc = lo | (hi << 16);
+      }
     }
-    if (++lpp >= pend) { lpp = pbeg; ++lr; }
+    if (++le >= Ep) { le = 0; ++lr; }
   };
 #pragma unroll
-  for (int i = 0; i < kPairs; ++i) load_elem(ra[i], rb[i], rs[i]);
+  for (int i = 0; i < kPairs; ++i) load_elem(ra[i], rb[i], rs[i], i == 0);
 
   // ---- x -> NVFP4 (global amax over all of [B, K], then per 16-value block)
   auto vec_absmax = [&](const u32x4& v) {
@@ -538,7 +533,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     if (c0 >= K) c[0] = c[1] = sc = 0u;        // padding past K: x' = 0
     if (XF16) {
       const v2h h = e4m3_h2(sc);
-      v8h* dst = reinterpret_cast<v8h*>(lds + row * xf_row + c0 * 2);
+      v8h* dst = reinterpret_cast<v8h*>(lds + row * xf_row + c0 * 2 + 16 * (c0 / 64));
       dst[0] = dq8(c[0], h);
       dst[1] = dq8(c[1], h);
     } else {
@@ -591,69 +586,68 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     }
   };
   v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
-  int cr = 0, cpp = pbeg;
+  int cr = 0, ce = 0;                            // element being computed
   const int wsw = (r8 ^ c8) << 4;
-  // One element from ring slot i: stage its W codes (and at a round's first
-  // element its scale block) in LDS, refill the slot with the element kPairs
-  // ahead, then dequantize and accumulate.
-  auto elem = [&](u32x4& ra_i, u32x4& rb_i, uint32_t& rs_i) {
+  // One element from ring slot i: stage its W codes (and in slot 0 the scale
+  // group) in LDS, refill the slot with the element kPairs ahead, then
+  // dequantize and accumulate.
+  auto elem = [&](u32x4& ra_i, u32x4& rb_i, uint32_t& rs_i, int i) {
     uint32_t sw = rs_i;
-    if (SCM == kScaleBlock) {
-      if (cpp == pbeg) {
-#pragma unroll
-        for (int k = 0; k < kSB; ++k)
-          if (k < nsb) *reinterpret_cast<u32x4*>(sa + k * 1024 + lane * 16) = sbv[k];
-      }
-      sw = *reinterpret_cast<const uint32_t*>(sa + b * (16 * E) + 16 * (cpp - pbeg) + 4 * g);
-    }
+    if (SCM == kScaleGroup && i == 0)
+      *reinterpret_cast<u32x4*>(sa + lane * 16) = sg;   // [pair q][row b] x 16 bytes
     *reinterpret_cast<u32x4*>(tb + r8 * 128 + wsw) = ra_i;
     *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + (wsw ^ 64)) = rb_i;
-    load_elem(ra_i, rb_i, rs_i);
+    load_elem(ra_i, rb_i, rs_i, i == 0);
+    if (ce < E) {
+      if (SCM == kScaleGroup)
+        sw = *reinterpret_cast<const uint32_t*>(sa + (16 * i + b) * 16 + 4 * g);
+      const int cpp = pbeg + ce;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int c = 2 * g + st;
-      const u32x4 codes = *reinterpret_cast<const u32x4*>(
-          tb + b * 128 + ((c ^ (b & 7) ^ ((b >> 3) << 2)) << 4));
-      const int v0 = 256 * cpp + 64 * g + 32 * st;   // first of this lane's 32 values
-      v8h xq[4];
-      if (XF16) {
-        const v8h* src = reinterpret_cast<const v8h*>(lds + xrow * xf_row + v0 * 2);
+      for (int st = 0; st < 2; ++st) {
+        const int c = 2 * g + st;
+        const u32x4 codes = *reinterpret_cast<const u32x4*>(
+            tb + b * 128 + ((c ^ (b & 7) ^ ((b >> 3) << 2)) << 4));
+        const int v0 = 256 * cpp + 64 * g + 32 * st;   // first of this lane's 32 values
+        v8h xq[4];
+        if (XF16) {
+          const v8h* src = reinterpret_cast<const v8h*>(lds + xrow * xf_row + v0 * 2 + 16 * (v0 / 64));
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) xq[s4] = src[s4];
-      } else {
-        const u32x4 xc = *reinterpret_cast<const u32x4*>(lds + xrow * xc_row + v0 / 2);
-        const uint32_t xsb = *reinterpret_cast<const uint16_t*>(xs_base + xrow * bpr + v0 / 16);
-        const v2h h0 = e4m3_h2(xsb & 0xffu), h1 = e4m3_h2(xsb >> 8);
-        xq[0] = dq8(xc.x, h0);
-        xq[1] = dq8(xc.y, h0);
-        xq[2] = dq8(xc.z, h1);
-        xq[3] = dq8(xc.w, h1);
+          for (int s4 = 0; s4 < 4; ++s4) xq[s4] = src[s4];
+        } else {
+          const u32x4 xc = *reinterpret_cast<const u32x4*>(lds + xrow * xc_row + v0 / 2);
+          const uint32_t xsb = *reinterpret_cast<const uint16_t*>(xs_base + xrow * bpr + v0 / 16);
+          const v2h h0 = e4m3_h2(xsb & 0xffu), h1 = e4m3_h2(xsb >> 8);
+          xq[0] = dq8(xc.x, h0);
+          xq[1] = dq8(xc.y, h0);
+          xq[2] = dq8(xc.z, h1);
+          xq[3] = dq8(xc.w, h1);
+        }
+        const v2h w0 = e4m3_h2((sw >> (16 * st)) & 0xffu);
+        const v2h w1 = e4m3_h2((sw >> (16 * st + 8)) & 0xffu);
+        v4f& acc = st ? acc1 : acc0;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[0], dq8(codes.x, w0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[1], dq8(codes.y, w0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[2], dq8(codes.z, w1), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[3], dq8(codes.w, w1), acc, 0, 0, 0);
       }
-      const v2h w0 = e4m3_h2((sw >> (16 * st)) & 0xffu);
-      const v2h w1 = e4m3_h2((sw >> (16 * st + 8)) & 0xffu);
-      v4f& acc = st ? acc1 : acc0;
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[0], dq8(codes.x, w0), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[1], dq8(codes.y, w0), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[2], dq8(codes.z, w1), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[3], dq8(codes.w, w1), acc, 0, 0, 0);
     }
-    if (cpp == pend - 1) {
+    if (ce == Ep - 1) {
       finish(cr, acc0 + acc1, true);
       acc0 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       acc1 = acc0;
     }
-    if (++cpp == pend) { cpp = pbeg; ++cr; }
+    if (++ce == Ep) { ce = 0; ++cr; }
   };
-  // element j lives in slot j % kPairs and is refilled with element j + kPairs
+  // element j lives in slot j % kPairs and is refilled with element j + kPairs;
+  // J is a multiple of kPairs, so slot 0 always starts a group
   for (int j0 = 0; j0 < J; j0 += kPairs) {
 #pragma unroll
-    for (int i = 0; i < kPairs; ++i)
-      if (j0 + i < J) elem(ra[i], rb[i], rs[i]);
+    for (int i = 0; i < kPairs; ++i) elem(ra[i], rb[i], rs[i], i);
   }
   // Every wave takes part in all R rounds' exchanges: a wave whose part of K is
-  // empty (E == 0) contributes zeros for its valid rounds, and rounds without a
-  // strip for this slot exchange nothing that is stored.
-  for (int r = E > 0 ? nmine : 0; r < R; ++r) finish(r, acc0, r < nmine);
+  // empty (Ep == 0) contributes zeros for its valid rounds, and rounds without
+  // a strip for this slot exchange nothing that is stored.
+  for (int r = Ep > 0 ? nmine : 0; r < R; ++r) finish(r, acc0, r < nmine);
 }
 
 // K = 0: every output is an empty sum.
@@ -726,20 +720,12 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   const int nstrips = (int)((N + 15) / 16);
   // fused streaming kernel when the quantized x fits in LDS
   const int64_t Kq = (K + 255) / 256 * 256;
-  const int64_t lds_f16 = B * (Kq * 2 + 16);
+  const int64_t lds_f16 = B * xf16_row_bytes((int)Kq);
   const int64_t lds_fp4 = B * (Kq / 2 + 16) + B * (Kq / 16);
-  const int Pq = (int)(Kq / 256);
-  const int E = (Pq + kSplit - 1) / kSplit;
-  const int nsb = (16 * E + 63) / 64;
   int scm = kScaleHalf;
   if (K % 64 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 4 == 0) scm = kScaleDword;
-  // scale blocks: one register copy, so the next round's block (loaded kPairs
-  // elements ahead) must not arrive before this round's first compute: E >= kPairs
-  if (K % 256 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 16 == 0 && nsb <= kSB &&
-      E >= kPairs)
-    scm = kScaleBlock;
-  const int64_t lds_fixed =
-      kStreamWaves * 2048 + kRedBytes + (scm == kScaleBlock ? kStreamWaves * nsb * 1024 : 0);
+  if (K % 256 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 16 == 0) scm = kScaleGroup;
+  const int64_t lds_fixed = kStreamWaves * 2048 + kRedBytes + kStreamWaves * 1024;
   const int64_t lds_max = 160 * 1024 - 256;
   const bool xf16 = lds_f16 + lds_fixed <= lds_max;
   // (the strip-relative buffer offsets need 16 rows of W to span < 2^31 bytes;
@@ -753,16 +739,16 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
     switch (sel * 3 + scm) {
       case 0: return launch_stream<false, false, kScaleHalf>(sa, grid, lds, stream);
       case 1: return launch_stream<false, false, kScaleDword>(sa, grid, lds, stream);
-      case 2: return launch_stream<false, false, kScaleBlock>(sa, grid, lds, stream);
+      case 2: return launch_stream<false, false, kScaleGroup>(sa, grid, lds, stream);
       case 6: return launch_stream<false, true, kScaleHalf>(sa, grid, lds, stream);
       case 7: return launch_stream<false, true, kScaleDword>(sa, grid, lds, stream);
-      case 8: return launch_stream<false, true, kScaleBlock>(sa, grid, lds, stream);
+      case 8: return launch_stream<false, true, kScaleGroup>(sa, grid, lds, stream);
       case 12: return launch_stream<true, false, kScaleHalf>(sa, grid, lds, stream);
       case 13: return launch_stream<true, false, kScaleDword>(sa, grid, lds, stream);
-      case 14: return launch_stream<true, false, kScaleBlock>(sa, grid, lds, stream);
+      case 14: return launch_stream<true, false, kScaleGroup>(sa, grid, lds, stream);
       case 18: return launch_stream<true, true, kScaleHalf>(sa, grid, lds, stream);
       case 19: return launch_stream<true, true, kScaleDword>(sa, grid, lds, stream);
-      default: return launch_stream<true, true, kScaleBlock>(sa, grid, lds, stream);
+      default: return launch_stream<true, true, kScaleGroup>(sa, grid, lds, stream);
     }
   }
 
