@@ -183,9 +183,9 @@ def main():
            "k_nv_quant_fast", qsrc),
         Op("mxfp4_quantize", mx_q, nA, "GB/s", b_mx, HBM_PEAK_GBS, "hbm", "k_mx_quant_fast", qsrc),
         Op("nvfp4_dequantize_bf16", nv_deq, nA, "GB/s", b_nv - 4, HBM_PEAK_GBS, "hbm",
-           "k_nv_dequant_fast", qsrc),
+           "k_dequant_fast<NV>", qsrc),
         Op("mxfp4_dequantize_bf16", mx_deq, nA, "GB/s", b_mx, HBM_PEAK_GBS, "hbm",
-           "k_mx_dequant_fast", qsrc),
+           "k_dequant_fast<MX>", qsrc),
     ]
 
     # --------------------------------------------------------- decode GEMV --
@@ -210,7 +210,7 @@ def main():
             assert st == 0, st
 
         ops.append(Op(f"gemv_b{B}", gemv, nG, "GB/s", w_bytes + B * Kv * 2 + B * Nv * 2,
-                      HBM_PEAK_GBS, "hbm", "k_gemv_xquant + k_gemv", gsrc))
+                      HBM_PEAK_GBS, "hbm", "k_gemv_stream (x quantized in-kernel, W streamed)", gsrc))
 
     # -------------------------------------------------------- prefill GEMM --
     Mg, Ng, Kg = 8192, 28672, 8192

@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(kThreads)
     k_nv_quant_fast(const void* __restrict__ x, int64_t nblk, uint8_t* __restrict__ q,
                     uint8_t* __restrict__ scales, const float* __restrict__ amax_in,
                     const uint32_t* __restrict__ partials, int npart, float* __restrict__ amax_out,
-                    float* __restrict__ scale_out) {
+                    float* __restrict__ scale_out, bool reverse) {
   constexpr int VPB = BF16 ? 2 : 4;
   __shared__ u32x4 lds[VPB * (kThreads + 1)];
   const float G = resolve_amax(amax_in, partials, npart);
@@ -176,8 +176,9 @@ __global__ void __launch_bounds__(kThreads)
     *scale_out = s_global;
   }
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblk;
-       base += (int64_t)gridDim.x * kThreads) {
+  const int64_t nchunk = (nblk + kThreads - 1) / kThreads;
+  for (int64_t c = blockIdx.x; c < nchunk; c += gridDim.x) {
+    const int64_t base = (reverse ? nchunk - 1 - c : c) * kThreads;
     const int nb = (int)(nblk - base < kThreads ? nblk - base : kThreads);
     u32x4 w[VPB];
     stage_blocks<VPB, kThreads>(xv, base, nb, lds, w);
@@ -425,6 +426,10 @@ __global__ void k_empty_scales(float* amax_out, float* scale_out) {
   }
 }
 
+// After an amax pass the encode pass walks the tensor backwards, starting on the data
+// the amax pass read last (the likeliest to still be cached).
+constexpr bool kReverseAfterAmax = true;
+
 inline int grid_for(int64_t work_items) {
   int64_t g = (work_items + kThreads - 1) / kThreads;
   if (g < 1) g = 1;
@@ -468,13 +473,14 @@ hipError_t launch_nv_quant(const void* x, bool bf16, int64_t rows, int64_t cols,
   const bool fast = (cols % 16 == 0) && aligned16(x) && aligned16(q);
   if (fast) {
     const int64_t nblk = rows * (cols / 16);
+    const bool reverse = kReverseAfterAmax && amax_in == nullptr;
     const int g = grid_for(nblk);
     if (bf16)
       hipLaunchKernelGGL(k_nv_quant_fast<true>, dim3(g), dim3(kThreads), 0, stream, x, nblk, q,
-                         scales, amax_in, partials, npart, amax_out, scale_out);
+                         scales, amax_in, partials, npart, amax_out, scale_out, reverse);
     else
       hipLaunchKernelGGL(k_nv_quant_fast<false>, dim3(g), dim3(kThreads), 0, stream, x, nblk, q,
-                         scales, amax_in, partials, npart, amax_out, scale_out);
+                         scales, amax_in, partials, npart, amax_out, scale_out, reverse);
   } else {
     const int g = grid_for(rows * ((cols + 15) / 16));
     if (bf16)
