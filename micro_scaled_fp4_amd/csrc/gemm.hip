@@ -6,31 +6,37 @@
 // are accumulated in float32, and g_d scales the output.
 //
 // MXFP4 (E8M0 per 32): the gfx950 block-scaled MFMA consumes exactly this
-// format -- v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands and one E8M0
-// scale per lane, covering (row, 32-value block).  Each MFMA result is exact
-// (FP4 x FP4 x 2^k products are exact and the 64-term sums fit the float32
+// format -- v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 operands and one E8M0
+// scale byte per lane, covering (row, 32-value block), chosen from a scale
+// dword by the instruction's byte select.  Each MFMA result is exact (FP4 x
+// FP4 x 2^k products are exact and the 128-term sums fit the float32
 // accumulator at these exponents); only the float32 accumulation rounds.
 //
 // NVFP4 (E4M3 per 16): no gfx950 MFMA takes E4M3 block scales, and FP8 cannot
 // hold E2M1 x E4M3 products exactly (up to 6 significant bits), so each lane
-// dequantizes its operand fragment to fp16 in registers: v_cvt_scalef32_pk_f16_fp4
-// applies the scale's power of two (exact), one v_pk_mul_f16 applies its 3-bit
-// mantissa (exact: <= 6 significant bits), then v_mfma_f32_32x32x16_f16
-// accumulates in float32.  Ceiling: the dense fp16 MFMA rate.
+// dequantizes its operand fragment to fp16 in registers:
+// v_cvt_scalef32_pk_f16_fp4 with the constant scale 2^8, times the E4M3 scale
+// byte moved into fp16 fields (= E4M3 * 2^-8), both exact; then
+// v_mfma_f32_16x16x32_f16 accumulates in float32.  Ceiling: the fp16 MFMA rate.
 //
 // Tiling: 256x256 output tile per workgroup, 4 waves in a 2x2 grid, 128x128 per
-// wave (4x4 MFMA tiles of 32x32).  K advances 128 values (64 bytes per row)
-// per stage; operand stages are double-buffered in LDS with a 16-byte row pad
-// (80-byte row stride keeps the 16-byte fragment reads of 8 consecutive rows on
-// distinct banks).  Global loads for stage k+1 are in flight while stage k
-// computes.  Inside a 64-value half stage, lane group g = lane/32 owns values
-// [32g, 32g+32) of its row, so one 16-byte LDS read feeds the whole half
-// (MXFP4: one MFMA; NVFP4: four MFMAs whose K order is permuted identically for
-// both operands, which leaves the sum unchanged).
+// wave (8x8 MFMA tiles of 16x16, accumulators in AGPRs).  K advances 256 values
+// (128 bytes per row) per stage; stages are double-buffered in LDS through
+// registers (the next stage's global loads are in flight while this stage
+// computes; one barrier per stage).  A 16-byte chunk c of tile row r is stored
+// at chunk position c ^ ((r >> 1) & 7): the 16 rows of a fragment read then
+// cover all 64 banks.  Inside a stage, lane group g (lane / 16) takes values
+// [64g + 32ks, +32) in k-step ks, identically for both operands (the MFMA sum
+// does not depend on the K order), so a lane's scale bytes for the stage are
+// contiguous: 2 bytes (MXFP4, byte ks selected by the MFMA) or 4 (NVFP4).
+// The MFMA's first operand is the W fragment, so each lane ends with 4
+// consecutive columns of one output row (one 8- or 16-byte store).
 // Workgroup -> tile map: workgroups are dealt round-robin to the 8 XCDs, so
 // each XCD is given a contiguous range of tiles; tiles are visited in groups
 // of 8 row-tiles so concurrently running workgroups of an XCD share operand
 // rows in its L2.
+#include <type_traits>
+
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
@@ -39,24 +45,25 @@ using namespace fp4dev;
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 256, BK = 128;   // BK in FP4 values
-constexpr int kRowBytes = BK / 2;             // 64
-constexpr int kRowStride = kRowBytes + 16;    // 80 (padded)
-constexpr int kTileBytes = BM * kRowStride;   // 20480
+constexpr int BM = 256, BN = 256, BK = 256;   // BK in FP4 values
+constexpr int kRowBytes = BK / 2;             // 128
+constexpr int kTileBytes = BM * kRowBytes;    // 32 KB
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
+constexpr int kBufferWord3 = 0x00020000;      // raw buffer descriptor word 3 (gfx9 family)
+constexpr int kOutOfRange = 0x7ffffff0;       // a buffer offset past every range: reads 0
 
 template <bool MX>
 struct Cfg {
-  static constexpr int kScalesPerRow = MX ? BK / 32 : BK / 16;    // per stage: 4 or 8
-  static constexpr int kScaleBytes = BM * kScalesPerRow;
+  static constexpr int kScaleRow = MX ? BK / 32 : BK / 16;          // scale bytes per row per stage
+  static constexpr int kScaleBytes = BM * kScaleRow;
   static constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
+  static constexpr int kLdsBytes = 2 * kStageBytes;                 // 136 KB (MX) / 144 KB (NV)
 };
 
 // ----------------------------------------------------------- tile mapping --
@@ -73,219 +80,266 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = r / gsize;
 }
 
+__device__ __forceinline__ int swz(int row, int chunk) {   // byte offset in a tile
+  return row * kRowBytes + 16 * (chunk ^ ((row >> 1) & 7));
+}
+
 // ------------------------------------------------------------- stage loads --
+// Thread t loads 16-byte chunks t + 256 j (j < 8) of each 256-row x 128-byte
+// tile (row = chunk / 8) and the stage's scale bytes of row t.  Reads go
+// through per-tile buffer descriptors whose range is the tile's rows that
+// exist; chunks past K and rows past the matrix read zeros (value 0, and the
+// scale bytes of such rows are never stored to an output).
+// One operand's part of a stage: its 8 chunks per thread and its scale bytes.
 template <bool MX>
 struct StageRegs {
-  u32x4 a[4], w[4];
-  uint32_t as[MX ? 1 : 2], ws[MX ? 1 : 2];
+  u32x4 d[8];
+  uint32_t s[MX ? 2 : 4];
 };
 
-// Thread t loads 16-byte chunks t + 256 j (j < 4) of each 256x64-byte tile and
-// the scale bytes of row t.  Rows past the matrix edge are clamped (their
-// results are never stored); chunks past K are zero (value 0).
-template <bool MX>
-__device__ __forceinline__ void load_stage(StageRegs<MX>& r, const uint8_t* __restrict__ A,
-                                           const uint8_t* __restrict__ as,
-                                           const uint8_t* __restrict__ W,
-                                           const uint8_t* __restrict__ ws, int m0, int n0, int M,
-                                           int N, int K, int k0) {
+template <bool MX, bool SCALE_VEC>
+__device__ __forceinline__ void load_part(StageRegs<MX>& r, __amdgpu_buffer_rsrc_t data,
+                                          __amdgpu_buffer_rsrc_t scales, int rowb, int nsc, int K,
+                                          int k0) {
   const int t = threadIdx.x;
-  const int64_t rowb = K / 2;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 8; ++j) {
     const int c = t + kThreads * j;
-    const int row = c >> 2, ch = c & 3;
-    const int kc = k0 + 32 * ch;                 // first value of the chunk
-    const int ra = min(m0 + row, M - 1), rw = min(n0 + row, N - 1);
-    if (kc < K) {
-      r.a[j] = *reinterpret_cast<const u32x4*>(A + (int64_t)ra * rowb + kc / 2);
-      r.w[j] = *reinterpret_cast<const u32x4*>(W + (int64_t)rw * rowb + kc / 2);
-    } else {
-      r.a[j] = u32x4{0, 0, 0, 0};
-      r.w[j] = u32x4{0, 0, 0, 0};
-    }
+    const int row = c >> 3, ch = c & 7;
+    const int kc = k0 + 32 * ch;
+    r.d[j] = __builtin_amdgcn_raw_buffer_load_b128(data, kc < K ? row * rowb + kc / 2 : kOutOfRange,
+                                                   0, 0);
   }
   constexpr int bs = MX ? 32 : 16;
-  const int nsc = K / bs;
+  constexpr int spr = Cfg<MX>::kScaleRow;
   const int kb = k0 / bs;
-  const int ra = min(m0 + t, M - 1), rw = min(n0 + t, N - 1);
-  const uint8_t* pa = as + (int64_t)ra * nsc;
-  const uint8_t* pw = ws + (int64_t)rw * nsc;
-#pragma unroll
-  for (int q = 0; q < (MX ? 1 : 2); ++q) {
-    uint32_t va = 0, vw = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = kb + 4 * q + i;
-      if (b < nsc) {
-        va |= (uint32_t)pa[b] << (8 * i);
-        vw |= (uint32_t)pw[b] << (8 * i);
-      }
+  if (SCALE_VEC) {   // K % 256 == 0 and 16-byte aligned scale rows
+    if (MX) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(scales, t * nsc + kb, 0, 0);
+      r.s[0] = v.x;
+      r.s[1] = v.y;
+    } else {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(scales, t * nsc + kb, 0, 0);
+      r.s[0] = v.x;
+      r.s[1] = v.y;
+      r.s[2] = v.z;
+      r.s[3] = v.w;
     }
-    r.as[q] = va;
-    r.ws[q] = vw;
+  } else {
+#pragma unroll
+    for (int q = 0; q < spr / 4; ++q) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = kb + 4 * q + i;
+        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(scales, b < nsc ? t * nsc + b : kOutOfRange,
+                                                             0, 0) << (8 * i);
+      }
+      r.s[q] = v;
+    }
   }
 }
 
+// tile: the operand's 32 KB tile in the stage buffer; sc: its scale rows
 template <bool MX>
-__device__ __forceinline__ void store_stage(const StageRegs<MX>& r, uint8_t* __restrict__ lds) {
+__device__ __forceinline__ void store_part(const StageRegs<MX>& r, uint8_t* __restrict__ tile,
+                                           uint8_t* __restrict__ sc) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 8; ++j) {
     const int c = t + kThreads * j;
-    const int row = c >> 2, ch = c & 3;
-    *reinterpret_cast<u32x4*>(lds + row * kRowStride + 16 * ch) = r.a[j];
-    *reinterpret_cast<u32x4*>(lds + kTileBytes + row * kRowStride + 16 * ch) = r.w[j];
+    *reinterpret_cast<u32x4*>(tile + swz(c >> 3, c & 7)) = r.d[j];
   }
-  constexpr int spr = Cfg<MX>::kScalesPerRow;
-  uint32_t* sa = reinterpret_cast<uint32_t*>(lds + 2 * kTileBytes);
-  uint32_t* sw = reinterpret_cast<uint32_t*>(lds + 2 * kTileBytes + Cfg<MX>::kScaleBytes);
-#pragma unroll
-  for (int q = 0; q < (MX ? 1 : 2); ++q) {
-    sa[t * (spr / 4) + q] = r.as[q];
-    sw[t * (spr / 4) + q] = r.ws[q];
-  }
+  uint8_t* sp = sc + t * Cfg<MX>::kScaleRow;
+  if (MX)
+    *reinterpret_cast<u32x2*>(sp) = u32x2{r.s[0], r.s[1]};
+  else
+    *reinterpret_cast<u32x4*>(sp) = u32x4{r.s[0], r.s[1], r.s[2], r.s[3]};
 }
 
 // --------------------------------------------------------- NV fragment dequant --
-// E4M3 byte -> (power of two as f32 for the cvt scale operand, 3-bit mantissa
-// factor as an f16 pair).  Normal: 2^(E-7) * (1 + m/8); subnormal: 2^-9 * m.
-__device__ __forceinline__ void e4m3_split(uint32_t b, float& pow2, v2h& mant) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  pow2 = __uint_as_float(e ? ((e + 120u) << 23) : (118u << 23));
-  const float mf = e ? 1.0f + (float)m * 0.125f : (float)m;
-  const _Float16 mh = (_Float16)mf;   // exact
-  mant = v2h{mh, mh};
+// f16 pair (h, h), h = E4M3 value * 2^-8 exactly: the byte's exponent and
+// mantissa fields drop into the f16 fields (bias 7 against 15 gives the 2^-8;
+// E4M3 subnormals land on f16 subnormals), its sign on the sign.  Bytes
+// 0x7f / 0xff (NaN) read as +-480; quantizers never emit them.
+__device__ __forceinline__ v2h e4m3_h2(uint32_t byte) {
+  const uint32_t h = ((byte & 0x80u) << 8) | ((byte & 0x7fu) << 7);
+  return __builtin_bit_cast(v2h, h | (h << 16));
 }
 
-// 8 FP4 codes (one dword) -> 8 fp16 values v * scale.
-__device__ __forceinline__ v8h dequant8(uint32_t codes, float pow2, v2h mant) {
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, pow2, 0) * mant;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, pow2, 1) * mant;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, pow2, 2) * mant;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, pow2, 3) * mant;
+// The 8 values E2M1(code) * E4M3 of one dword of codes: the conversion scales by
+// 2^8 (exact) and the f16 product with E4M3 * 2^-8 is exact (at most 6
+// significant bits, magnitude in [2^-10, 2688]).
+__device__ __forceinline__ v8h dq8(uint32_t codes, v2h s) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s;
   return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // ------------------------------------------------------------------ kernel --
-template <bool MX, bool OUT_BF16>
+template <bool MX, bool OUT_BF16, bool SCALE_VEC>
 __global__ void __launch_bounds__(kThreads, 1)
     k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ as,
            const uint8_t* __restrict__ W, const uint8_t* __restrict__ ws,
            const float* __restrict__ g_a, const float* __restrict__ g_b, float g_d, int M, int N,
-           int K, void* __restrict__ D, int tiles_m, int tiles_n) {
+           int K, void* __restrict__ D, int tiles_m, int tiles_n, bool vec_out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, g = lane >> 5;
+  const int r16 = lane & 15, g = lane >> 4;
+  constexpr int spr = Cfg<MX>::kScaleRow;
+  constexpr int bs = MX ? 32 : 16;
+  const int rowb = K / 2, nsc = K / bs;
 
-  v16f acc[4][4];
+  __amdgpu_buffer_rsrc_t src_a, src_w, src_as, src_ws;
+  {
+    const int rows_a = min(BM, M - m0), rows_w = min(BN, N - n0);
+    src_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A) + (int64_t)m0 * rowb, 0,
+                                              rows_a * rowb, kBufferWord3);
+    src_w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W) + (int64_t)n0 * rowb, 0,
+                                              rows_w * rowb, kBufferWord3);
+    src_as = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(as) + (int64_t)m0 * nsc, 0,
+                                               rows_a * nsc, kBufferWord3);
+    src_ws = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ws) + (int64_t)n0 * nsc, 0,
+                                               rows_w * nsc, kBufferWord3);
+  }
+
+  v4f acc[8][8];   // [W tile nt][A tile mt]: rows n, columns m of the MFMA
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nk = (K + BK - 1) / BK;
+  constexpr int kStage = Cfg<MX>::kStageBytes;
+  // stage buffer layout: A tile | W tile | A scale rows | W scale rows
+  auto tile_a = [&](int b) { return smem + b * kStage; };
+  auto tile_w = [&](int b) { return smem + b * kStage + kTileBytes; };
+  auto sc_a = [&](int b) { return smem + b * kStage + 2 * kTileBytes; };
+  auto sc_w = [&](int b) { return smem + b * kStage + 2 * kTileBytes + Cfg<MX>::kScaleBytes; };
   StageRegs<MX> st;
-  load_stage<MX>(st, A, as, W, ws, m0, n0, M, N, K, 0);
-  store_stage<MX>(st, smem);
+  load_part<MX, SCALE_VEC>(st, src_a, src_as, rowb, nsc, K, 0);
+  store_part<MX>(st, tile_a(0), sc_a(0));
+  load_part<MX, SCALE_VEC>(st, src_w, src_ws, rowb, nsc, K, 0);
+  store_part<MX>(st, tile_w(0), sc_w(0));
   __syncthreads();
 
-  constexpr int kStage = Cfg<MX>::kStageBytes;
-  constexpr int spr = Cfg<MX>::kScalesPerRow;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_stage<MX>(st, A, as, W, ws, m0, n0, M, N, K, (kt + 1) * BK);
-    const uint8_t* buf = smem + (kt & 1) * kStage;
-    const uint8_t* la = buf + (wm * 128 + l32) * kRowStride + 16 * g;
-    const uint8_t* lw = buf + kTileBytes + (wn * 128 + l32) * kRowStride + 16 * g;
-    const uint8_t* lsa = buf + 2 * kTileBytes + (wm * 128 + l32) * spr;
-    const uint8_t* lsw = buf + 2 * kTileBytes + Cfg<MX>::kScaleBytes + (wn * 128 + l32) * spr;
+    const bool more = kt + 1 < nk;
+    const int nb = (kt + 1) & 1;
+    // the next stage passes through registers one operand at a time: A during
+    // k-step 0, W during k-step 1
+    if (more) load_part<MX, SCALE_VEC>(st, src_a, src_as, rowb, nsc, K, (kt + 1) * BK);
+    const uint8_t* la = tile_a(kt & 1);
+    const uint8_t* lw = tile_w(kt & 1);
+    const uint8_t* lsa = sc_a(kt & 1);
+    const uint8_t* lsw = sc_w(kt & 1);
+    const int ra0 = wm * 128 + r16, rw0 = wn * 128 + r16;
+    // this lane's scale bytes for the stage, one dword per tile
+    uint32_t sa[8], sw[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 fa[4], fw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = *reinterpret_cast<const u32x4*>(la + i * 32 * kRowStride + 32 * h);
-        fw[i] = *reinterpret_cast<const u32x4*>(lw + i * 32 * kRowStride + 32 * h);
+    for (int i = 0; i < 8; ++i) {
+      if (MX) {
+        sa[i] = *reinterpret_cast<const uint16_t*>(lsa + (ra0 + 16 * i) * spr + 2 * g);
+        sw[i] = *reinterpret_cast<const uint16_t*>(lsw + (rw0 + 16 * i) * spr + 2 * g);
+      } else {
+        sa[i] = *reinterpret_cast<const uint32_t*>(lsa + (ra0 + 16 * i) * spr + 4 * g);
+        sw[i] = *reinterpret_cast<const uint32_t*>(lsw + (rw0 + 16 * i) * spr + 4 * g);
       }
+    }
+    // k-step ks of the stage (the MFMA's scale byte select must be a constant)
+    auto kstep = [&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
       if constexpr (MX) {
-        uint32_t sa[4], sw[4];
+        u32x4 fa[8], fw[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sa[i] = lsa[i * 32 * spr + 2 * h + g];
-          sw[i] = lsw[i * 32 * spr + 2 * h + g];
+        for (int i = 0; i < 8; ++i) {
+          fa[i] = *reinterpret_cast<const u32x4*>(la + swz(ra0 + 16 * i, 2 * g + ks));
+          fw[i] = *reinterpret_cast<const u32x4*>(lw + swz(rw0 + 16 * i, 2 * g + ks));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v8i av = {(int)fa[i].x, (int)fa[i].y, (int)fa[i].z, (int)fa[i].w, 0, 0, 0, 0};
+        for (int i = 0; i < 8; ++i) {
+          const v8i wv = {(int)fw[i].x, (int)fw[i].y, (int)fw[i].z, (int)fw[i].w, 0, 0, 0, 0};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v8i bv = {(int)fw[j].x, (int)fw[j].y, (int)fw[j].z, (int)fw[j].w, 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av, bv, acc[i][j], 4, 4, 0, (int)sa[i], 0, (int)sw[j]);
+          for (int j = 0; j < 8; ++j) {
+            const v8i av = {(int)fa[j].x, (int)fa[j].y, (int)fa[j].z, (int)fa[j].w, 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                wv, av, acc[i][j], 4, 4, ks, (int)sw[i], ks, (int)sa[j]);
           }
         }
       } else {
-        // lane group g holds values [32g, 32g+32) of this 64-value half: NV
-        // blocks 4h+2g (dwords 0,1) and 4h+2g+1 (dwords 2,3)
-        float pa[4][2], pw[4][2];
-        v2h ma[4][2], mw[4][2];
+        // (a loop, not unrolled: keeps the accumulators in place in the AGPRs)
+#pragma unroll 1
+        for (int s4 = 0; s4 < 4; ++s4) {
+          // dword s4 of the fragment: 8 values of NV block 4g + 2ks + s4 / 2
+          const int sh = 8 * (2 * ks + (s4 >> 1));
+          v8h da[8], dw[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            e4m3_split(lsa[i * 32 * spr + 4 * h + 2 * g + b], pa[i][b], ma[i][b]);
-            e4m3_split(lsw[i * 32 * spr + 4 * h + 2 * g + b], pw[i][b], mw[i][b]);
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t ca = *reinterpret_cast<const uint32_t*>(la + swz(ra0 + 16 * i, 2 * g + ks) + 4 * s4);
+            const uint32_t cw = *reinterpret_cast<const uint32_t*>(lw + swz(rw0 + 16 * i, 2 * g + ks) + 4 * s4);
+            da[i] = dq8(ca, e4m3_h2((sa[i] >> sh) & 0xffu));
+            dw[i] = dq8(cw, e4m3_h2((sw[i] >> sh) & 0xffu));
           }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          v8h da[4], dw[4];
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            da[i] = dequant8(fa[i][s], pa[i][s >> 1], ma[i][s >> 1]);
-            dw[i] = dequant8(fw[i][s], pw[i][s >> 1], mw[i][s >> 1]);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[i], dw[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 8; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[i], da[j], acc[i][j], 0, 0, 0);
         }
       }
+    };
+    kstep(std::integral_constant<int, 0>{});
+    if (more) {
+      store_part<MX>(st, tile_a(nb), sc_a(nb));
+      load_part<MX, SCALE_VEC>(st, src_w, src_ws, rowb, nsc, K, (kt + 1) * BK);
     }
-    if (kt + 1 < nk) store_stage<MX>(st, smem + ((kt + 1) & 1) * kStage);
+    kstep(std::integral_constant<int, 1>{});
+    if (more) store_part<MX>(st, tile_w(nb), sc_w(nb));
     __syncthreads();
   }
 
-  // epilogue: D = acc * ((g_a * g_b) * g_d)
+  // epilogue: lane holds D[m][n .. n+3] for each tile pair; D = acc * ((g_a * g_b) * g_d)
   float alpha = g_d;
   if (!MX) alpha = ((*g_a) * (*g_b)) * g_d;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 8; ++j) {
+    const int m = m0 + wm * 128 + 16 * j + r16;
+    if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + l32;
-      if (col >= N) continue;
+    for (int i = 0; i < 8; ++i) {
+      const int n = n0 + wn * 128 + 16 * i + 4 * g;
+      const v4f v = acc[i][j] * alpha;
+      if (OUT_BF16) {
+        uint16_t* row = reinterpret_cast<uint16_t*>(D) + (int64_t)m * N;
+        if (vec_out && n + 3 < N) {
+          *reinterpret_cast<u32x2*>(row + n) =
+              u32x2{f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16)};
+        } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (row < M) {
-          const float v = acc[i][j][r] * alpha;
-          if (OUT_BF16)
-            reinterpret_cast<uint16_t*>(D)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16(v);
-          else
-            reinterpret_cast<float*>(D)[(int64_t)row * N + col] = v;
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) row[n + q] = (uint16_t)f32_to_bf16(v[q]);
+        }
+      } else {
+        float* row = reinterpret_cast<float*>(D) + (int64_t)m * N;
+        if (vec_out && n + 3 < N) {
+          *reinterpret_cast<v4f*>(row + n) = v;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) row[n + q] = v[q];
         }
       }
     }
+  }
 }
 
-template <bool MX, bool OUT_BF16>
+template <bool MX, bool OUT_BF16, bool SCALE_VEC>
 hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
                     const float* g_a, const float* g_b, float g_d, int M, int N, int K, void* D,
                     hipStream_t stream) {
@@ -293,14 +347,26 @@ hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const
   constexpr int lds = Cfg<MX>::kLdsBytes;
   static bool attr_set = false;   // per process; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MX, OUT_BF16>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MX, OUT_BF16, SCALE_VEC>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm<MX, OUT_BF16>), dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream,
-                     A, as, W, ws, g_a, g_b, g_d, M, N, K, D, tiles_m, tiles_n);
+  // 4 outputs per store when every row start is aligned to 4 outputs
+  const bool vec_out = N % 4 == 0 && reinterpret_cast<uintptr_t>(D) % (OUT_BF16 ? 8 : 16) == 0;
+  hipLaunchKernelGGL((k_gemm<MX, OUT_BF16, SCALE_VEC>), dim3(tiles_m * tiles_n), dim3(kThreads), lds,
+                     stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, D, tiles_m, tiles_n, vec_out);
   return hipGetLastError();
+}
+
+template <bool MX, bool OUT_BF16>
+hipError_t launch_s(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
+                    const float* g_a, const float* g_b, float g_d, int M, int N, int K, void* D,
+                    hipStream_t stream) {
+  const bool vec = K % BK == 0 && (reinterpret_cast<uintptr_t>(as) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
+  return vec ? launch_t<MX, OUT_BF16, true>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream)
+             : launch_t<MX, OUT_BF16, false>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
 }
 
 }  // namespace
@@ -310,16 +376,17 @@ namespace fp4impl {
 hipError_t launch_gemm(bool mx, const uint8_t* A, const uint8_t* a_scales, const float* g_a,
                        const uint8_t* W, const uint8_t* w_scales, const float* g_b, float g_d,
                        int64_t M, int64_t N, int64_t K, void* D, bool d_bf16, hipStream_t stream) {
-  if (M > (1 << 30) || N > (1 << 30) || K > (1 << 30)) return hipErrorInvalidValue;
+  // buffer ranges cover one 256-row tile of an operand: 256 * K / 2 < 2^31
+  if (M > (1 << 30) || N > (1 << 30) || K >= (1 << 23)) return hipErrorInvalidValue;
   if (mx) {
-    return d_bf16 ? launch_t<true, true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
+    return d_bf16 ? launch_s<true, true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
                                          (int)K, D, stream)
-                  : launch_t<true, false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
+                  : launch_s<true, false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
                                           (int)K, D, stream);
   }
-  return d_bf16 ? launch_t<false, true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
+  return d_bf16 ? launch_s<false, true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
                                         (int)K, D, stream)
-                : launch_t<false, false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
+                : launch_s<false, false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
                                          (int)K, D, stream);
 }
 
