@@ -19,8 +19,8 @@
 // byte moved into fp16 fields (= E4M3 * 2^-8), both exact; then
 // v_mfma_f32_16x16x32_f16 accumulates in float32.  Ceiling: the fp16 MFMA rate.
 //
-// Tiling: 256x256 output tile per workgroup, 4 waves in a 2x2 grid, 128x128 per
-// wave (8x8 MFMA tiles of 16x16, accumulators in AGPRs).  K advances 256 values
+// Tiling: 256x256 output tile per workgroup, kWavesM x kWavesN waves, each with
+// its own block of 16x16 MFMA tiles (accumulators in AGPRs).  K advances 256 values
 // (128 bytes per row) per stage; stages are double-buffered in LDS through
 // registers (the next stage's global loads are in flight while this stage
 // computes; one barrier per stage).  A 16-byte chunk c of tile row r is stored
@@ -49,10 +49,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+constexpr int kWavesM = 2, kWavesN = 2;       // wave grid of the workgroup
+constexpr int kThreads = 64 * kWavesM * kWavesN;
+constexpr int kTM = 256 / 16 / kWavesM;       // 16-row A tiles per wave
+constexpr int kTN = 256 / 16 / kWavesN;       // 16-row W tiles per wave
 constexpr int BM = 256, BN = 256, BK = 256;   // BK in FP4 values
 constexpr int kRowBytes = BK / 2;             // 128
 constexpr int kTileBytes = BM * kRowBytes;    // 32 KB
+constexpr int kChunks = kTileBytes / 16 / kThreads;   // 16-byte chunks per thread per tile
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;      // raw buffer descriptor word 3 (gfx9 family)
@@ -85,7 +89,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {   // byte offset in a t
 }
 
 // ------------------------------------------------------------- stage loads --
-// Thread t loads 16-byte chunks t + 256 j (j < 8) of each 256-row x 128-byte
+// Thread t loads 16-byte chunks t + kThreads j (j < kChunks) of each 256-row x 128-byte
 // tile (row = chunk / 8) and the stage's scale bytes of row t.  Reads go
 // through per-tile buffer descriptors whose range is the tile's rows that
 // exist; chunks past K and rows past the matrix read zeros (value 0, and the
@@ -93,7 +97,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {   // byte offset in a t
 // One operand's part of a stage: its 8 chunks per thread and its scale bytes.
 template <bool MX>
 struct StageRegs {
-  u32x4 d[8];
+  u32x4 d[kChunks];
   uint32_t s[MX ? 2 : 4];
 };
 
@@ -103,23 +107,25 @@ __device__ __forceinline__ void load_part(StageRegs<MX>& r, __amdgpu_buffer_rsrc
                                           int k0) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < kChunks; ++j) {
     const int c = t + kThreads * j;
     const int row = c >> 3, ch = c & 7;
     const int kc = k0 + 32 * ch;
-    r.d[j] = __builtin_amdgcn_raw_buffer_load_b128(data, kc < K ? row * rowb + kc / 2 : kOutOfRange,
-                                                   0, 0);
+    // (SCALE_VEC implies K % 256 == 0: no chunk of a stage is past K)
+    r.d[j] = __builtin_amdgcn_raw_buffer_load_b128(
+        data, (SCALE_VEC || kc < K) ? row * rowb + kc / 2 : kOutOfRange, 0, 0);
   }
   constexpr int bs = MX ? 32 : 16;
   constexpr int spr = Cfg<MX>::kScaleRow;
   const int kb = k0 / bs;
+  const int sr = t % BM;   // scale row (threads past 256 repeat rows: same bytes, same place)
   if (SCALE_VEC) {   // K % 256 == 0 and 16-byte aligned scale rows
     if (MX) {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(scales, t * nsc + kb, 0, 0);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(scales, sr * nsc + kb, 0, 0);
       r.s[0] = v.x;
       r.s[1] = v.y;
     } else {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(scales, t * nsc + kb, 0, 0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(scales, sr * nsc + kb, 0, 0);
       r.s[0] = v.x;
       r.s[1] = v.y;
       r.s[2] = v.z;
@@ -132,7 +138,7 @@ __device__ __forceinline__ void load_part(StageRegs<MX>& r, __amdgpu_buffer_rsrc
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int b = kb + 4 * q + i;
-        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(scales, b < nsc ? t * nsc + b : kOutOfRange,
+        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(scales, b < nsc ? sr * nsc + b : kOutOfRange,
                                                              0, 0) << (8 * i);
       }
       r.s[q] = v;
@@ -146,11 +152,11 @@ __device__ __forceinline__ void store_part(const StageRegs<MX>& r, uint8_t* __re
                                            uint8_t* __restrict__ sc) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < kChunks; ++j) {
     const int c = t + kThreads * j;
     *reinterpret_cast<u32x4*>(tile + swz(c >> 3, c & 7)) = r.d[j];
   }
-  uint8_t* sp = sc + t * Cfg<MX>::kScaleRow;
+  uint8_t* sp = sc + (t % BM) * Cfg<MX>::kScaleRow;
   if (MX)
     *reinterpret_cast<u32x2*>(sp) = u32x2{r.s[0], r.s[1]};
   else
@@ -190,7 +196,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int r16 = lane & 15, g = lane >> 4;
   constexpr int spr = Cfg<MX>::kScaleRow;
   constexpr int bs = MX ? 32 : 16;
@@ -209,11 +215,11 @@ __global__ void __launch_bounds__(kThreads, 1)
                                                rows_w * nsc, kBufferWord3);
   }
 
-  v4f acc[8][8];   // [W tile nt][A tile mt]: rows n, columns m of the MFMA
+  v4f acc[kTN][kTM];   // [W tile][A tile]: rows n, columns m of the MFMA
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kTN; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < kTM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nk = (K + BK - 1) / BK;
   constexpr int kStage = Cfg<MX>::kStageBytes;
@@ -229,78 +235,112 @@ __global__ void __launch_bounds__(kThreads, 1)
   store_part<MX>(st, tile_w(0), sc_w(0));
   __syncthreads();
 
+  // The loop body has no branch (a branch lets the compiler sink the MFMAs past
+  // the stores and the barrier): after the last stage the next-stage loads read
+  // through empty descriptors (zeros, no memory traffic) into the buffer nobody
+  // reads again.
+  const __amdgpu_buffer_rsrc_t none =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A), 0, 0, kBufferWord3);
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
     const int nb = (kt + 1) & 1;
     // the next stage passes through registers one operand at a time: A during
     // k-step 0, W during k-step 1
-    if (more) load_part<MX, SCALE_VEC>(st, src_a, src_as, rowb, nsc, K, (kt + 1) * BK);
+    load_part<MX, SCALE_VEC>(st, more ? src_a : none, more ? src_as : none, rowb, nsc, K,
+                             (kt + 1) * BK);
     const uint8_t* la = tile_a(kt & 1);
     const uint8_t* lw = tile_w(kt & 1);
     const uint8_t* lsa = sc_a(kt & 1);
     const uint8_t* lsw = sc_w(kt & 1);
-    const int ra0 = wm * 128 + r16, rw0 = wn * 128 + r16;
+    const int ra0 = wm * 16 * kTM + r16, rw0 = wn * 16 * kTN + r16;
     // this lane's scale bytes for the stage, one dword per tile
-    uint32_t sa[8], sw[8];
+    uint32_t sa[kTM], sw[kTN];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (MX) {
-        sa[i] = *reinterpret_cast<const uint16_t*>(lsa + (ra0 + 16 * i) * spr + 2 * g);
-        sw[i] = *reinterpret_cast<const uint16_t*>(lsw + (rw0 + 16 * i) * spr + 2 * g);
-      } else {
-        sa[i] = *reinterpret_cast<const uint32_t*>(lsa + (ra0 + 16 * i) * spr + 4 * g);
-        sw[i] = *reinterpret_cast<const uint32_t*>(lsw + (rw0 + 16 * i) * spr + 4 * g);
-      }
-    }
-    // k-step ks of the stage (the MFMA's scale byte select must be a constant)
-    auto kstep = [&](auto ks_c) {
+    for (int i = 0; i < kTM; ++i)
+      sa[i] = MX ? *reinterpret_cast<const uint16_t*>(lsa + (ra0 + 16 * i) * spr + 2 * g)
+                 : *reinterpret_cast<const uint32_t*>(lsa + (ra0 + 16 * i) * spr + 4 * g);
+#pragma unroll
+    for (int i = 0; i < kTN; ++i)
+      sw[i] = MX ? *reinterpret_cast<const uint16_t*>(lsw + (rw0 + 16 * i) * spr + 2 * g)
+                 : *reinterpret_cast<const uint32_t*>(lsw + (rw0 + 16 * i) * spr + 4 * g);
+    // MXFP4: both k-steps' fragments are read up front, so the second k-step's
+    // LDS reads are in flight while the first k-step's MFMAs run (one wave per
+    // SIMD has no other wave to hide them behind).  The MFMA's scale byte
+    // select must be a constant, hence the k-step template.
+    auto read_frags = [&](auto ks_c, u32x4 (&fa)[kTM], u32x4 (&fw)[kTN]) {
       constexpr int ks = decltype(ks_c)::value;
-      if constexpr (MX) {
-        u32x4 fa[8], fw[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          fa[i] = *reinterpret_cast<const u32x4*>(la + swz(ra0 + 16 * i, 2 * g + ks));
-          fw[i] = *reinterpret_cast<const u32x4*>(lw + swz(rw0 + 16 * i, 2 * g + ks));
-        }
+      for (int i = 0; i < kTM; ++i)
+        fa[i] = *reinterpret_cast<const u32x4*>(la + swz(ra0 + 16 * i, 2 * g + ks));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const v8i wv = {(int)fw[i].x, (int)fw[i].y, (int)fw[i].z, (int)fw[i].w, 0, 0, 0, 0};
+      for (int i = 0; i < kTN; ++i)
+        fw[i] = *reinterpret_cast<const u32x4*>(lw + swz(rw0 + 16 * i, 2 * g + ks));
+    };
+    auto mx_kstep = [&](auto ks_c, const u32x4 (&fa)[kTM], const u32x4 (&fw)[kTN]) {
+      constexpr int ks = decltype(ks_c)::value;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const v8i av = {(int)fa[j].x, (int)fa[j].y, (int)fa[j].z, (int)fa[j].w, 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                wv, av, acc[i][j], 4, 4, ks, (int)sw[i], ks, (int)sa[j]);
-          }
-        }
-      } else {
-        // (a loop, not unrolled: keeps the accumulators in place in the AGPRs)
-#pragma unroll 1
-        for (int s4 = 0; s4 < 4; ++s4) {
-          // dword s4 of the fragment: 8 values of NV block 4g + 2ks + s4 / 2
-          const int sh = 8 * (2 * ks + (s4 >> 1));
-          v8h da[8], dw[8];
+      for (int i = 0; i < kTN; ++i) {
+        const v8i wv = {(int)fw[i].x, (int)fw[i].y, (int)fw[i].z, (int)fw[i].w, 0, 0, 0, 0};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t ca = *reinterpret_cast<const uint32_t*>(la + swz(ra0 + 16 * i, 2 * g + ks) + 4 * s4);
-            const uint32_t cw = *reinterpret_cast<const uint32_t*>(lw + swz(rw0 + 16 * i, 2 * g + ks) + 4 * s4);
-            da[i] = dq8(ca, e4m3_h2((sa[i] >> sh) & 0xffu));
-            dw[i] = dq8(cw, e4m3_h2((sw[i] >> sh) & 0xffu));
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[i], da[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < kTM; ++j) {
+          const v8i av = {(int)fa[j].x, (int)fa[j].y, (int)fa[j].z, (int)fa[j].w, 0, 0, 0, 0};
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wv, av, acc[i][j], 4, 4, ks, (int)sw[i], ks, (int)sa[j]);
         }
       }
     };
-    kstep(std::integral_constant<int, 0>{});
-    if (more) {
+    auto nv_kstep = [&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
+      // (a loop, not unrolled: keeps the accumulators in place in the AGPRs)
+#pragma unroll 1
+      for (int s4 = 0; s4 < 4; ++s4) {
+        // dword s4 of the fragment: 8 values of NV block 4g + 2ks + s4 / 2
+        const int sh = 8 * (2 * ks + (s4 >> 1));
+        v8h da[kTM], dw[kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+          const uint32_t ca = *reinterpret_cast<const uint32_t*>(la + swz(ra0 + 16 * i, 2 * g + ks) + 4 * s4);
+          da[i] = dq8(ca, e4m3_h2((sa[i] >> sh) & 0xffu));
+        }
+#pragma unroll
+        for (int i = 0; i < kTN; ++i) {
+          const uint32_t cw = *reinterpret_cast<const uint32_t*>(lw + swz(rw0 + 16 * i, 2 * g + ks) + 4 * s4);
+          dw[i] = dq8(cw, e4m3_h2((sw[i] >> sh) & 0xffu));
+        }
+#pragma unroll
+        for (int i = 0; i < kTN; ++i)
+#pragma unroll
+          for (int j = 0; j < kTM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[i], da[j], acc[i][j], 0, 0, 0);
+      }
+    };
+    // scheduling barriers keep each part's LDS store after the k-step that hides
+    // its loads (the compiler would otherwise hoist the stores, and the wait
+    // for their loads, above the MFMAs)
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    if constexpr (MX) {
+      u32x4 fa0[kTM], fw0[kTN], fa1[kTM], fw1[kTN];
+      read_frags(K0{}, fa0, fw0);
+      read_frags(K1{}, fa1, fw1);
+      mx_kstep(K0{}, fa0, fw0);
+      __builtin_amdgcn_sched_barrier(0);
       store_part<MX>(st, tile_a(nb), sc_a(nb));
-      load_part<MX, SCALE_VEC>(st, src_w, src_ws, rowb, nsc, K, (kt + 1) * BK);
+      load_part<MX, SCALE_VEC>(st, more ? src_w : none, more ? src_ws : none, rowb, nsc, K,
+                               (kt + 1) * BK);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_kstep(K1{}, fa1, fw1);
+    } else {
+      nv_kstep(K0{});
+      __builtin_amdgcn_sched_barrier(0);
+      store_part<MX>(st, tile_a(nb), sc_a(nb));
+      load_part<MX, SCALE_VEC>(st, more ? src_w : none, more ? src_ws : none, rowb, nsc, K,
+                               (kt + 1) * BK);
+      __builtin_amdgcn_sched_barrier(0);
+      nv_kstep(K1{});
     }
-    kstep(std::integral_constant<int, 1>{});
-    if (more) store_part<MX>(st, tile_w(nb), sc_w(nb));
+    __builtin_amdgcn_sched_barrier(0);
+    store_part<MX>(st, tile_w(nb), sc_w(nb));
     __syncthreads();
   }
 
@@ -308,12 +348,12 @@ __global__ void __launch_bounds__(kThreads, 1)
   float alpha = g_d;
   if (!MX) alpha = ((*g_a) * (*g_b)) * g_d;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = m0 + wm * 128 + 16 * j + r16;
+  for (int j = 0; j < kTM; ++j) {
+    const int m = m0 + wm * 16 * kTM + 16 * j + r16;
     if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = n0 + wn * 128 + 16 * i + 4 * g;
+    for (int i = 0; i < kTN; ++i) {
+      const int n = n0 + wn * 16 * kTN + 16 * i + 4 * g;
       const v4f v = acc[i][j] * alpha;
       if (OUT_BF16) {
         uint16_t* row = reinterpret_cast<uint16_t*>(D) + (int64_t)m * N;
