@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   auto tile_w = [&](int b) { return smem + b * kStage + kTileBytes; };
   auto sc_a = [&](int b) { return smem + b * kStage + 2 * kTileBytes; };
   auto sc_w = [&](int b) { return smem + b * kStage + 2 * kTileBytes + Cfg<MX>::kScaleBytes; };
-  StageRegs<MX> st;
+  StageRegs<MX> st, st2;
   load_part<MX, SCALE_VEC>(st, src_a, src_as, rowb, nsc, K, 0);
   store_part<MX>(st, tile_a(0), sc_a(0));
   load_part<MX, SCALE_VEC>(st, src_w, src_ws, rowb, nsc, K, 0);
@@ -244,9 +244,11 @@ __global__ void __launch_bounds__(kThreads, 1)
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
     const int nb = (kt + 1) & 1;
-    // the next stage passes through registers one operand at a time: A during
-    // k-step 0, W during k-step 1
+    // the next stage's loads are issued first; A is stored after k-step 0, W
+    // after k-step 1
     load_part<MX, SCALE_VEC>(st, more ? src_a : none, more ? src_as : none, rowb, nsc, K,
+                             (kt + 1) * BK);
+    load_part<MX, SCALE_VEC>(st2, more ? src_w : none, more ? src_ws : none, rowb, nsc, K,
                              (kt + 1) * BK);
     const uint8_t* la = tile_a(kt & 1);
     const uint8_t* lw = tile_w(kt & 1);
@@ -326,21 +328,17 @@ __global__ void __launch_bounds__(kThreads, 1)
       mx_kstep(K0{}, fa0, fw0);
       __builtin_amdgcn_sched_barrier(0);
       store_part<MX>(st, tile_a(nb), sc_a(nb));
-      load_part<MX, SCALE_VEC>(st, more ? src_w : none, more ? src_ws : none, rowb, nsc, K,
-                               (kt + 1) * BK);
       __builtin_amdgcn_sched_barrier(0);
       mx_kstep(K1{}, fa1, fw1);
     } else {
       nv_kstep(K0{});
       __builtin_amdgcn_sched_barrier(0);
       store_part<MX>(st, tile_a(nb), sc_a(nb));
-      load_part<MX, SCALE_VEC>(st, more ? src_w : none, more ? src_ws : none, rowb, nsc, K,
-                               (kt + 1) * BK);
       __builtin_amdgcn_sched_barrier(0);
       nv_kstep(K1{});
     }
     __builtin_amdgcn_sched_barrier(0);
-    store_part<MX>(st, tile_w(nb), sc_w(nb));
+    store_part<MX>(st2, tile_w(nb), sc_w(nb));
     __syncthreads();
   }
 
