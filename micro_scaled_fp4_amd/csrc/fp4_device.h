@@ -144,6 +144,38 @@ __device__ __forceinline__ void stage_blocks(const u32x4* __restrict__ src, int6
   __syncthreads();
 }
 
+// The same staging split in two, so a kernel can issue a chunk's loads one
+// chunk ahead: chunk_load reads vectors threadIdx.x + NT k (k < VPB) of the
+// chunk (past the chunk's end the address is clamped onto its last vector, so
+// the loaded registers are never selected on, which would make the load wait);
+// chunk_deal writes them to LDS and hands thread t its block's VPB vectors.
+template <int VPB, int NT>
+__device__ __forceinline__ void chunk_load(const u32x4* __restrict__ src, int64_t base, int nb,
+                                           u32x4 (&raw)[VPB]) {
+#pragma unroll
+  for (int k = 0; k < VPB; ++k) {
+    const int i = threadIdx.x + NT * k;
+    const int ic = i < VPB * nb ? i : VPB * nb - 1;
+    raw[k] = __builtin_nontemporal_load(src + base * VPB + ic);
+  }
+}
+
+template <int VPB, int NT>
+__device__ __forceinline__ void chunk_deal(const u32x4 (&raw)[VPB], int nb, u32x4* lds,
+                                           u32x4 (&out)[VPB]) {
+#pragma unroll
+  for (int k = 0; k < VPB; ++k) {
+    const int i = threadIdx.x + NT * k;
+    if (i < VPB * nb) lds[(i % VPB) * (NT + 1) + i / VPB] = raw[k];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nb) {
+#pragma unroll
+    for (int k = 0; k < VPB; ++k) out[k] = lds[k * (NT + 1) + threadIdx.x];
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------- wave reductions --
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

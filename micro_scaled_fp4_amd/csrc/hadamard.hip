@@ -171,12 +171,18 @@ __global__ void __launch_bounds__(kThreads)
   const int p = threadIdx.x & 3;
   uint32_t m = 0;
   // nslots and the chunk bases are multiples of 4, so the lanes of a quad are
-  // all active or all idle (DPP partners are always active).
-  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nslots;
-       base += (int64_t)gridDim.x * kThreads) {
-    const int nb = (int)(nslots - base < kThreads ? nslots - base : kThreads);
+  // all active or all idle (DPP partners are always active).  The next chunk's
+  // loads are in flight while this chunk is rotated.
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  auto chunk_nb = [&](int64_t b) { return (int)(nslots - b < kThreads ? nslots - b : kThreads); };
+  u32x4 raw[VPB];
+  int64_t base = (int64_t)blockIdx.x * kThreads;
+  if (base < nslots) chunk_load<VPB, kThreads>(xv, base, chunk_nb(base), raw);
+  for (; base < nslots; base += stride) {
+    const int nb = chunk_nb(base);
     u32x4 w[VPB];
-    stage_blocks<VPB, kThreads>(xv, base, nb, lds, w);
+    chunk_deal<VPB, kThreads>(raw, nb, lds, w);
+    if (base + stride < nslots) chunk_load<VPB, kThreads>(xv, base + stride, chunk_nb(base + stride), raw);
     if ((int)threadIdx.x >= nb) continue;
     float v[kPer];
     unpack32<BF16>(w, v);
@@ -212,11 +218,17 @@ __global__ void __launch_bounds__(kThreads)
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   const int p = threadIdx.x & 3;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nslots;
-       base += (int64_t)gridDim.x * kThreads) {
-    const int nb = (int)(nslots - base < kThreads ? nslots - base : kThreads);
+  // the next chunk's loads are in flight while this chunk is rotated and encoded
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  auto chunk_nb = [&](int64_t b) { return (int)(nslots - b < kThreads ? nslots - b : kThreads); };
+  u32x4 raw[VPB];
+  int64_t base = (int64_t)blockIdx.x * kThreads;
+  if (base < nslots) chunk_load<VPB, kThreads>(xv, base, chunk_nb(base), raw);
+  for (; base < nslots; base += stride) {
+    const int nb = chunk_nb(base);
     u32x4 wv[VPB];
-    stage_blocks<VPB, kThreads>(xv, base, nb, lds, wv);
+    chunk_deal<VPB, kThreads>(raw, nb, lds, wv);
+    if (base + stride < nslots) chunk_load<VPB, kThreads>(xv, base + stride, chunk_nb(base + stride), raw);
     if ((int)threadIdx.x >= nb) continue;
     const int64_t s = base + threadIdx.x;
     float v[kPer];
