@@ -19,8 +19,8 @@
 // byte moved into fp16 fields (= E4M3 * 2^-8), both exact; then
 // v_mfma_f32_16x16x32_f16 accumulates in float32.  Ceiling: the fp16 MFMA rate.
 //
-// Tiling: 256x256 output tile per workgroup, kWavesM x kWavesN waves, each with
-// its own block of 16x16 MFMA tiles (accumulators in AGPRs).  K advances 256 values
+// Tiling: BM x BN (256 x 256) output tile per workgroup, 2 x 2 waves, each with
+// its own 8 x 8 block of 16x16 MFMA tiles (accumulators in AGPRs).  K advances 256 values
 // (128 bytes per row) per stage; stages are double-buffered in LDS through
 // registers (the next stage's global loads are in flight while this stage
 // computes; one barrier per stage).  A 16-byte chunk c of tile row r is stored
@@ -51,12 +51,20 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kWavesM = 2, kWavesN = 2;       // wave grid of the workgroup
 constexpr int kThreads = 64 * kWavesM * kWavesN;
-constexpr int kTM = 256 / 16 / kWavesM;       // 16-row A tiles per wave
-constexpr int kTN = 256 / 16 / kWavesN;       // 16-row W tiles per wave
-constexpr int BM = 256, BN = 256, BK = 256;   // BK in FP4 values
+// 16-row MFMA tiles per wave: 8 of A by 8 of W (256 accumulator registers)
+constexpr int kTM = 8;
+constexpr int kTN = 8;
+constexpr int BM = 16 * kTM * kWavesM;        // 256 rows of A per workgroup
+constexpr int BN = 16 * kTN * kWavesN;        // 256 rows of W
+constexpr int BK = 256;                       // FP4 values per stage
 constexpr int kRowBytes = BK / 2;             // 128
-constexpr int kTileBytes = BM * kRowBytes;    // 32 KB
-constexpr int kChunks = kTileBytes / 16 / kThreads;   // 16-byte chunks per thread per tile
+constexpr int kTileA = BM * kRowBytes;        // 32 KB
+constexpr int kTileW = BN * kRowBytes;        // 32 KB
+// 16-byte chunks per thread for a tile of ROWS rows (ROWS * 8 is a multiple of kThreads)
+template <int ROWS>
+constexpr int chunks_of() { return ROWS * kRowBytes / 16 / kThreads; }
+static_assert(BM * kRowBytes % (16 * kThreads) == 0 && BN * kRowBytes % (16 * kThreads) == 0,
+              "tiles must split evenly over the threads");
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;      // raw buffer descriptor word 3 (gfx9 family)
@@ -65,8 +73,9 @@ constexpr int kOutOfRange = 0x7ffffff0;       // a buffer offset past every rang
 template <bool MX>
 struct Cfg {
   static constexpr int kScaleRow = MX ? BK / 32 : BK / 16;          // scale bytes per row per stage
-  static constexpr int kScaleBytes = BM * kScaleRow;
-  static constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleBytes;
+  static constexpr int kScaleA = BM * kScaleRow;
+  static constexpr int kScaleW = BN * kScaleRow;
+  static constexpr int kStageBytes = kTileA + kTileW + kScaleA + kScaleW;
   static constexpr int kLdsBytes = 2 * kStageBytes;                 // 136 KB (MX) / 144 KB (NV)
 };
 
@@ -89,25 +98,25 @@ __device__ __forceinline__ int swz(int row, int chunk) {   // byte offset in a t
 }
 
 // ------------------------------------------------------------- stage loads --
-// Thread t loads 16-byte chunks t + kThreads j (j < kChunks) of each 256-row x 128-byte
+// Thread t loads 16-byte chunks t + kThreads j of each ROWS-row x 128-byte
 // tile (row = chunk / 8) and the stage's scale bytes of row t.  Reads go
 // through per-tile buffer descriptors whose range is the tile's rows that
 // exist; chunks past K and rows past the matrix read zeros (value 0, and the
 // scale bytes of such rows are never stored to an output).
-// One operand's part of a stage: its 8 chunks per thread and its scale bytes.
-template <bool MX>
+// One operand's part of a stage: its chunks and its scale bytes.
+template <bool MX, int ROWS>
 struct StageRegs {
-  u32x4 d[kChunks];
+  u32x4 d[chunks_of<ROWS>()];
   uint32_t s[MX ? 2 : 4];
 };
 
-template <bool MX, bool SCALE_VEC>
-__device__ __forceinline__ void load_part(StageRegs<MX>& r, __amdgpu_buffer_rsrc_t data,
+template <bool MX, bool SCALE_VEC, int ROWS>
+__device__ __forceinline__ void load_part(StageRegs<MX, ROWS>& r, __amdgpu_buffer_rsrc_t data,
                                           __amdgpu_buffer_rsrc_t scales, int rowb, int nsc, int K,
                                           int k0) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
+  for (int j = 0; j < chunks_of<ROWS>(); ++j) {
     const int c = t + kThreads * j;
     const int row = c >> 3, ch = c & 7;
     const int kc = k0 + 32 * ch;
@@ -118,7 +127,7 @@ __device__ __forceinline__ void load_part(StageRegs<MX>& r, __amdgpu_buffer_rsrc
   constexpr int bs = MX ? 32 : 16;
   constexpr int spr = Cfg<MX>::kScaleRow;
   const int kb = k0 / bs;
-  const int sr = t % BM;   // scale row (threads past 256 repeat rows: same bytes, same place)
+  const int sr = t % ROWS;   // scale row (threads past ROWS repeat rows: same bytes, same place)
   if (SCALE_VEC) {   // K % 256 == 0 and 16-byte aligned scale rows
     if (MX) {
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(scales, sr * nsc + kb, 0, 0);
@@ -147,16 +156,16 @@ __device__ __forceinline__ void load_part(StageRegs<MX>& r, __amdgpu_buffer_rsrc
 }
 
 // tile: the operand's 32 KB tile in the stage buffer; sc: its scale rows
-template <bool MX>
-__device__ __forceinline__ void store_part(const StageRegs<MX>& r, uint8_t* __restrict__ tile,
+template <bool MX, int ROWS>
+__device__ __forceinline__ void store_part(const StageRegs<MX, ROWS>& r, uint8_t* __restrict__ tile,
                                            uint8_t* __restrict__ sc) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
+  for (int j = 0; j < chunks_of<ROWS>(); ++j) {
     const int c = t + kThreads * j;
     *reinterpret_cast<u32x4*>(tile + swz(c >> 3, c & 7)) = r.d[j];
   }
-  uint8_t* sp = sc + (t % BM) * Cfg<MX>::kScaleRow;
+  uint8_t* sp = sc + (t % ROWS) * Cfg<MX>::kScaleRow;
   if (MX)
     *reinterpret_cast<u32x2*>(sp) = u32x2{r.s[0], r.s[1]};
   else
@@ -225,14 +234,15 @@ __global__ void __launch_bounds__(kThreads, 1)
   constexpr int kStage = Cfg<MX>::kStageBytes;
   // stage buffer layout: A tile | W tile | A scale rows | W scale rows
   auto tile_a = [&](int b) { return smem + b * kStage; };
-  auto tile_w = [&](int b) { return smem + b * kStage + kTileBytes; };
-  auto sc_a = [&](int b) { return smem + b * kStage + 2 * kTileBytes; };
-  auto sc_w = [&](int b) { return smem + b * kStage + 2 * kTileBytes + Cfg<MX>::kScaleBytes; };
-  StageRegs<MX> st, st2;
-  load_part<MX, SCALE_VEC>(st, src_a, src_as, rowb, nsc, K, 0);
-  store_part<MX>(st, tile_a(0), sc_a(0));
-  load_part<MX, SCALE_VEC>(st, src_w, src_ws, rowb, nsc, K, 0);
-  store_part<MX>(st, tile_w(0), sc_w(0));
+  auto tile_w = [&](int b) { return smem + b * kStage + kTileA; };
+  auto sc_a = [&](int b) { return smem + b * kStage + kTileA + kTileW; };
+  auto sc_w = [&](int b) { return smem + b * kStage + kTileA + kTileW + Cfg<MX>::kScaleA; };
+  StageRegs<MX, BM> st;
+  StageRegs<MX, BN> st2;
+  load_part<MX, SCALE_VEC, BM>(st, src_a, src_as, rowb, nsc, K, 0);
+  store_part<MX, BM>(st, tile_a(0), sc_a(0));
+  load_part<MX, SCALE_VEC, BN>(st2, src_w, src_ws, rowb, nsc, K, 0);
+  store_part<MX, BN>(st2, tile_w(0), sc_w(0));
   __syncthreads();
 
   // The loop body has no branch (a branch lets the compiler sink the MFMAs past
@@ -246,10 +256,10 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int nb = (kt + 1) & 1;
     // the next stage's loads are issued first; A is stored after k-step 0, W
     // after k-step 1
-    load_part<MX, SCALE_VEC>(st, more ? src_a : none, more ? src_as : none, rowb, nsc, K,
-                             (kt + 1) * BK);
-    load_part<MX, SCALE_VEC>(st2, more ? src_w : none, more ? src_ws : none, rowb, nsc, K,
-                             (kt + 1) * BK);
+    load_part<MX, SCALE_VEC, BM>(st, more ? src_a : none, more ? src_as : none, rowb, nsc, K,
+                                 (kt + 1) * BK);
+    load_part<MX, SCALE_VEC, BN>(st2, more ? src_w : none, more ? src_ws : none, rowb, nsc, K,
+                                 (kt + 1) * BK);
     const uint8_t* la = tile_a(kt & 1);
     const uint8_t* lw = tile_w(kt & 1);
     const uint8_t* lsa = sc_a(kt & 1);
@@ -327,18 +337,18 @@ __global__ void __launch_bounds__(kThreads, 1)
       read_frags(K1{}, fa1, fw1);
       mx_kstep(K0{}, fa0, fw0);
       __builtin_amdgcn_sched_barrier(0);
-      store_part<MX>(st, tile_a(nb), sc_a(nb));
+      store_part<MX, BM>(st, tile_a(nb), sc_a(nb));
       __builtin_amdgcn_sched_barrier(0);
       mx_kstep(K1{}, fa1, fw1);
     } else {
       nv_kstep(K0{});
       __builtin_amdgcn_sched_barrier(0);
-      store_part<MX>(st, tile_a(nb), sc_a(nb));
+      store_part<MX, BM>(st, tile_a(nb), sc_a(nb));
       __builtin_amdgcn_sched_barrier(0);
       nv_kstep(K1{});
     }
     __builtin_amdgcn_sched_barrier(0);
-    store_part<MX>(st2, tile_w(nb), sc_w(nb));
+    store_part<MX, BN>(st2, tile_w(nb), sc_w(nb));
     __syncthreads();
   }
 
