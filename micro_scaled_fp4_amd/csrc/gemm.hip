@@ -21,11 +21,14 @@
 //
 // Tiling: BM x BN (256 x 256) output tile per workgroup, 2 x 2 waves, each with
 // its own 8 x 8 block of 16x16 MFMA tiles (accumulators in AGPRs).  K advances 256 values
-// (128 bytes per row) per stage; stages are double-buffered in LDS through
-// registers (the next stage's global loads are in flight while this stage
-// computes; one barrier per stage).  A 16-byte chunk c of tile row r is stored
-// at chunk position c ^ ((r >> 1) & 7): the 16 rows of a fragment read then
-// cover all 64 banks.  Inside a stage, lane group g (lane / 16) takes values
+// (128 bytes per row) per stage in two k-steps of 128; stages are
+// double-buffered in LDS and filled by buffer loads that write LDS directly
+// (no register staging, no LDS store instructions), one barrier per stage.
+// MXFP4 runs the loads two stages ahead and reads the next k-step's operand
+// fragments while the current k-step's MFMAs run, one MFMA row at a time, so
+// no MFMA waits on LDS after a barrier.  A 16-byte chunk c of tile row r is
+// stored at chunk position c ^ ((r >> 1) & 7): the 16 rows of a fragment read
+// then cover all 64 banks.  Inside a stage, lane group g (lane / 16) takes values
 // [64g + 32ks, +32) in k-step ks, identically for both operands (the MFMA sum
 // does not depend on the K order), so a lane's scale bytes for the stage are
 // contiguous: 2 bytes (MXFP4, byte ks selected by the MFMA) or 4 (NVFP4).
@@ -36,6 +39,7 @@
 // of 8 row-tiles so concurrently running workgroups of an XCD share operand
 // rows in its L2.
 #include <type_traits>
+#include <utility>
 
 #include "fp4_device.h"
 #include "fp4_internal.h"
@@ -60,11 +64,8 @@ constexpr int BK = 256;                       // FP4 values per stage
 constexpr int kRowBytes = BK / 2;             // 128
 constexpr int kTileA = BM * kRowBytes;        // 32 KB
 constexpr int kTileW = BN * kRowBytes;        // 32 KB
-// 16-byte chunks per thread for a tile of ROWS rows (ROWS * 8 is a multiple of kThreads)
-template <int ROWS>
-constexpr int chunks_of() { return ROWS * kRowBytes / 16 / kThreads; }
-static_assert(BM * kRowBytes % (16 * kThreads) == 0 && BN * kRowBytes % (16 * kThreads) == 0,
-              "tiles must split evenly over the threads");
+// the stage loads below assume 256-row tiles of both operands, one scale row per thread
+static_assert(BM == 256 && BN == 256 && kThreads == 256, "stage loads assume 256-row tiles");
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;      // raw buffer descriptor word 3 (gfx9 family)
@@ -93,41 +94,106 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = r / gsize;
 }
 
+// D += W x A with block scales, FP4 operands (16 bytes of codes per lane):
+// v_mfma_scale_f32_16x16x128_f8f6f4, accumulating in place in AGPRs.  SW / SA
+// select the scale byte of sw / sa.  Written as inline asm because the
+// compiler, with all 256 AGPRs holding accumulators, moves accumulators
+// between AGPRs and VGPRs around its own MFMAs (hundreds of copies per stage).
+// The compiler does not apply MFMA hazard rules to inline asm, so the callers
+// keep them: operands come straight from LDS reads (waited on by the
+// compiler), each group of MFMAs starts after 2 wait states (s_nop 1, for a
+// vector-ALU write of an operand just before), and results are read only
+// after mfma_drain.
+template <int SW, int SA>
+__device__ __forceinline__ void mfma_fp4(v4f& acc, const u32x4& w, const u32x4& a, uint32_t sw,
+                                         uint32_t sa) {
+  asm volatile(
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0] "
+      "cbsz:4 blgp:4"
+      : "+a"(acc)
+      : "v"(w), "v"(a), "v"(sw), "v"(sa), "n"(SW & 1), "n"(SA & 1), "n"(SW >> 1), "n"(SA >> 1));
+}
+// 2 wait states before a group of MFMAs (vector-ALU write -> MFMA read)
+__device__ __forceinline__ void mfma_lead() { asm volatile("s_nop 1"); }
+// wait states after the last MFMA before its result is read (24 >= what a
+// 4-pass MFMA result needs before a vector-ALU or accvgpr read)
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+
+// Wait until this wave's buffer loads, including those that write LDS
+// directly, have completed (vmcnt(0); the lgkm and exp counters are left
+// alone).  The compiler does not count direct-to-LDS loads as LDS writes, so
+// each barrier that publishes such loads to the workgroup is preceded by this.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// lgkmcnt(0): LDS and scalar-memory operations of this wave have completed
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{})
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ int swz(int row, int chunk) {   // byte offset in a tile
   return row * kRowBytes + 16 * (chunk ^ ((row >> 1) & 7));
 }
 
 // ------------------------------------------------------------- stage loads --
-// Thread t loads 16-byte chunks t + kThreads j of each ROWS-row x 128-byte
-// tile (row = chunk / 8) and the stage's scale bytes of row t.  Reads go
-// through per-tile buffer descriptors whose range is the tile's rows that
-// exist; chunks past K and rows past the matrix read zeros (value 0, and the
-// scale bytes of such rows are never stored to an output).
-// One operand's part of a stage: its chunks and its scale bytes.
-template <bool MX, int ROWS>
-struct StageRegs {
-  u32x4 d[chunks_of<ROWS>()];
+// Operand tiles go from global memory straight into LDS (buffer loads with the
+// LDS flag): one instruction moves 64 x 16 bytes, lane l's 16 bytes landing at
+// LDS base + 16 l.  A 256-row tile is 32 such 1 KB blocks (8 rows each); wave
+// w loads blocks w, w + 4, ...  Lane l of block b fills tile row 8b + l / 8 at
+// chunk position l % 8, so it fetches the chunk that the swizzle puts there.
+// Reads go through per-tile buffer descriptors whose range is the tile's rows
+// that exist: rows past the matrix and chunks past K land in LDS as zeros
+// (value 0; the scale bytes of such rows never reach an output).
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kBlocksPerWave = 256 * kRowBytes / 1024 / (kThreads / 64);   // 8
+static_assert(kThreads == 256, "blocks are dealt to 4 waves");
+
+// Block q (of kBlocksPerWave) of this wave's share of an operand tile.
+template <bool SCALE_VEC>
+__device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t src, uint8_t* tile, int rowb, int K,
+                                          int k0, int q) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // block b = wave + 4q holds rows 8b .. 8b + 7; the swizzle of those rows
+  // depends only on the parity of b, which is the parity of the wave
+  const int row0 = 8 * wave + (lane >> 3);
+  const int ch = (lane & 7) ^ ((row0 >> 1) & 7);   // logical chunk stored at position lane % 8
+  const int kc = k0 + 32 * ch;
+  lds_void* dst = (lds_void*)(tile + 1024 * (wave + 4 * q));
+  if (SCALE_VEC)   // K % 256 == 0: no chunk of a stage is past K; the block's row offset is scalar
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, row0 * rowb + kc / 2, 32 * q * rowb, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, kc < K ? (row0 + 32 * q) * rowb + kc / 2 : kOutOfRange,
+                                             0, 0, 0);
+}
+
+template <bool SCALE_VEC>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t src, uint8_t* tile, int rowb, int K,
+                                         int k0) {
+#pragma unroll
+  for (int q = 0; q < kBlocksPerWave; ++q) dma_block<SCALE_VEC>(src, tile, rowb, K, k0, q);
+}
+
+// One operand's scale bytes of a stage, in registers between their global load
+// and their LDS store: thread t holds row t's 8 (MXFP4) or 16 (NVFP4) bytes.
+template <bool MX>
+struct StageScales {
   uint32_t s[MX ? 2 : 4];
 };
 
-template <bool MX, bool SCALE_VEC, int ROWS>
-__device__ __forceinline__ void load_part(StageRegs<MX, ROWS>& r, __amdgpu_buffer_rsrc_t data,
-                                          __amdgpu_buffer_rsrc_t scales, int rowb, int nsc, int K,
-                                          int k0) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < chunks_of<ROWS>(); ++j) {
-    const int c = t + kThreads * j;
-    const int row = c >> 3, ch = c & 7;
-    const int kc = k0 + 32 * ch;
-    // (SCALE_VEC implies K % 256 == 0: no chunk of a stage is past K)
-    r.d[j] = __builtin_amdgcn_raw_buffer_load_b128(
-        data, (SCALE_VEC || kc < K) ? row * rowb + kc / 2 : kOutOfRange, 0, 0);
-  }
+template <bool MX, bool SCALE_VEC>
+__device__ __forceinline__ void load_scales(StageScales<MX>& r, __amdgpu_buffer_rsrc_t scales, int nsc,
+                                            int k0) {
   constexpr int bs = MX ? 32 : 16;
   constexpr int spr = Cfg<MX>::kScaleRow;
   const int kb = k0 / bs;
-  const int sr = t % ROWS;   // scale row (threads past ROWS repeat rows: same bytes, same place)
+  const int sr = threadIdx.x;
   if (SCALE_VEC) {   // K % 256 == 0 and 16-byte aligned scale rows
     if (MX) {
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(scales, sr * nsc + kb, 0, 0);
@@ -155,21 +221,23 @@ __device__ __forceinline__ void load_part(StageRegs<MX, ROWS>& r, __amdgpu_buffe
   }
 }
 
-// tile: the operand's 32 KB tile in the stage buffer; sc: its scale rows
-template <bool MX, int ROWS>
-__device__ __forceinline__ void store_part(const StageRegs<MX, ROWS>& r, uint8_t* __restrict__ tile,
-                                           uint8_t* __restrict__ sc) {
-  const int t = threadIdx.x;
+// LDS scale layout of an operand: entry (h, g, r16, i) holds the bytes that lane
+// group g of MFMA tile i of wave half h needs for tile row r16 (MXFP4: 2 bytes,
+// one per k-step; NVFP4: 4 bytes, one per 16 values).  The 8 tiles' entries of
+// (h, g, r16) are contiguous, so a lane fetches its whole stage's scales with
+// one (MXFP4) or two (NVFP4) 16-byte reads.  Thread t holds scale row t, which
+// is row r16 = t % 16 of tile t / 16 = 8 h + i of the 256-row operand tile.
+template <bool MX>
+__device__ __forceinline__ void store_scales(const StageScales<MX>& r, uint8_t* __restrict__ sc) {
+  const int t = threadIdx.x, h = t >> 7, i = (t >> 4) & 7, r16 = t & 15;
 #pragma unroll
-  for (int j = 0; j < chunks_of<ROWS>(); ++j) {
-    const int c = t + kThreads * j;
-    *reinterpret_cast<u32x4*>(tile + swz(c >> 3, c & 7)) = r.d[j];
+  for (int g = 0; g < 4; ++g) {
+    const int e = ((h * 4 + g) * 16 + r16) * 8 + i;
+    if (MX)
+      reinterpret_cast<uint16_t*>(sc)[e] = (uint16_t)(r.s[g >> 1] >> (16 * (g & 1)));
+    else
+      reinterpret_cast<uint32_t*>(sc)[e] = r.s[g];
   }
-  uint8_t* sp = sc + (t % ROWS) * Cfg<MX>::kScaleRow;
-  if (MX)
-    *reinterpret_cast<u32x2*>(sp) = u32x2{r.s[0], r.s[1]};
-  else
-    *reinterpret_cast<u32x4*>(sp) = u32x4{r.s[0], r.s[1], r.s[2], r.s[3]};
 }
 
 // --------------------------------------------------------- NV fragment dequant --
@@ -231,125 +299,202 @@ __global__ void __launch_bounds__(kThreads, 1)
     for (int j = 0; j < kTM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nk = (K + BK - 1) / BK;
-  constexpr int kStage = Cfg<MX>::kStageBytes;
-  // stage buffer layout: A tile | W tile | A scale rows | W scale rows
-  auto tile_a = [&](int b) { return smem + b * kStage; };
-  auto tile_w = [&](int b) { return smem + b * kStage + kTileA; };
-  auto sc_a = [&](int b) { return smem + b * kStage + kTileA + kTileW; };
-  auto sc_w = [&](int b) { return smem + b * kStage + kTileA + kTileW + Cfg<MX>::kScaleA; };
-  StageRegs<MX, BM> st;
-  StageRegs<MX, BN> st2;
-  load_part<MX, SCALE_VEC, BM>(st, src_a, src_as, rowb, nsc, K, 0);
-  store_part<MX, BM>(st, tile_a(0), sc_a(0));
-  load_part<MX, SCALE_VEC, BN>(st2, src_w, src_ws, rowb, nsc, K, 0);
-  store_part<MX, BN>(st2, tile_w(0), sc_w(0));
-  __syncthreads();
-
-  // The loop body has no branch (a branch lets the compiler sink the MFMAs past
-  // the stores and the barrier): after the last stage the next-stage loads read
-  // through empty descriptors (zeros, no memory traffic) into the buffer nobody
-  // reads again.
+  // LDS layout: A scales of buffers 0, 1 | W scales 0, 1 | A tiles 0, 1 | W tiles 0, 1
+  // (every access of one kind differs from the others by a 16-bit LDS offset)
+  constexpr int kScA = Cfg<MX>::kScaleA, kScW = Cfg<MX>::kScaleW;
+  constexpr int kTiles = 2 * (kScA + kScW);
+  auto sc_a = [&](int b) { return smem + b * kScA; };
+  auto sc_w = [&](int b) { return smem + 2 * kScA + b * kScW; };
+  auto tile_a = [&](int b) { return smem + kTiles + b * kTileA; };
+  auto tile_w = [&](int b) { return smem + kTiles + 2 * kTileA + b * kTileW; };
+  // an empty range: loads through it read zeros and touch no memory
   const __amdgpu_buffer_rsrc_t none =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A), 0, 0, kBufferWord3);
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    const int nb = (kt + 1) & 1;
-    // the next stage's loads are issued first; A is stored after k-step 0, W
-    // after k-step 1
-    load_part<MX, SCALE_VEC, BM>(st, more ? src_a : none, more ? src_as : none, rowb, nsc, K,
-                                 (kt + 1) * BK);
-    load_part<MX, SCALE_VEC, BN>(st2, more ? src_w : none, more ? src_ws : none, rowb, nsc, K,
-                                 (kt + 1) * BK);
-    const uint8_t* la = tile_a(kt & 1);
-    const uint8_t* lw = tile_w(kt & 1);
-    const uint8_t* lsa = sc_a(kt & 1);
-    const uint8_t* lsw = sc_w(kt & 1);
-    const int ra0 = wm * 16 * kTM + r16, rw0 = wn * 16 * kTN + r16;
-    // this lane's scale bytes for the stage, one dword per tile
-    uint32_t sa[kTM], sw[kTN];
+  const int ra0 = wm * 16 * kTM + r16, rw0 = wn * 16 * kTN + r16;
+
+  // this lane's scale bytes of a stage (layout at store_scales).  MXFP4: tile i's
+  // two bytes are bytes 2 (i & 1) + ks of dword i / 2 (the MFMA selects the
+  // byte); NVFP4: dword i, byte 2 ks + s4 / 2 for dword s4 of k-step ks.
+  constexpr int kScDw = MX ? 4 : 8;   // dwords per lane per operand
+  auto read_scales = [&](int b, uint32_t (&sa)[kScDw], uint32_t (&sw)[kScDw]) {
+    const u32x4* lsa = reinterpret_cast<const u32x4*>(sc_a(b)) + ((wm * 4 + g) * 16 + r16) * (kScDw / 4);
+    const u32x4* lsw = reinterpret_cast<const u32x4*>(sc_w(b)) + ((wn * 4 + g) * 16 + r16) * (kScDw / 4);
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
-      sa[i] = MX ? *reinterpret_cast<const uint16_t*>(lsa + (ra0 + 16 * i) * spr + 2 * g)
-                 : *reinterpret_cast<const uint32_t*>(lsa + (ra0 + 16 * i) * spr + 4 * g);
+    for (int q = 0; q < kScDw / 4; ++q) {
+      const u32x4 va = lsa[q], vw = lsw[q];
+      sa[4 * q] = va.x; sa[4 * q + 1] = va.y; sa[4 * q + 2] = va.z; sa[4 * q + 3] = va.w;
+      sw[4 * q] = vw.x; sw[4 * q + 1] = vw.y; sw[4 * q + 2] = vw.z; sw[4 * q + 3] = vw.w;
+    }
+  };
+  // MXFP4 operand fragment: 32 FP4 values (16 bytes) of a tile row per lane
+  auto frag = [&](const uint8_t* tile, int row, int chunk) {
+    return *reinterpret_cast<const u32x4*>(tile + swz(row, chunk));
+  };
+  auto read_frags = [&](int b, auto ks_c, u32x4 (&fa)[kTM], u32x4 (&fw)[kTN]) {
+    constexpr int ks = decltype(ks_c)::value;
 #pragma unroll
-    for (int i = 0; i < kTN; ++i)
-      sw[i] = MX ? *reinterpret_cast<const uint16_t*>(lsw + (rw0 + 16 * i) * spr + 2 * g)
-                 : *reinterpret_cast<const uint32_t*>(lsw + (rw0 + 16 * i) * spr + 4 * g);
-    // MXFP4: both k-steps' fragments are read up front, so the second k-step's
-    // LDS reads are in flight while the first k-step's MFMAs run (one wave per
-    // SIMD has no other wave to hide them behind).  The MFMA's scale byte
-    // select must be a constant, hence the k-step template.
-    auto read_frags = [&](auto ks_c, u32x4 (&fa)[kTM], u32x4 (&fw)[kTN]) {
-      constexpr int ks = decltype(ks_c)::value;
+    for (int i = 0; i < kTM; ++i) fa[i] = frag(tile_a(b), ra0 + 16 * i, 2 * g + ks);
 #pragma unroll
-      for (int i = 0; i < kTM; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(la + swz(ra0 + 16 * i, 2 * g + ks));
+    for (int i = 0; i < kTN; ++i) fw[i] = frag(tile_w(b), rw0 + 16 * i, 2 * g + ks);
+  };
+  // row i of k-step ks: W tile i against the kTM A tiles.  The MFMA's scale
+  // byte select must be a constant, hence the templates.
+  auto mx_row = [&](auto i_c, auto ks_c, const u32x4 (&fa)[kTM], const u32x4 (&fw)[kTN],
+                    const uint32_t (&sa)[kScDw], const uint32_t (&sw)[kScDw]) {
+    constexpr int i = decltype(i_c)::value;
+    constexpr int ks = decltype(ks_c)::value;
+    static_for<kTM>([&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      mfma_fp4<2 * (i & 1) + ks, 2 * (j & 1) + ks>(acc[i][j], fw[i], fa[j], sw[i >> 1], sa[j >> 1]);
+    });
+  };
+  // NVFP4 k-step: per dword of the fragment, dequantize 8 values per tile to
+  // fp16 and run the fp16 MFMAs (the dwords are read from LDS as they are used)
+  auto nv_kstep = [&](int b, auto ks_c, const uint32_t (&sa)[kScDw], const uint32_t (&sw)[kScDw]) {
+    constexpr int ks = decltype(ks_c)::value;
+    const uint8_t* la = tile_a(b);
+    const uint8_t* lw = tile_w(b);
+    // (a loop, not unrolled: keeps the accumulators in place in the AGPRs)
+#pragma unroll 1
+    for (int s4 = 0; s4 < 4; ++s4) {
+      // dword s4 of the fragment: 8 values of NV block 4g + 2ks + s4 / 2
+      const int sh = 8 * (2 * ks + (s4 >> 1));
+      v8h da[kTM], dw[kTN];
 #pragma unroll
-      for (int i = 0; i < kTN; ++i)
-        fw[i] = *reinterpret_cast<const u32x4*>(lw + swz(rw0 + 16 * i, 2 * g + ks));
-    };
-    auto mx_kstep = [&](auto ks_c, const u32x4 (&fa)[kTM], const u32x4 (&fw)[kTN]) {
-      constexpr int ks = decltype(ks_c)::value;
+      for (int i = 0; i < kTM; ++i) {
+        const uint32_t ca = *reinterpret_cast<const uint32_t*>(la + swz(ra0 + 16 * i, 2 * g + ks) + 4 * s4);
+        da[i] = dq8(ca, e4m3_h2((sa[i] >> sh) & 0xffu));
+      }
 #pragma unroll
       for (int i = 0; i < kTN; ++i) {
-        const v8i wv = {(int)fw[i].x, (int)fw[i].y, (int)fw[i].z, (int)fw[i].w, 0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < kTM; ++j) {
-          const v8i av = {(int)fa[j].x, (int)fa[j].y, (int)fa[j].z, (int)fa[j].w, 0, 0, 0, 0};
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wv, av, acc[i][j], 4, 4, ks, (int)sw[i], ks, (int)sa[j]);
-        }
+        const uint32_t cw = *reinterpret_cast<const uint32_t*>(lw + swz(rw0 + 16 * i, 2 * g + ks) + 4 * s4);
+        dw[i] = dq8(cw, e4m3_h2((sw[i] >> sh) & 0xffu));
       }
-    };
-    auto nv_kstep = [&](auto ks_c) {
-      constexpr int ks = decltype(ks_c)::value;
-      // (a loop, not unrolled: keeps the accumulators in place in the AGPRs)
-#pragma unroll 1
-      for (int s4 = 0; s4 < 4; ++s4) {
-        // dword s4 of the fragment: 8 values of NV block 4g + 2ks + s4 / 2
-        const int sh = 8 * (2 * ks + (s4 >> 1));
-        v8h da[kTM], dw[kTN];
 #pragma unroll
-        for (int i = 0; i < kTM; ++i) {
-          const uint32_t ca = *reinterpret_cast<const uint32_t*>(la + swz(ra0 + 16 * i, 2 * g + ks) + 4 * s4);
-          da[i] = dq8(ca, e4m3_h2((sa[i] >> sh) & 0xffu));
-        }
+      for (int i = 0; i < kTN; ++i)
 #pragma unroll
-        for (int i = 0; i < kTN; ++i) {
-          const uint32_t cw = *reinterpret_cast<const uint32_t*>(lw + swz(rw0 + 16 * i, 2 * g + ks) + 4 * s4);
-          dw[i] = dq8(cw, e4m3_h2((sw[i] >> sh) & 0xffu));
-        }
-#pragma unroll
-        for (int i = 0; i < kTN; ++i)
-#pragma unroll
-          for (int j = 0; j < kTM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[i], da[j], acc[i][j], 0, 0, 0);
-      }
-    };
-    // scheduling barriers keep each part's LDS store after the k-step that hides
-    // its loads (the compiler would otherwise hoist the stores, and the wait
-    // for their loads, above the MFMAs)
-    using K0 = std::integral_constant<int, 0>;
-    using K1 = std::integral_constant<int, 1>;
-    if constexpr (MX) {
-      u32x4 fa0[kTM], fw0[kTN], fa1[kTM], fw1[kTN];
-      read_frags(K0{}, fa0, fw0);
-      read_frags(K1{}, fa1, fw1);
-      mx_kstep(K0{}, fa0, fw0);
-      __builtin_amdgcn_sched_barrier(0);
-      store_part<MX, BM>(st, tile_a(nb), sc_a(nb));
-      __builtin_amdgcn_sched_barrier(0);
-      mx_kstep(K1{}, fa1, fw1);
-    } else {
-      nv_kstep(K0{});
-      __builtin_amdgcn_sched_barrier(0);
-      store_part<MX, BM>(st, tile_a(nb), sc_a(nb));
-      __builtin_amdgcn_sched_barrier(0);
-      nv_kstep(K1{});
+        for (int j = 0; j < kTM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[i], da[j], acc[i][j], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    store_part<MX, BN>(st2, tile_w(nb), sc_w(nb));
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+
+  // Every loop body below is branch-free (a branch lets the compiler sink the
+  // MFMAs past the stores and the barrier): stages past the last one are loaded
+  // through the empty range (zeros into a buffer that is never read again).
+  StageScales<MX> ssa, ssw;   // a later stage's scale bytes, from global load to LDS store
+  if constexpr (MX) {
+    // Stage s lives in buffer s & 1.  Loads run two stages ahead: stage kt + 2
+    // is issued right after the barrier of iteration kt, into the buffer stage
+    // kt has finished with, and must land by the next barrier.  The operand
+    // fragments of the first k-step of stage kt + 1 are read during the second
+    // k-step's MFMAs of stage kt, so no MFMA waits for LDS after a barrier.
+    load_scales<MX, SCALE_VEC>(ssa, src_as, nsc, 0);
+    load_scales<MX, SCALE_VEC>(ssw, src_ws, nsc, 0);
+    dma_tile<SCALE_VEC>(src_a, tile_a(0), rowb, K, 0);
+    dma_tile<SCALE_VEC>(src_w, tile_w(0), rowb, K, 0);
+    store_scales<MX>(ssa, sc_a(0));
+    store_scales<MX>(ssw, sc_w(0));
+    const bool two = nk > 1;
+    load_scales<MX, SCALE_VEC>(ssa, two ? src_as : none, nsc, BK);
+    load_scales<MX, SCALE_VEC>(ssw, two ? src_ws : none, nsc, BK);
+    dma_tile<SCALE_VEC>(two ? src_a : none, tile_a(1), rowb, K, BK);
+    dma_tile<SCALE_VEC>(two ? src_w : none, tile_w(1), rowb, K, BK);
+    wait_dma();
     __syncthreads();
+    uint32_t sa0[kScDw], sw0[kScDw], sa1[kScDw], sw1[kScDw];
+    u32x4 fa0[kTM], fw0[kTN], fa1[kTM], fw1[kTN];
+    read_scales(0, sa0, sw0);
+    read_frags(0, K0{}, fa0, fw0);
+    // nothing but LDS reads outstanding on the LDS/scalar counter from here on
+    // (a pending scalar load would turn every LDS wait in the loop into a full drain)
+    wait_lgkm();
+    static_assert(kTM == 8 && kTN == 8 && kBlocksPerWave == 8, "one load slot per W tile row");
+    // One stage: buffer CB holds stage kt (scales sa / sw); the scales of stage
+    // kt + 1 are read into sa_n / sw_n.  Fragment reads are spread over the
+    // MFMA rows in the order the next k-step consumes them (its first row needs
+    // every A fragment and W fragment 0).
+    auto mx_stage = [&](auto cb_c, int kt, const uint32_t (&sa)[kScDw], const uint32_t (&sw)[kScDw],
+                        uint32_t (&sa_n)[kScDw], uint32_t (&sw_n)[kScDw]) {
+      constexpr int cb = decltype(cb_c)::value, nb = cb ^ 1;
+      // k-step 0 of stage kt, reading the fragments of k-step 1
+      mfma_lead();
+      static_for<kTN>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        mx_row(i_c, K0{}, fa0, fw0, sa, sw);
+        if constexpr (i < 4) {
+          fa1[2 * i] = frag(tile_a(cb), ra0 + 32 * i, 2 * g + 1);
+          fa1[2 * i + 1] = frag(tile_a(cb), ra0 + 32 * i + 16, 2 * g + 1);
+        } else {
+          fw1[2 * i - 8] = frag(tile_w(cb), rw0 + 32 * i - 128, 2 * g + 1);
+          fw1[2 * i - 7] = frag(tile_w(cb), rw0 + 32 * i - 112, 2 * g + 1);
+        }
+      });
+      store_scales<MX>(ssa, sc_a(nb));   // stage kt + 1
+      store_scales<MX>(ssw, sc_w(nb));
+      wait_dma();        // stage kt + 1 (issued during the previous stage) has landed
+      __syncthreads();   // stage kt + 1 is in buffer nb; nobody reads buffer cb any more
+      // k-step 1 of stage kt, issuing one block of each operand's stage kt + 2
+      // loads per row and reading the fragments of stage kt + 1, k-step 0
+      const bool more = kt + 2 < nk;
+      const __amdgpu_buffer_rsrc_t la = more ? src_a : none, lw = more ? src_w : none;
+      load_scales<MX, SCALE_VEC>(ssa, more ? src_as : none, nsc, (kt + 2) * BK);
+      load_scales<MX, SCALE_VEC>(ssw, more ? src_ws : none, nsc, (kt + 2) * BK);
+      mfma_lead();
+      static_for<kTN>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        mx_row(i_c, K1{}, fa1, fw1, sa, sw);
+        if constexpr (i == 0) read_scales(nb, sa_n, sw_n);
+        dma_block<SCALE_VEC>(la, tile_a(cb), rowb, K, (kt + 2) * BK, i);
+        dma_block<SCALE_VEC>(lw, tile_w(cb), rowb, K, (kt + 2) * BK, i);
+        if constexpr (i < 4) {
+          fa0[2 * i] = frag(tile_a(nb), ra0 + 32 * i, 2 * g);
+          fa0[2 * i + 1] = frag(tile_a(nb), ra0 + 32 * i + 16, 2 * g);
+        } else {
+          fw0[2 * i - 8] = frag(tile_w(nb), rw0 + 32 * i - 128, 2 * g);
+          fw0[2 * i - 7] = frag(tile_w(nb), rw0 + 32 * i - 112, 2 * g);
+        }
+      });
+      // the accumulators are read after the loop: 24 wait states after the last MFMA
+      mfma_drain();
+    };
+    // Two stages per iteration, so the scale registers alternate without
+    // copies.  With an odd stage count the last iteration's second stage is
+    // one past the end: it was loaded through the empty range (FP4 codes 0,
+    // scale bytes 0) and adds exact zeros.
+    for (int kt = 0; kt < nk; kt += 2) {
+      mx_stage(std::integral_constant<int, 0>{}, kt, sa0, sw0, sa1, sw1);
+      mx_stage(std::integral_constant<int, 1>{}, kt + 1, sa1, sw1, sa0, sw0);
+    }
+  } else {
+    // Stage s lives in buffer s & 1; stage kt + 1 is loaded while stage kt
+    // computes (its fragments are read from LDS throughout the stage).
+    load_scales<MX, SCALE_VEC>(ssa, src_as, nsc, 0);
+    load_scales<MX, SCALE_VEC>(ssw, src_ws, nsc, 0);
+    dma_tile<SCALE_VEC>(src_a, tile_a(0), rowb, K, 0);
+    dma_tile<SCALE_VEC>(src_w, tile_w(0), rowb, K, 0);
+    store_scales<MX>(ssa, sc_a(0));
+    store_scales<MX>(ssw, sc_w(0));
+    wait_dma();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cb = kt & 1, nb = cb ^ 1;
+      const bool more = kt + 1 < nk;
+      load_scales<MX, SCALE_VEC>(ssa, more ? src_as : none, nsc, (kt + 1) * BK);
+      load_scales<MX, SCALE_VEC>(ssw, more ? src_ws : none, nsc, (kt + 1) * BK);
+      dma_tile<SCALE_VEC>(more ? src_a : none, tile_a(nb), rowb, K, (kt + 1) * BK);
+      dma_tile<SCALE_VEC>(more ? src_w : none, tile_w(nb), rowb, K, (kt + 1) * BK);
+      uint32_t sa[kScDw], sw[kScDw];
+      read_scales(cb, sa, sw);
+      nv_kstep(cb, K0{}, sa, sw);
+      nv_kstep(cb, K1{}, sa, sw);
+      __builtin_amdgcn_sched_barrier(0);
+      store_scales<MX>(ssa, sc_a(nb));
+      store_scales<MX>(ssw, sc_w(nb));
+      wait_dma();
+      __syncthreads();
+    }
   }
 
   // epilogue: lane holds D[m][n .. n+3] for each tile pair; D = acc * ((g_a * g_b) * g_d)
@@ -362,6 +507,9 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
     for (int i = 0; i < kTN; ++i) {
       const int n = n0 + wn * 16 * kTN + 16 * i + 4 * g;
+      // (keeps the accumulator in its AGPRs until here: read tile by tile, the
+      // epilogue needs a few VGPRs, not 256)
+      asm volatile("" : "+a"(acc[i][j]));
       const v4f v = acc[i][j] * alpha;
       if (OUT_BF16) {
         uint16_t* row = reinterpret_cast<uint16_t*>(D) + (int64_t)m * N;
