@@ -144,6 +144,26 @@ def test_activation_workload_full_size_sampled_rows():
     assert np.array_equal(bf16_bits(ym)[xf_rows], o.f32_to_bf16_bits(o.mxfp4_dequantize(rqm, rsm, 8192)))
 
 
+@pytest.mark.parametrize("shape", [(2053, 4112), (1031, 8192)])
+def test_nvfp4_quantize_large_matches_oracle(shape):
+    """bf16 tensors of several million values (hundreds of workgroups, a ragged
+    last chunk), computed amax: every byte against the oracle."""
+    announce(f"nvfp4 large {shape}")
+    xg, xf = _input(shape, "bf16", 900 + shape[0])
+    _check_nv(xg, xf)
+
+
+def test_nvfp4_full_activation_computed_amax_equals_given_amax():
+    """8192x8192 activation: quantizing with the computed amax gives the same
+    bytes everywhere as quantizing with that amax given (the oracle pins the
+    given-amax path on sampled rows of this workload)."""
+    announce("nvfp4 computed vs given amax 8192x8192")
+    xg = to_gpu_bf16(workloads.activation())
+    q, s, G, sg = fp4.nvfp4_quantize(xg)
+    qs, ss, _, sgs = fp4.nvfp4_quantize(xg, amax=float(G.cpu()[0]))
+    assert torch.equal(q, qs) and torch.equal(s, ss) and torch.equal(sg, sgs)
+
+
 # ---------------------------------------------------------------- Hadamard --
 HSHAPES = [(1, 128), (3, 256), (64, 1024), (33, 640), (512, 2048)]
 
