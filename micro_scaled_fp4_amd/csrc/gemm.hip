@@ -113,8 +113,18 @@ __device__ __forceinline__ void mfma_fp4(v4f& acc, const u32x4& w, const u32x4& 
       : "+a"(acc)
       : "v"(w), "v"(a), "v"(sw), "v"(sa), "n"(SW & 1), "n"(SA & 1), "n"(SW >> 1), "n"(SA >> 1));
 }
-// 2 wait states before a group of MFMAs (vector-ALU write -> MFMA read)
-__device__ __forceinline__ void mfma_lead() { asm volatile("s_nop 1"); }
+// D += W x A, fp16 operands (8 values per lane each): v_mfma_f32_16x16x32_f16
+// in place in AGPRs, under the same rules as mfma_fp4.
+__device__ __forceinline__ void mfma_f16(v4f& acc, const v8h& w, const v8h& a) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(w), "v"(a));
+}
+// 2 wait states before a group of MFMAs (vector-ALU write -> MFMA read); no
+// instruction is scheduled across it
+__device__ __forceinline__ void mfma_lead() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
+  __builtin_amdgcn_sched_barrier(0);
+}
 // wait states after the last MFMA before its result is read (24 >= what a
 // 4-pass MFMA result needs before a vector-ALU or accvgpr read)
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
@@ -348,34 +358,27 @@ __global__ void __launch_bounds__(kThreads, 1)
       mfma_fp4<2 * (i & 1) + ks, 2 * (j & 1) + ks>(acc[i][j], fw[i], fa[j], sw[i >> 1], sa[j >> 1]);
     });
   };
-  // NVFP4 k-step: per dword of the fragment, dequantize 8 values per tile to
-  // fp16 and run the fp16 MFMAs (the dwords are read from LDS as they are used)
-  auto nv_kstep = [&](int b, auto ks_c, const uint32_t (&sa)[kScDw], const uint32_t (&sw)[kScDw]) {
-    constexpr int ks = decltype(ks_c)::value;
-    const uint8_t* la = tile_a(b);
-    const uint8_t* lw = tile_w(b);
-    // (a loop, not unrolled: keeps the accumulators in place in the AGPRs)
-#pragma unroll 1
-    for (int s4 = 0; s4 < 4; ++s4) {
-      // dword s4 of the fragment: 8 values of NV block 4g + 2ks + s4 / 2
-      const int sh = 8 * (2 * ks + (s4 >> 1));
-      v8h da[kTM], dw[kTN];
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        const uint32_t ca = *reinterpret_cast<const uint32_t*>(la + swz(ra0 + 16 * i, 2 * g + ks) + 4 * s4);
-        da[i] = dq8(ca, e4m3_h2((sa[i] >> sh) & 0xffu));
-      }
-#pragma unroll
-      for (int i = 0; i < kTN; ++i) {
-        const uint32_t cw = *reinterpret_cast<const uint32_t*>(lw + swz(rw0 + 16 * i, 2 * g + ks) + 4 * s4);
-        dw[i] = dq8(cw, e4m3_h2((sw[i] >> sh) & 0xffu));
-      }
-#pragma unroll
-      for (int i = 0; i < kTN; ++i)
-#pragma unroll
-        for (int j = 0; j < kTM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[i], da[j], acc[i][j], 0, 0, 0);
-    }
+  // NVFP4 sub-step u (k-step u / 4, dword u % 4 of the lane's 16-byte chunk):
+  // one dword of codes per tile (8 values of NV block 4g + 2 (u / 4) + (u % 4) / 2),
+  // dequantized to fp16, then 64 fp16 MFMAs.
+  auto raw_dw = [&](const uint8_t* tile, int row, int u) {
+    return *reinterpret_cast<const uint32_t*>(tile + swz(row, 2 * g + (u >> 2)) + 4 * (u & 3));
+  };
+  // f16 pair (h(b0), h(b1)) of the two E4M3 scale bytes of k-step ks in a tile's
+  // scale dword, h(b) = E4M3(b) * 2^-8 exactly (see e4m3_h2)
+  auto scale_pair = [&](uint32_t scale_dw, int ks) {
+    const uint32_t y = (scale_dw >> (16 * ks)) & 0xffffu;
+    return ((y & 0x80u) << 8) | ((y & 0x7fu) << 7) | ((y & 0x8000u) << 16) | ((y & 0x7f00u) << 15);
+  };
+  // values 2k, 2k + 1 (k = part) of the 8 dequantized values of sub-step u: the
+  // E2M1 codes scaled by 2^8, times the scale of block half (u % 4) / 2
+  auto dq_part = [&](v8h& d, uint32_t codes, uint32_t pair, auto part_c, int u) {
+    constexpr int part = decltype(part_c)::value;
+    const v2h t = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, part);
+    const v2h h = __builtin_bit_cast(v2h, pair);
+    const v2h r = t * (((u & 3) >> 1) ? v2h{h.y, h.y} : v2h{h.x, h.x});
+    d[2 * part] = r.x;
+    d[2 * part + 1] = r.y;
   };
   using K0 = std::integral_constant<int, 0>;
   using K1 = std::integral_constant<int, 1>;
@@ -468,32 +471,119 @@ __global__ void __launch_bounds__(kThreads, 1)
       mx_stage(std::integral_constant<int, 1>{}, kt + 1, sa1, sw1, sa0, sw0);
     }
   } else {
-    // Stage s lives in buffer s & 1; stage kt + 1 is loaded while stage kt
-    // computes (its fragments are read from LDS throughout the stage).
+    // Stage s lives in buffer s & 1.  A stage is 8 sub-steps; in sub-step u the
+    // 64 MFMAs run on the fp16 operands of u while the codes of u + 1 are
+    // dequantized and those of u + 2 read from LDS (one tile row of each after
+    // each MFMA row), all double-buffered in registers.  The barrier comes after
+    // sub-step 5, once this stage's last codes have been read: sub-steps 6 and 7
+    // then issue the loads of stage kt + 2 (into this stage's buffer) and read
+    // and dequantize the first codes of stage kt + 1, so no MFMA waits at a
+    // stage boundary.
     load_scales<MX, SCALE_VEC>(ssa, src_as, nsc, 0);
     load_scales<MX, SCALE_VEC>(ssw, src_ws, nsc, 0);
     dma_tile<SCALE_VEC>(src_a, tile_a(0), rowb, K, 0);
     dma_tile<SCALE_VEC>(src_w, tile_w(0), rowb, K, 0);
     store_scales<MX>(ssa, sc_a(0));
     store_scales<MX>(ssw, sc_w(0));
+    const bool two = nk > 1;
+    load_scales<MX, SCALE_VEC>(ssa, two ? src_as : none, nsc, BK);
+    load_scales<MX, SCALE_VEC>(ssw, two ? src_ws : none, nsc, BK);
+    dma_tile<SCALE_VEC>(two ? src_a : none, tile_a(1), rowb, K, BK);
+    dma_tile<SCALE_VEC>(two ? src_w : none, tile_w(1), rowb, K, BK);
     wait_dma();
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cb = kt & 1, nb = cb ^ 1;
-      const bool more = kt + 1 < nk;
-      load_scales<MX, SCALE_VEC>(ssa, more ? src_as : none, nsc, (kt + 1) * BK);
-      load_scales<MX, SCALE_VEC>(ssw, more ? src_ws : none, nsc, (kt + 1) * BK);
-      dma_tile<SCALE_VEC>(more ? src_a : none, tile_a(nb), rowb, K, (kt + 1) * BK);
-      dma_tile<SCALE_VEC>(more ? src_w : none, tile_w(nb), rowb, K, (kt + 1) * BK);
-      uint32_t sa[kScDw], sw[kScDw];
-      read_scales(cb, sa, sw);
-      nv_kstep(cb, K0{}, sa, sw);
-      nv_kstep(cb, K1{}, sa, sw);
-      __builtin_amdgcn_sched_barrier(0);
-      store_scales<MX>(ssa, sc_a(nb));
-      store_scales<MX>(ssw, sc_w(nb));
-      wait_dma();
-      __syncthreads();
+    uint32_t sa0[kScDw], sw0[kScDw], sa1[kScDw], sw1[kScDw];
+    uint32_t ra[2][kTM], rw[2][kTN];   // codes of sub-steps u (parity u & 1)
+    v8h da[2][kTM], dw[2][kTN];        // fp16 operands of sub-steps u (parity u & 1)
+    uint32_t pa[2][kTM], pw[2][kTN];   // scale pairs of k-steps 0 and 1 of a stage
+    read_scales(0, sa0, sw0);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      ra[0][i] = raw_dw(tile_a(0), ra0 + 16 * i, 0);
+      ra[1][i] = raw_dw(tile_a(0), ra0 + 16 * i, 1);
+      rw[0][i] = raw_dw(tile_w(0), rw0 + 16 * i, 0);
+      rw[1][i] = raw_dw(tile_w(0), rw0 + 16 * i, 1);
+    }
+    wait_lgkm();
+    static_for<kTM>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      pa[0][i] = scale_pair(sa0[i], 0);
+      pw[0][i] = scale_pair(sw0[i], 0);
+      static_for<4>([&](auto k_c) {
+        dq_part(da[0][i], ra[0][i], pa[0][i], k_c, 0);
+        dq_part(dw[0][i], rw[0][i], pw[0][i], k_c, 0);
+      });
+    });
+    // Each MFMA is issued with its share of the other work in a slot of its
+    // own (no instruction crosses a slot), so the vector ALU work runs while
+    // the MFMA pipe is busy: per MFMA row i, slot j dequantizes dword j % 4 of
+    // the next sub-step's A (j < 4) or W (j >= 4) tile i; slots 0 and 4 read
+    // the codes two sub-steps ahead; sub-step 2 forms the scale pairs of
+    // k-step 1, sub-step 6 those of the next stage's k-step 0 (rows 4-7) and
+    // issues one block of each operand's loads per row.
+    auto nv_stage = [&](auto cb_c, int kt, const uint32_t (&sa)[kScDw], const uint32_t (&sw)[kScDw],
+                        uint32_t (&sa_n)[kScDw], uint32_t (&sw_n)[kScDw]) {
+      constexpr int cb = decltype(cb_c)::value, nb = cb ^ 1;
+      const bool more = kt + 2 < nk;
+      const __amdgpu_buffer_rsrc_t la = more ? src_a : none, lw = more ? src_w : none;
+      static_for<8>([&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        constexpr int p = u & 1, q = p ^ 1;
+        constexpr int un = (u + 1) & 7;          // sub-step dequantized here (next stage's 0 after 7)
+        constexpr int kn = un >> 2;              // its k-step
+        if constexpr (u == 6) {
+          // every wave has read this stage's last codes (sub-step 7, read in 5)
+          store_scales<MX>(ssa, sc_a(nb));   // stage kt + 1
+          store_scales<MX>(ssw, sc_w(nb));
+          wait_dma();        // stage kt + 1 (issued during the previous stage) has landed
+          __syncthreads();   // stage kt + 1 is in buffer nb; buffer cb is free
+          load_scales<MX, SCALE_VEC>(ssa, more ? src_as : none, nsc, (kt + 2) * BK);
+          load_scales<MX, SCALE_VEC>(ssw, more ? src_ws : none, nsc, (kt + 2) * BK);
+          read_scales(nb, sa_n, sw_n);
+        }
+        mfma_lead();
+        static_for<kTN>([&](auto i_c) {
+          constexpr int i = decltype(i_c)::value;
+          static_for<kTM>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            mfma_f16(acc[i][j], dw[p][i], da[p][j]);
+            if constexpr (j < 4)
+              dq_part(da[q][i], ra[q][i], pa[kn][i], std::integral_constant<int, j>{}, un);
+            else
+              dq_part(dw[q][i], rw[q][i], pw[kn][i], std::integral_constant<int, j - 4>{}, un);
+            if constexpr (j == 0) {   // codes of sub-step u + 2 (the next stage's 0, 1 after the barrier)
+              if constexpr (u + 2 < 8) ra[p][i] = raw_dw(tile_a(cb), ra0 + 16 * i, u + 2);
+              else ra[p][i] = raw_dw(tile_a(nb), ra0 + 16 * i, u - 6);
+            }
+            if constexpr (j == 4) {
+              if constexpr (u + 2 < 8) rw[p][i] = raw_dw(tile_w(cb), rw0 + 16 * i, u + 2);
+              else rw[p][i] = raw_dw(tile_w(nb), rw0 + 16 * i, u - 6);
+            }
+            if constexpr (u == 2 && j == 1) pa[1][i] = scale_pair(sa[i], 1);
+            if constexpr (u == 2 && j == 5) pw[1][i] = scale_pair(sw[i], 1);
+            if constexpr (u == 6 && i >= 4 && j == 1) {
+              pa[0][2 * i - 8] = scale_pair(sa_n[2 * i - 8], 0);
+              pa[0][2 * i - 7] = scale_pair(sa_n[2 * i - 7], 0);
+            }
+            if constexpr (u == 6 && i >= 4 && j == 5) {
+              pw[0][2 * i - 8] = scale_pair(sw_n[2 * i - 8], 0);
+              pw[0][2 * i - 7] = scale_pair(sw_n[2 * i - 7], 0);
+            }
+            if constexpr (u == 6 && j == 2) dma_block<SCALE_VEC>(la, tile_a(cb), rowb, K, (kt + 2) * BK, i);
+            if constexpr (u == 6 && j == 6) dma_block<SCALE_VEC>(lw, tile_w(cb), rowb, K, (kt + 2) * BK, i);
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        });
+      });
+      // the accumulators are read after the loop: 24 wait states after the last MFMA
+      mfma_drain();
+    };
+    // two stages per iteration (scale registers alternate); an odd stage count
+    // runs one stage past the end, loaded through the empty range (codes 0,
+    // scale bytes 0: exact zeros)
+    for (int kt = 0; kt < nk; kt += 2) {
+      nv_stage(std::integral_constant<int, 0>{}, kt, sa0, sw0, sa1, sw1);
+      nv_stage(std::integral_constant<int, 1>{}, kt + 1, sa1, sw1, sa0, sw0);
     }
   }
 
