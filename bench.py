@@ -18,8 +18,11 @@ launch overhead is timed.  HIP events on the capture/replay stream bracket
 every replay.
 
 The printed JSON line's `value` is the NVFP4 quantize throughput (dynamic
-amax) on the activation workload in GB/s of algorithmic bytes (input read
-once + codes + scales); every other call is reported under `components`.
+amax) on the activation workload in GB/s of algorithmic bytes; every other
+call is reported under `components`.  Algorithmic bytes: the input once, codes
+and scale bytes, and the two scalars, plus, for a computed amax (dynamic
+quantize and rotate), the input a second time: the global scale has to be
+known before any block is encoded, so the method reads the input twice.
 """
 from __future__ import annotations
 
@@ -149,6 +152,7 @@ def main():
     y_bf = torch.empty((R_A, C_A), dtype=torch.bfloat16, device=dev)
     elems = R_A * C_A
     b_nv = elems * 2 + elems // 2 + elems // 16 + 8
+    b_nv_dyn = b_nv + elems * 2          # + the amax pass's read of x
     b_mx = elems * 2 + elems // 2 + elems // 32
 
     def nv_dyn(i):
@@ -177,7 +181,7 @@ def main():
 
     qsrc = _src_hash("quantize.hip", "fp4_device.h")
     ops += [
-        Op("nvfp4_quantize_dynamic", nv_dyn, nA, "GB/s", b_nv, HBM_PEAK_GBS, "hbm",
+        Op("nvfp4_quantize_dynamic", nv_dyn, nA, "GB/s", b_nv_dyn, HBM_PEAK_GBS, "hbm",
            "k_amax + k_nv_quant_fast", qsrc),
         Op("nvfp4_quantize_static", nv_static, nA, "GB/s", b_nv, HBM_PEAK_GBS, "hbm",
            "k_nv_quant_fast", qsrc),
@@ -256,7 +260,7 @@ def main():
     gh = torch.empty(1, dtype=torch.float32, device=dev)
     wh = torch.empty(fp4.AMAX_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     eh = R_H * C_H
-    b_h = eh * 2 + eh // 2 + eh // 16 + 8
+    b_h = eh * 2 + eh // 2 + eh // 16 + 8 + eh * 2   # computed amax: x is read twice
     hsrc = _src_hash("hadamard.hip", "fp4_device.h")
     for mode, nm in ((fp4.FP4_RNE, "rne"), (fp4.FP4_SR, "sr")):
         def had(i, mode=mode):
@@ -356,7 +360,8 @@ def main():
             "workload": "activation quantization: bf16 8192x8192, N(0,1), 8 outlier channels x40, "
                         "nvfp4_quantize with dynamic (computed) amax",
             "rows": R_A, "cols": C_A,
-            "value_bytes_per_call": b_nv,
+            "value_bytes_per_call": b_nv_dyn,
+            "value_bytes_note": "x read twice (amax pass, encode pass) + codes + scale bytes + 2 floats",
             "step_also_runs": "mxfp4_quantize, NV/MX dequantize (8192x8192); GEMV W 27648x5120 "
                               "B=1,4,16; GEMM 8192x28672x8192 NVFP4 and MXFP4; FWHT+NVFP4 "
                               "16384x8192 RNE and SR",
