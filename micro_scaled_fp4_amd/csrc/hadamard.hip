@@ -268,8 +268,9 @@ __global__ void __launch_bounds__(kThreads)
         }
       }
     }
-    reinterpret_cast<u32x4*>(q)[s] = u32x4{w[0], w[1], w[2], w[3]};
-    reinterpret_cast<uint16_t*>(scales)[s] = (uint16_t)(sc[0] | (sc[1] << 8));
+    // (non-temporal stores: written once, read by another kernel)
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(q) + s);
+    __builtin_nontemporal_store((uint16_t)(sc[0] | (sc[1] << 8)), reinterpret_cast<uint16_t*>(scales) + s);
   }
 }
 
