@@ -138,6 +138,18 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return E4M3_VALUES[np.asarray(codes, dtype=np.int64)]
 
 
+def e4m3_encode_signed(x: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 byte of each float32 x (the GEMM's E4M3 output): sign bit of x,
+    then the nearest finite magnitude, ties to the even code, saturating at 448
+    ([MS] section 五: the scaled-mm example writes its output as
+    torch.float8_e4m3fn after g_d; the kernel sketch there notes that the
+    output is often stored as FP8).  Saturation, not NaN, above 448 is a
+    reading: E4M3 "fn" has no infinity and the block-scale codec saturates."""
+    x = np.asarray(x, dtype=F32)
+    sign = (np.signbit(x).astype(np.uint8) << 7).astype(np.uint8)
+    return (sign | e4m3_encode_rne_sat(np.abs(x))).astype(np.uint8)
+
+
 # ------------------------------------------------------------------ E8M0 ----
 # MXFP4 block scale: one power of two per 32 values ([DT] "mxFP4的技术局限";
 # [NV] Table 1).  [LPF] "FP4 / MXFP4 / NVFP4": the ideal scale is A/6 and the
@@ -450,6 +462,12 @@ def scaled_gemm_ref(A_hat: np.ndarray, W_hat: np.ndarray, g_d: float):
 
 GEMM_REL_TOL = 1e-5            # |D - D_ref| <= 1e-5 * |g_d| * sum |a*b|
 BF16_UNIT_ROUNDOFF = 2.0 ** -8
+
+
+def gemm_e4m3_output(D_f32: np.ndarray) -> np.ndarray:
+    """The GEMM's E4M3 output from its float32 result D = fl(acc * alpha): one
+    E4M3 byte per element (e4m3_encode_signed)."""
+    return e4m3_encode_signed(np.asarray(D_f32, dtype=F32))
 
 
 def gemm_within_tolerance(D, D_ref, mag, out_bf16: bool = False):

@@ -108,6 +108,22 @@ def test_e4m3_encode_matches_torch_cast_up_to_448():
     assert np.array_equal(o.e4m3_encode_rne_sat(t), ref)
 
 
+def test_e4m3_signed_encode_for_gemm_output():
+    """The GEMM's E4M3 output byte: sign of x | E4M3 of |x|.  Negative values,
+    -0, the page's 0.9 -> 0.875 example with its sign, saturation on both
+    sides, and torch's float8_e4m3fn cast on signed values inside +-448."""
+    x = np.array([0.9, -0.9, 448.0, -448.0, 1e6, -1e6, 0.0, -0.0, 2.0 ** -10, -3 * 2.0 ** -10],
+                 dtype=F32)
+    got = o.e4m3_encode_signed(x)
+    assert got.tolist() == [0x36, 0xB6, 0x7E, 0xFE, 0x7E, 0xFE, 0x00, 0x80, 0x00, 0x82]
+    rng = np.random.default_rng(4)
+    mag = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 200000))
+    t = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(F32)
+    ref = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.e4m3_encode_signed(t), ref)
+    assert np.array_equal(o.gemm_e4m3_output(t), ref)
+
+
 def test_e4m3_relative_error_and_neighbour_ratio():
     # [LPF] section FP8: relative error of E4M3 rounding <= 2^-(M+1) = 6.25% (normal range)
     rng = np.random.default_rng(3)
