@@ -9,7 +9,8 @@ workload's shape:
                nvfp4_quantize (dynamic amax), nvfp4_quantize (static amax),
                mxfp4_quantize, NVFP4 and MXFP4 dequantize to bf16
   decode GEMV  W 27648x5120 NVFP4, x bf16 [B, 5120] quantized on the fly, B = 1, 4, 16
-  prefill GEMM 8192 x 28672 x 8192, NVFP4 and MXFP4 operands, bf16 output
+  prefill GEMM 8192 x 28672 x 8192, NVFP4 and MXFP4 operands, bf16 output;
+               NVFP4 again with the output requantized to FP8 E4M3 in the epilogue
   rotate       16384x8192 bf16, 16 outlier channels x60: FWHT-128 + NVFP4, RNE and SR
 Each call kind is captured in its own HIP graph of R back-to-back calls that
 cycle through input copies totalling >= 1 GiB (more than the 256 MiB Infinity
@@ -237,6 +238,13 @@ def main():
                                  P(gw_nv), 1.0, Mg, Ng, Kg, P(Dg), fp4.FP4_BF16, stream_of())
         assert st == 0, st
 
+    D8 = torch.empty((Mg, Ng), dtype=torch.float8_e4m3fn, device=dev)
+
+    def gemm_nv_e4m3(i):
+        st = lib.fp4_scaled_gemm(fp4.FP4_NVFP4, P(aq_nv), P(as_nv), P(ga_nv), P(wq_nv), P(wsc_nv),
+                                 P(gw_nv), 1.0, Mg, Ng, Kg, P(D8), fp4.FP4_E4M3, stream_of())
+        assert st == 0, st
+
     def gemm_mx(i):
         st = lib.fp4_scaled_gemm(fp4.FP4_MXFP4, P(aq_mx), P(as_mx), None, P(wq_mx), P(wsc_mx), None,
                                  1.0, Mg, Ng, Kg, P(Dg), fp4.FP4_BF16, stream_of())
@@ -247,6 +255,8 @@ def main():
            "k_gemm<NV> (fp16 MFMA after exact in-register dequant)", msrc),
         Op("gemm_mxfp4", gemm_mx, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp4"], "mfma",
            "k_gemm<MX> (scaled FP4 MFMA)", msrc),
+        Op("gemm_nvfp4_e4m3_out", gemm_nv_e4m3, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp16"], "mfma",
+           "k_gemm<NV, E4M3 out> (output requantized to FP8 E4M3 in the epilogue)", msrc),
     ]
 
     # -------------------------------------------------------------- rotate --
@@ -338,7 +348,7 @@ def main():
             ("bytes_per_call" if op.unit == "GB/s" else "flop_per_call"): op.per_call,
             "kernels": op.kernel, "calls_per_replay": op.n, "traffic": tr_bytes,
         }
-        if op.name == "gemm_nvfp4":
+        if op.name in ("gemm_nvfp4", "gemm_nvfp4_e4m3_out"):
             comps[op.name]["frac_of_fp4_peak"] = round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4)
 
     head = comps.get("nvfp4_quantize_dynamic") or next(iter(comps.values()))
@@ -363,7 +373,8 @@ def main():
             "value_bytes_per_call": b_nv_dyn,
             "value_bytes_note": "x read twice (amax pass, encode pass) + codes + scale bytes + 2 floats",
             "step_also_runs": "mxfp4_quantize, NV/MX dequantize (8192x8192); GEMV W 27648x5120 "
-                              "B=1,4,16; GEMM 8192x28672x8192 NVFP4 and MXFP4; FWHT+NVFP4 "
+                              "B=1,4,16; GEMM 8192x28672x8192 NVFP4 and MXFP4 (bf16 out), NVFP4 "
+                              "(E4M3 out); FWHT+NVFP4 "
                               "16384x8192 RNE and SR",
         },
         "roofline": {

@@ -49,7 +49,8 @@ typedef enum {
   FP4_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed        */
 } fp4_status;
 
-typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
+/* FP4_E4M3 (one FP8 E4M3 byte per value) is valid only as fp4_scaled_gemm's output. */
+typedef enum { FP4_F32 = 0, FP4_BF16 = 1, FP4_E4M3 = 2 } fp4_dtype;
 typedef enum { FP4_NVFP4 = 0, FP4_MXFP4 = 1 } fp4_format;
 typedef enum { FP4_RNE = 0, FP4_SR = 1 } fp4_rounding;
 
@@ -122,7 +123,11 @@ fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* q, const uint8_t* scale
  *   g_a, g_b  device floats: NVFP4 -> the global_scale written by nvfp4_quantize;
  *             MXFP4 -> must be NULL (tensor scale 1).
  *   g_d       host float output multiplier.
- *   D         out [M, N], float32 or bf16 (nearest-even from the float32 result).
+ *   D         out [M, N], float32, bf16 (nearest-even from the float32 result) or
+ *             FP8 E4M3 bytes (FP4_E4M3): the sign of the float32 result, then its
+ *             magnitude to the nearest E4M3 value, ties to the even code, saturating
+ *             at 448 (section 五's scaled-mm example writes its output as
+ *             float8_e4m3fn after g_d, fusing the next layer's input cast).
  * Each block product s_a * s_w * sum_k v_a v_w is exact; blocks are summed in
  * float32; |D - D_ref| <= 1e-5 * |g_d| * sum_k |A_hat_mk W_hat_nk| (+ one bf16
  * rounding for bf16 output).  K must be a multiple of bs (FP4_ERR_SHAPE);

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("FP4_LIBRARY") or os.path.join(_PKG, "libfp4.so")
 
 # enums of include/fp4.h
 FP4_OK = 0
-FP4_F32, FP4_BF16 = 0, 1
+FP4_F32, FP4_BF16, FP4_E4M3 = 0, 1, 2
 FP4_NVFP4, FP4_MXFP4 = 0, 1
 FP4_RNE, FP4_SR = 0, 1
 AMAX_WORKSPACE_BYTES = 4096
@@ -98,6 +98,8 @@ def _dtype_code(dt: torch.dtype) -> int:
         return FP4_BF16
     if dt == torch.float32:
         return FP4_F32
+    if dt == torch.float8_e4m3fn:   # accepted by the library as a GEMM output only
+        return FP4_E4M3
     raise TypeError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
 
 
@@ -174,7 +176,10 @@ def fp4_dequantize(fmt: int, q: torch.Tensor, scales: torch.Tensor, global_scale
 def fp4_scaled_gemm(fmt: int, A: torch.Tensor, a_scales: torch.Tensor, g_a, W: torch.Tensor,
                     w_scales: torch.Tensor, g_b, K: int, g_d: float = 1.0,
                     out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
-    """D [M, N] = g_d * ((g_a s_a . A) @ (g_b s_b . W)^T); A [M, K/2], W [N, K/2] packed."""
+    """D [M, N] = g_d * ((g_a s_a . A) @ (g_b s_b . W)^T); A [M, K/2], W [N, K/2] packed.
+
+    out_dtype float32, bfloat16 or float8_e4m3fn (E4M3 of the float32 result,
+    nearest with ties to even, saturating at 448)."""
     A = _gpu_2d(A, "A")
     W = _gpu_2d(W, "W")
     a_scales = _gpu_2d(a_scales, "a_scales")

@@ -155,28 +155,28 @@ fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_sc
                            const float* g_b, float g_d, int64_t M, int64_t N, int64_t K, void* D,
                            fp4_dtype dt, hipStream_t stream) {
   if (fmt != FP4_NVFP4 && fmt != FP4_MXFP4) return FP4_ERR_DTYPE;
-  if (!valid_dtype(dt)) return FP4_ERR_DTYPE;
+  if (!valid_dtype(dt) && dt != FP4_E4M3) return FP4_ERR_DTYPE;
+  const int d_bytes = dt == FP4_F32 ? 4 : dt == FP4_BF16 ? 2 : 1;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_SHAPE;
   if (K % 32 != 0) return FP4_ERR_SHAPE;
   if (fmt == FP4_MXFP4 && (g_a != nullptr || g_b != nullptr)) return FP4_ERR_DTYPE;
   if (M == 0 || N == 0) return FP4_OK;
   if (K == 0) {   // empty contraction: D = 0, operands are not read
     if (D == nullptr) return FP4_ERR_NULL;
-    if (!aligned(D, dt == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+    if (!aligned(D, d_bytes)) return FP4_ERR_ALIGN;
     fp4_status st = check_arch();
     if (st != FP4_OK) return st;
-    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(D, M * N, dt == FP4_BF16, stream), "fp4_scaled_gemm");
+    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(D, M * N, d_bytes, stream), "fp4_scaled_gemm");
     return FP4_OK;
   }
   if (A == nullptr || a_scales == nullptr || W == nullptr || w_scales == nullptr || D == nullptr)
     return FP4_ERR_NULL;
   if (fmt == FP4_NVFP4 && (g_a == nullptr || g_b == nullptr)) return FP4_ERR_NULL;
-  if (!aligned(A, 16) || !aligned(W, 16) || !aligned(D, dt == FP4_BF16 ? 2 : 4))
-    return FP4_ERR_ALIGN;
+  if (!aligned(A, 16) || !aligned(W, 16) || !aligned(D, d_bytes)) return FP4_ERR_ALIGN;
   fp4_status st = check_arch();
   if (st != FP4_OK) return st;
   FP4_TRY_LAUNCH(fp4impl::launch_gemm(fmt == FP4_MXFP4, A, a_scales, g_a, W, w_scales, g_b, g_d, M,
-                                      N, K, D, dt == FP4_BF16, stream),
+                                      N, K, D, d_bytes, stream),
                  "fp4_scaled_gemm");
   return FP4_OK;
 }
@@ -198,7 +198,7 @@ fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_
     if (!aligned(y, yt == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
     fp4_status st = check_arch();
     if (st != FP4_OK) return st;
-    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(y, B * N, yt == FP4_BF16, stream), "fp4_gemv_batched");
+    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(y, B * N, yt == FP4_BF16 ? 2 : 4, stream), "fp4_gemv_batched");
     return FP4_OK;
   }
   if (x == nullptr || W == nullptr || w_scales == nullptr || g_w == nullptr || y == nullptr)

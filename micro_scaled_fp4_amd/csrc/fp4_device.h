@@ -27,6 +27,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two float32 values -> two bf16 in one dword (a in the low half), round to
+// nearest even: one v_cvt_pk_bf16_f32 on gfx950 (finite inputs give the bits
+// of f32_to_bf16).
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
+}
+
 // ---------------------------------------------------------------- E2M1 --
 // Code of the nearest E2M1 magnitude (ties to the even code), saturating at 6,
 // with the sign bit of q.  The thresholds are the midpoints of
@@ -82,6 +91,20 @@ __device__ __forceinline__ uint32_t e4m3_code(float t) {
   u = u + 0x7ffffu + ((u >> 20) & 1u);      // round the mantissa to 3 bits
   uint32_t c = (u >> 20) - (120u << 3);     // exponent bias 127 -> 7
   return c > 0x7eu ? 0x7eu : c;
+}
+
+// Four float32 values -> four signed E4M3 bytes (value q in byte q): sign,
+// then the nearest magnitude with ties to the even code, subnormals kept,
+// saturating at 448.  gfx950's v_cvt_pk_fp8_f32 rounds to nearest even into
+// OCP E4M3 but turns magnitudes that round past 448 into NaN (0x7F), so the
+// values are clamped to [-448, 448] first (v_med3_f32).
+__device__ __forceinline__ uint32_t e4m3_pack4_signed(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {

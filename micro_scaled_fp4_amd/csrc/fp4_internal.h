@@ -41,8 +41,9 @@ hipError_t launch_hadamard_quant(const void* x, bool bf16, int64_t rows, int64_t
                                  float* scale_out, hipStream_t stream);
 
 // ---- gemv.hip -------------------------------------------------------------
-// Writes n zeros (float or bf16) to y: the result of a contraction over K = 0.
-hipError_t launch_zero_fill(void* y, int64_t n, bool y_bf16, hipStream_t stream);
+// Writes n zeros of elem_bytes (4: float, 2: bf16, 1: E4M3) each to y: the result
+// of a contraction over K = 0.
+hipError_t launch_zero_fill(void* y, int64_t n, int elem_bytes, hipStream_t stream);
 size_t gemv_workspace_bytes(int64_t B, int64_t K);
 hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
                        const uint8_t* w_scales, const float* g_w, int64_t N, int64_t K, float g_d,
@@ -51,6 +52,6 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
 // ---- gemm.hip -------------------------------------------------------------
 hipError_t launch_gemm(bool mx, const uint8_t* A, const uint8_t* a_scales, const float* g_a,
                        const uint8_t* W, const uint8_t* w_scales, const float* g_b, float g_d,
-                       int64_t M, int64_t N, int64_t K, void* D, bool d_bf16, hipStream_t stream);
+                       int64_t M, int64_t N, int64_t K, void* D, int d_bytes, hipStream_t stream);
 
 }  // namespace fp4impl

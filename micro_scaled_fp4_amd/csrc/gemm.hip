@@ -33,7 +33,10 @@
 // does not depend on the K order), so a lane's scale bytes for the stage are
 // contiguous: 2 bytes (MXFP4, byte ks selected by the MFMA) or 4 (NVFP4).
 // The MFMA's first operand is the W fragment, so each lane ends with 4
-// consecutive columns of one output row (one 8- or 16-byte store).
+// consecutive columns of one output row (one 4-, 8- or 16-byte store for an
+// E4M3, bf16 or float32 output).  The E4M3 output (section 五's scaled-mm
+// example writes float8_e4m3fn) is the float32 result's sign bit followed by
+// the nearest E4M3 magnitude, ties to the even code, saturating at 448.
 // Workgroup -> tile map: workgroups are dealt round-robin to the 8 XCDs, so
 // each XCD is given a contiguous range of tiles; tiles are visited in groups
 // of 8 row-tiles so concurrently running workgroups of an XCD share operand
@@ -272,7 +275,7 @@ __device__ __forceinline__ v8h dq8(uint32_t codes, v2h s) {
 }
 
 // ------------------------------------------------------------------ kernel --
-template <bool MX, bool OUT_BF16, bool SCALE_VEC>
+template <bool MX, int OUT, bool SCALE_VEC>
 __global__ void __launch_bounds__(kThreads, 1)
     k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ as,
            const uint8_t* __restrict__ W, const uint8_t* __restrict__ ws,
@@ -601,15 +604,25 @@ __global__ void __launch_bounds__(kThreads, 1)
       // epilogue needs a few VGPRs, not 256)
       asm volatile("" : "+a"(acc[i][j]));
       const v4f v = acc[i][j] * alpha;
-      if (OUT_BF16) {
+      if (OUT == 2) {
         uint16_t* row = reinterpret_cast<uint16_t*>(D) + (int64_t)m * N;
+        const u32x2 h = u32x2{bf16_pack2(v.x, v.y), bf16_pack2(v.z, v.w)};
         if (vec_out && n + 3 < N) {
-          *reinterpret_cast<u32x2*>(row + n) =
-              u32x2{f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16)};
+          *reinterpret_cast<u32x2*>(row + n) = h;
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (n + q < N) row[n + q] = (uint16_t)f32_to_bf16(v[q]);
+            if (n + q < N) row[n + q] = (uint16_t)(h[q >> 1] >> (16 * (q & 1)));
+        }
+      } else if (OUT == 1) {
+        uint8_t* row = reinterpret_cast<uint8_t*>(D) + (int64_t)m * N;
+        const uint32_t c = e4m3_pack4_signed(v.x, v.y, v.z, v.w);
+        if (vec_out && n + 3 < N) {
+          *reinterpret_cast<uint32_t*>(row + n) = c;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) row[n + q] = (uint8_t)(c >> (8 * q));
         }
       } else {
         float* row = reinterpret_cast<float*>(D) + (int64_t)m * N;
@@ -625,7 +638,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
 }
 
-template <bool MX, bool OUT_BF16, bool SCALE_VEC>
+template <bool MX, int OUT, bool SCALE_VEC>
 hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
                     const float* g_a, const float* g_b, float g_d, int M, int N, int K, void* D,
                     hipStream_t stream) {
@@ -633,26 +646,39 @@ hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const
   constexpr int lds = Cfg<MX>::kLdsBytes;
   static bool attr_set = false;   // per process; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MX, OUT_BF16, SCALE_VEC>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MX, OUT, SCALE_VEC>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   // 4 outputs per store when every row start is aligned to 4 outputs
-  const bool vec_out = N % 4 == 0 && reinterpret_cast<uintptr_t>(D) % (OUT_BF16 ? 8 : 16) == 0;
-  hipLaunchKernelGGL((k_gemm<MX, OUT_BF16, SCALE_VEC>), dim3(tiles_m * tiles_n), dim3(kThreads), lds,
+  const bool vec_out = N % 4 == 0 && reinterpret_cast<uintptr_t>(D) % (4 * OUT) == 0;
+  hipLaunchKernelGGL((k_gemm<MX, OUT, SCALE_VEC>), dim3(tiles_m * tiles_n), dim3(kThreads), lds,
                      stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, D, tiles_m, tiles_n, vec_out);
   return hipGetLastError();
 }
 
-template <bool MX, bool OUT_BF16>
+template <bool MX, int OUT>
 hipError_t launch_s(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
                     const float* g_a, const float* g_b, float g_d, int M, int N, int K, void* D,
                     hipStream_t stream) {
   const bool vec = K % BK == 0 && (reinterpret_cast<uintptr_t>(as) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
-  return vec ? launch_t<MX, OUT_BF16, true>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream)
-             : launch_t<MX, OUT_BF16, false>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
+  return vec ? launch_t<MX, OUT, true>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream)
+             : launch_t<MX, OUT, false>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
+}
+
+// d_bytes: 4 float32, 2 bf16, 1 E4M3
+template <bool MX>
+hipError_t launch_o(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
+                    const float* g_a, const float* g_b, float g_d, int M, int N, int K, void* D,
+                    int d_bytes, hipStream_t stream) {
+  switch (d_bytes) {
+    case 4: return launch_s<MX, 4>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
+    case 2: return launch_s<MX, 2>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
+    case 1: return launch_s<MX, 1>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -661,19 +687,13 @@ namespace fp4impl {
 
 hipError_t launch_gemm(bool mx, const uint8_t* A, const uint8_t* a_scales, const float* g_a,
                        const uint8_t* W, const uint8_t* w_scales, const float* g_b, float g_d,
-                       int64_t M, int64_t N, int64_t K, void* D, bool d_bf16, hipStream_t stream) {
+                       int64_t M, int64_t N, int64_t K, void* D, int d_bytes, hipStream_t stream) {
   // buffer ranges cover one 256-row tile of an operand: 256 * K / 2 < 2^31
   if (M > (1 << 30) || N > (1 << 30) || K >= (1 << 23)) return hipErrorInvalidValue;
-  if (mx) {
-    return d_bf16 ? launch_s<true, true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
-                                         (int)K, D, stream)
-                  : launch_s<true, false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
-                                          (int)K, D, stream);
-  }
-  return d_bf16 ? launch_s<false, true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
-                                        (int)K, D, stream)
-                : launch_s<false, false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
-                                         (int)K, D, stream);
+  return mx ? launch_o<true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N, (int)K, D,
+                             d_bytes, stream)
+            : launch_o<false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N, (int)K, D,
+                              d_bytes, stream);
 }
 
 }  // namespace fp4impl

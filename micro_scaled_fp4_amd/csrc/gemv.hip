@@ -651,14 +651,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
 }
 
 // K = 0: every output is an empty sum.
-template <bool YBF16>
-__global__ void __launch_bounds__(256) k_zero_fill(int64_t n, void* __restrict__ y) {
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    if (YBF16)
-      reinterpret_cast<uint16_t*>(y)[i] = 0;
-    else
-      reinterpret_cast<float*>(y)[i] = 0.0f;
-  }
+template <typename T>
+__global__ void __launch_bounds__(256) k_zero_fill(int64_t n, T* __restrict__ y) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) y[i] = 0;
 }
 
 int g_num_cus = 0;
@@ -689,14 +684,18 @@ hipError_t launch_stream(const StreamArgs& a, int grid, int lds, hipStream_t str
 
 namespace fp4impl {
 
-hipError_t launch_zero_fill(void* y, int64_t n, bool y_bf16, hipStream_t stream) {
+hipError_t launch_zero_fill(void* y, int64_t n, int elem_bytes, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int64_t nb = (n + 255) / 256;
   const dim3 g0((unsigned)(nb < 4096 ? nb : 4096));
-  if (y_bf16)
-    hipLaunchKernelGGL(k_zero_fill<true>, g0, dim3(256), 0, stream, n, y);
+  if (elem_bytes == 4)
+    hipLaunchKernelGGL(k_zero_fill<uint32_t>, g0, dim3(256), 0, stream, n, static_cast<uint32_t*>(y));
+  else if (elem_bytes == 2)
+    hipLaunchKernelGGL(k_zero_fill<uint16_t>, g0, dim3(256), 0, stream, n, static_cast<uint16_t*>(y));
+  else if (elem_bytes == 1)
+    hipLaunchKernelGGL(k_zero_fill<uint8_t>, g0, dim3(256), 0, stream, n, static_cast<uint8_t*>(y));
   else
-    hipLaunchKernelGGL(k_zero_fill<false>, g0, dim3(256), 0, stream, n, y);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -716,7 +715,7 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
     else
       g_num_cus = 256;
   }
-  if (K == 0) return launch_zero_fill(y, B * N, y_bf16, stream);
+  if (K == 0) return launch_zero_fill(y, B * N, y_bf16 ? 2 : 4, stream);
   const int nstrips = (int)((N + 15) / 16);
   // fused streaming kernel when the quantized x fits in LDS
   const int64_t Kq = (K + 255) / 256 * 256;

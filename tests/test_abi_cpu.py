@@ -92,3 +92,22 @@ def test_dequant_gemm_gemv_hadamard_argument_errors():
     assert h(P, 1, 4, 256, 64, 0, 0, P, P, P, 0, P, P, 4096, None) == SHAPE
     assert h(P, 1, 4, 200, 128, 0, 0, P, P, P, 0, P, P, 4096, None) == SHAPE
     assert h(P, 1, 4, 256, 128, 5, 0, P, P, P, 0, P, P, 4096, None) == DTYPE
+
+
+def test_e4m3_dtype_is_a_gemm_output_only():
+    """FP4_E4M3 (2) passes the GEMM's dtype check (the next check decides) and is
+    rejected as input or output dtype by every other call."""
+    lib = m.load_library()
+    E4M3 = 2
+    g = lib.fp4_scaled_gemm
+    assert g(0, ctypes.c_void_p(4104), P, P, P, P, P, 1.0, 8, 8, 64, P, E4M3, None) == ALIGN
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 48, P, E4M3, None) == SHAPE
+    assert g(0, None, None, None, None, None, None, 1.0, 8, 8, 0, None, E4M3, None) == NULL
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, 3, None) == DTYPE
+    assert lib.fp4_dequantize(0, P, P, P, 4, 16, P, E4M3, None) == DTYPE
+    assert lib.nvfp4_quantize(P, E4M3, 4, 16, P, P, P, 0, P, P, 4096, None) == DTYPE
+    assert lib.mxfp4_quantize(P, E4M3, 4, 32, P, P, None) == DTYPE
+    need = lib.fp4_gemv_workspace_bytes(4, 512)
+    assert lib.fp4_gemv_batched(P, 1, 4, P, P, P, 8, 512, 1.0, P, E4M3, P, need, None) == DTYPE
+    assert lib.fp4_gemv_batched(P, E4M3, 4, P, P, P, 8, 512, 1.0, P, 1, P, need, None) == DTYPE
+    assert lib.hadamard_quantize(P, E4M3, 4, 256, 128, 0, 0, P, P, P, 0, P, P, 4096, None) == DTYPE

@@ -5,6 +5,12 @@ output, plus one bf16 rounding of D_ref for bf16 output.  Small shapes span
 several 256x256 tiles with ragged M/N edges and K tails; the prefill shape
 (8192 x 28672 x 8192) is checked on sampled entries, two full rows, two full
 columns and one 128x128 tile.
+
+E4M3 output (an integer code decided by floating point): the bytes must equal,
+bit for bit, the oracle's E4M3 encoding of the kernel's own float32 output for
+the same call (both sides encode the same float32 value), and the decoded values
+must lie within the float32 bound above plus one E4M3 rounding of the float64
+reference (half a spacing: |x|/16, or 2^-10 below 2^-6), saturating at 448.
 """
 import numpy as np
 import pytest
@@ -89,6 +95,9 @@ def test_gemm_small_shapes(fmt, M, N, K):
     _check(D.cpu().numpy(), fmt, ops, K, 1.0, False)
     D = _gpu_gemm(fmt, ops, K, -2.5, torch.bfloat16)
     _check(D.float().cpu().numpy(), fmt, ops, K, -2.5, True)
+    # the bf16 output is the nearest-even bf16 of the float32 result, bit for bit
+    D32 = _gpu_gemm(fmt, ops, K, -2.5, torch.float32).cpu().numpy()
+    assert np.array_equal(D.cpu().view(torch.int16).numpy().view(np.uint16), o.f32_to_bf16_bits(D32))
 
 
 @pytest.mark.parametrize("fmt", ["nv", "mx"])
@@ -99,10 +108,10 @@ def test_gemm_empty_k_writes_zeros(fmt):
     e = torch.empty((5, 0), dtype=torch.uint8, device=dev)
     g = torch.ones(1, dtype=torch.float32, device=dev) if fmt == "nv" else None
     f = fp4.FP4_NVFP4 if fmt == "nv" else fp4.FP4_MXFP4
-    for out in (torch.float32, torch.bfloat16):
-        D = torch.full((5, 5), 3.0, dtype=out, device=dev)
+    for out in (torch.float32, torch.bfloat16, torch.float8_e4m3fn):
+        D = torch.full((5, 5), 3.0, dtype=torch.float32, device=dev).to(out)
         fp4.fp4_scaled_gemm(f, e, e, g, e, e, g, 0, 1.0, out, out=D)
-        assert torch.count_nonzero(D).item() == 0
+        assert torch.count_nonzero(D.view(torch.uint8)).item() == 0
     z = torch.empty((0, 16), dtype=torch.uint8, device=dev)
     assert fp4.fp4_scaled_gemm(f, z, z, g, z, z, g, 32).shape == (0, 0)
 
@@ -153,3 +162,85 @@ def test_gemm_prefill_shape_sampled(fmt):
     r0, c0 = 4096 + 64, 20480 + 96
     tr, tc = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
     _check(D[r0:r0 + 128, c0:c0 + 128].float().cpu().numpy(), fmt, ops, K, 1.0, True, rows=tr, cols=tc)
+
+
+def _check_e4m3(D8, D32, fmt, ops, K, g_d, rows=None, cols=None):
+    """E4M3 bytes D8 against (1) the oracle encoding of the kernel's float32
+    output D32 (bit-exact) and (2) the float64 reference (decoded values)."""
+    codes = D8.view(torch.uint8).cpu().numpy()
+    d32 = D32.cpu().numpy()
+    exp = o.gemm_e4m3_output(d32)
+    bad = np.flatnonzero(codes.ravel() != exp.ravel())
+    assert bad.size == 0, (f"{bad.size} E4M3 codes differ from the oracle encoding of the float32 "
+                           f"output, first at {np.unravel_index(bad[0], codes.shape)}")
+    qa, sa, ga, qw, sw, gw = ops
+    Ah = _hat(fmt, qa, sa, 1.0 if ga is None else ga, K, rows)
+    Wh = _hat(fmt, qw, sw, 1.0 if gw is None else gw, K, cols)
+    ref, mag = o.scaled_gemm_ref(Ah, Wh, g_d)
+    tol = o.GEMM_REL_TOL * mag
+    want = np.clip(ref, -o.E4M3_MAX, o.E4M3_MAX)
+    bound = tol + (np.abs(ref) + tol) / 16.0 + 2.0 ** -10
+    err = np.abs(o.e4m3_decode(codes) - want)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    return codes
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (17, 33, 96), (100, 300, 384), (300, 520, 4096),
+                                   (513, 257, 1056)])
+def test_gemm_e4m3_output(fmt, M, N, K):
+    """E4M3 output with g_d chosen so the results cover subnormal, normal and
+    saturated (|D| > 448) codes; N = 33 and 257 take the byte-store path."""
+    announce(f"gemm e4m3 out {fmt} {M}x{N}x{K}")
+    A = o.bf16_bits_to_f32(workloads.gemm_a(M, K, seed=170 + M))
+    W = o.bf16_bits_to_f32(workloads.gemm_w(N, K, seed=171 + N))
+    ops = _operands(fmt, M, N, K, 0, quantized_from=(A, W))
+    D32 = _gpu_gemm(fmt, ops, K, 1.0, torch.float32)
+    spread = float(torch.quantile(D32.abs().flatten()[:100000], 0.5).item()) if M * N > 1 else 1.0
+    for g_d in (1.0, 300.0 / max(spread, 1e-30), -0.01 / max(spread, 1e-30)):
+        D8 = _gpu_gemm(fmt, ops, K, g_d, torch.float8_e4m3fn)
+        assert D8.dtype == torch.float8_e4m3fn and D8.shape == (M, N)
+        D32g = _gpu_gemm(fmt, ops, K, g_d, torch.float32)
+        _check_e4m3(D8, D32g, fmt, ops, K, g_d)
+    if M * N >= 1000:
+        codes = D8.view(torch.uint8).cpu().numpy() & 0x7F
+        assert np.any(codes < 8), "no subnormal codes exercised"
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
+def test_gemm_e4m3_output_saturates(fmt):
+    """A large g_d pushes most outputs past 448: they saturate to +-448 with the
+    result's sign (0x7E / 0xFE), never NaN (0x7F / 0xFF)."""
+    announce(f"gemm e4m3 saturation {fmt}")
+    M, N, K = 64, 96, 512
+    A = o.bf16_bits_to_f32(workloads.gemm_a(M, K, seed=180))
+    W = o.bf16_bits_to_f32(workloads.gemm_w(N, K, seed=181))
+    ops = _operands(fmt, M, N, K, 0, quantized_from=(A, W))
+    D8 = _gpu_gemm(fmt, ops, K, 1e6, torch.float8_e4m3fn)
+    D32 = _gpu_gemm(fmt, ops, K, 1e6, torch.float32)
+    codes = _check_e4m3(D8, D32, fmt, ops, K, 1e6)
+    assert np.mean((codes & 0x7F) == 0x7E) > 0.9
+    assert not np.any((codes & 0x7F) == 0x7F)
+
+
+def test_gemm_e4m3_output_prefill_sampled():
+    """NVFP4 8192 x 28672 x 8192 (the timed prefill shape) with E4M3 output:
+    bit-exact against the oracle encoding of the float32 output on 2^20 sampled
+    entries and one 128x128 tile, and within bound of the float64 reference on
+    that tile."""
+    announce("gemm prefill nv e4m3 out")
+    M, N, K = 8192, 28672, 8192
+    ops = _operands("nv", M, N, K, 91)
+    g_d = 0.25
+    D8 = _gpu_gemm("nv", ops, K, g_d, torch.float8_e4m3fn)
+    D32 = _gpu_gemm("nv", ops, K, g_d, torch.float32)
+    rng = np.random.default_rng(94)
+    ii = torch.from_numpy(rng.integers(0, M, 1 << 20)).cuda()
+    jj = torch.from_numpy(rng.integers(0, N, 1 << 20)).cuda()
+    codes = D8.view(torch.uint8)[ii, jj].cpu().numpy()
+    exp = o.gemm_e4m3_output(D32[ii, jj].cpu().numpy())
+    assert np.array_equal(codes, exp), f"{np.count_nonzero(codes != exp)} sampled codes differ"
+    r0, c0 = 2048 + 32, 12288 + 160
+    tr, tc = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
+    _check_e4m3(D8[r0:r0 + 128, c0:c0 + 128], D32[r0:r0 + 128, c0:c0 + 128], "nv", ops, K, g_d,
+                rows=tr, cols=tc)
