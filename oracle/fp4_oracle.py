@@ -470,6 +470,18 @@ def gemm_e4m3_output(D_f32: np.ndarray) -> np.ndarray:
     return e4m3_encode_signed(np.asarray(D_f32, dtype=F32))
 
 
+def gemm_nvfp4_output(D_f32: np.ndarray, amax):
+    """The GEMM's NVFP4 output from its float32 result D = fl(acc * alpha): the
+    next layer's input quantization done on the GEMM's result ([MS] section 三:
+    the output is rescaled by g_d and stored at low precision; section 五: the
+    tensor scales come from calibration).  The tensor amax is a given
+    (calibrated) value: the global scale must be known before any output block
+    is encoded, and the GEMM writes blocks as it finishes them.  Blocks of 16
+    run along N, exactly as nvfp4_quantize with a static amax.
+    Returns (codes [M, ceil(N/2)], scale bytes [M, ceil(N/16)], G, s_global)."""
+    return nvfp4_quantize(np.asarray(D_f32, dtype=F32), amax=amax)
+
+
 def gemm_within_tolerance(D, D_ref, mag, out_bf16: bool = False):
     """Acceptance rule for GEMM/GEMV outputs: fp32 outputs within 1e-5 of the
     magnitude sum; bf16 outputs additionally allowed one bf16 rounding of D_ref."""

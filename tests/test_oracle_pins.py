@@ -124,6 +124,36 @@ def test_e4m3_signed_encode_for_gemm_output():
     assert np.array_equal(o.gemm_e4m3_output(t), ref)
 
 
+def test_gemm_nvfp4_output_worked_blocks():
+    """Hand-encoded 16-value output rows, every step done by hand:
+      - amax 2688: s_global = 1, block amax 6 -> t = 1 -> byte 0x38; the codes
+        are the E2M1 codes of the values themselves (0.25, the 0 / 0.5 tie,
+        goes to the even code 0);
+      - the row times 2 at amax 2688: t = 2 -> byte 0x40, s_b = 2, same codes;
+      - the row times 2^-6 at amax 42 = 2688 * 2^-6: s_global = 2^-6, t = 1;
+      - amax 5.25 = 2688 / 512 (below the row's max, as with a stale
+        calibration): t = 512 saturates to 448 (0x7E), s_b = 0.875, so
+        q = x / 0.875: 6 -> 6.86 -> 6, 3 -> 3.43 -> 3, 0.25 -> 0.286 -> 0.5;
+      - a ragged row of 5 values [0, .5, 1, 1.5, 2] at amax 2688: t = 1/3
+        -> nearest E4M3 0.34375 = 1.375 * 2^-2 (0x2B), q = x / 0.34375 =
+        [0, 1.45, 2.91, 4.36, 5.82] -> codes [0, 3, 5, 6, 7]; odd N leaves the
+        last high nibble 0."""
+    row = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6, 0.25], F32)
+    codes = [[0x10, 0x32, 0x54, 0x76, 0xA9, 0xCB, 0xED, 0x0F]]
+    q, s, G, sg = o.gemm_nvfp4_output(row[None, :], 2688.0)
+    assert s.tolist() == [[0x38]] and float(sg) == 1.0 and float(G) == 2688.0
+    assert q.tolist() == codes
+    q, s, _, sg = o.gemm_nvfp4_output((row * F32(2))[None, :], 2688.0)
+    assert float(sg) == 1.0 and s.tolist() == [[0x40]] and q.tolist() == codes
+    q, s, _, sg = o.gemm_nvfp4_output((row * F32(2.0 ** -6))[None, :], 42.0)
+    assert float(sg) == 2.0 ** -6 and s.tolist() == [[0x38]] and q.tolist() == codes
+    q, s, _, sg = o.gemm_nvfp4_output(row[None, :], 5.25)
+    assert float(sg) == 2.0 ** -9 and s.tolist() == [[0x7E]]
+    assert q.tolist() == [[0x10, 0x32, 0x54, 0x76, 0xA9, 0xCB, 0xED, 0x1F]]
+    q, s, _, _ = o.gemm_nvfp4_output(row[None, :5], 2688.0)
+    assert s.tolist() == [[0x2B]] and q.tolist() == [[0x30, 0x65, 0x07]]
+
+
 def test_e4m3_relative_error_and_neighbour_ratio():
     # [LPF] section FP8: relative error of E4M3 rounding <= 2^-(M+1) = 6.25% (normal range)
     rng = np.random.default_rng(3)
