@@ -10,7 +10,8 @@ workload's shape:
                mxfp4_quantize, NVFP4 and MXFP4 dequantize to bf16
   decode GEMV  W 27648x5120 NVFP4, x bf16 [B, 5120] quantized on the fly, B = 1, 4, 16
   prefill GEMM 8192 x 28672 x 8192, NVFP4 and MXFP4 operands, bf16 output;
-               NVFP4 again with the output requantized to FP8 E4M3 in the epilogue
+               NVFP4 again with the output requantized in the epilogue to FP8 E4M3,
+               and to NVFP4 at a given (calibrated) amax
   rotate       16384x8192 bf16, 16 outlier channels x60: FWHT-128 + NVFP4, RNE and SR
 Each call kind is captured in its own HIP graph of R back-to-back calls that
 cycle through input copies totalling >= 1 GiB (more than the 256 MiB Infinity
@@ -245,6 +246,19 @@ def main():
                                  P(gw_nv), 1.0, Mg, Ng, Kg, P(D8), fp4.FP4_E4M3, stream_of())
         assert st == 0, st
 
+    # NVFP4 output at a calibrated amax of D (its max, taken once here)
+    gemm_nv(0)
+    d_amax = Dg.abs().max().float().reshape(1)
+    Dq4 = torch.empty((Mg, Ng // 2), dtype=torch.uint8, device=dev)
+    Dsc4 = torch.empty((Mg, Ng // 16), dtype=torch.uint8, device=dev)
+    Dgs4 = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def gemm_nv_nv4(i):
+        st = lib.fp4_scaled_gemm_nvfp4_out(fp4.FP4_NVFP4, P(aq_nv), P(as_nv), P(ga_nv), P(wq_nv),
+                                           P(wsc_nv), P(gw_nv), 1.0, Mg, Ng, Kg, P(Dq4), P(Dsc4),
+                                           P(d_amax), P(Dgs4), stream_of())
+        assert st == 0, st
+
     def gemm_mx(i):
         st = lib.fp4_scaled_gemm(fp4.FP4_MXFP4, P(aq_mx), P(as_mx), None, P(wq_mx), P(wsc_mx), None,
                                  1.0, Mg, Ng, Kg, P(Dg), fp4.FP4_BF16, stream_of())
@@ -257,6 +271,8 @@ def main():
            "k_gemm<MX> (scaled FP4 MFMA)", msrc),
         Op("gemm_nvfp4_e4m3_out", gemm_nv_e4m3, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp16"], "mfma",
            "k_gemm<NV, E4M3 out> (output requantized to FP8 E4M3 in the epilogue)", msrc),
+        Op("gemm_nvfp4_nvfp4_out", gemm_nv_nv4, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp16"],
+           "mfma", "k_gemm<NV, NVFP4 out> (output requantized to NVFP4 at a given amax)", msrc),
     ]
 
     # -------------------------------------------------------------- rotate --
@@ -348,7 +364,7 @@ def main():
             ("bytes_per_call" if op.unit == "GB/s" else "flop_per_call"): op.per_call,
             "kernels": op.kernel, "calls_per_replay": op.n, "traffic": tr_bytes,
         }
-        if op.name in ("gemm_nvfp4", "gemm_nvfp4_e4m3_out"):
+        if op.name in ("gemm_nvfp4", "gemm_nvfp4_e4m3_out", "gemm_nvfp4_nvfp4_out"):
             comps[op.name]["frac_of_fp4_peak"] = round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4)
 
     head = comps.get("nvfp4_quantize_dynamic") or next(iter(comps.values()))
@@ -374,7 +390,7 @@ def main():
             "value_bytes_note": "x read twice (amax pass, encode pass) + codes + scale bytes + 2 floats",
             "step_also_runs": "mxfp4_quantize, NV/MX dequantize (8192x8192); GEMV W 27648x5120 "
                               "B=1,4,16; GEMM 8192x28672x8192 NVFP4 and MXFP4 (bf16 out), NVFP4 "
-                              "(E4M3 out); FWHT+NVFP4 "
+                              "(E4M3 out, NVFP4 out); FWHT+NVFP4 "
                               "16384x8192 RNE and SR",
         },
         "roofline": {

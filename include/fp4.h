@@ -139,6 +139,34 @@ fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_sc
                            const float* g_b, float g_d, int64_t M, int64_t N, int64_t K,
                            void* D, fp4_dtype dt, hipStream_t stream);
 
+/*
+ * fp4_scaled_gemm_nvfp4_out -- the same GEMM with its output requantized to
+ * NVFP4 in the epilogue: the next layer's input quantization fused into this
+ * layer's GEMM (article of fp4_scaled_gemm, section 三: the output is rescaled by
+ * g_d and stored at low precision; section 五: the scales come from calibration).
+ *   A .. g_d, M, N, K  as for fp4_scaled_gemm.
+ *   d_amax    in: device float, the given (calibrated) tensor amax G of D; the
+ *             tensor scale has to be known before any output block is encoded,
+ *             so it is not computed from D.
+ *   Dq        out [M, ceil(N/2)] packed E2M1 codes (low nibble first; for odd N
+ *             the last high nibble is 0);
+ *   d_scales  out [M, ceil(N/16)] E4M3 block-scale bytes, blocks of 16 along N
+ *             (the last block partial when N % 16 != 0);
+ *   d_global_scale out: device float s_global = G / 2688 (1 when G == 0), the g
+ *             of D for the next GEMM.
+ * Dq, d_scales and d_global_scale are exactly what nvfp4_quantize with
+ * amax_given writes for the float32 result D = fl(acc * alpha) that
+ * fp4_scaled_gemm produces for the same operands, bit for bit.  d_amax must not
+ * alias d_global_scale.  M == 0 or N == 0 is a no-op; K == 0 encodes D = 0
+ * (codes 0, scale bytes 0) without reading the operands.  Errors as for
+ * fp4_scaled_gemm; NULL d_amax, d_scales or d_global_scale -> FP4_ERR_NULL.
+ */
+fp4_status fp4_scaled_gemm_nvfp4_out(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
+                                     const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                                     const float* g_b, float g_d, int64_t M, int64_t N, int64_t K,
+                                     uint8_t* Dq, uint8_t* d_scales, const float* d_amax,
+                                     float* d_global_scale, hipStream_t stream);
+
 /* Bytes of workspace fp4_gemv_batched needs for a batch of B rows of length K. */
 size_t fp4_gemv_workspace_bytes(int64_t B, int64_t K);
 

@@ -40,6 +40,9 @@ SIGNATURES = {
     "fp4_scaled_gemm": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                        ctypes.c_float, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_int,
                                        _c_p]),
+    "fp4_scaled_gemm_nvfp4_out": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                 ctypes.c_float, _c_i64, _c_i64, _c_i64, _c_p,
+                                                 _c_p, _c_p, _c_p, _c_p]),
     "fp4_gemv_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "fp4_gemv_batched": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_p, _c_p, _c_p, _c_i64,
                                         _c_i64, ctypes.c_float, _c_p, ctypes.c_int, _c_p,
@@ -196,6 +199,35 @@ def fp4_scaled_gemm(fmt: int, A: torch.Tensor, a_scales: torch.Tensor, g_a, W: t
                                         _dtype_code(D.dtype), _stream(dev))
     _check(st, "fp4_scaled_gemm")
     return D
+
+
+def fp4_scaled_gemm_nvfp4_out(fmt: int, A: torch.Tensor, a_scales: torch.Tensor, g_a,
+                              W: torch.Tensor, w_scales: torch.Tensor, g_b, K: int,
+                              d_amax: torch.Tensor, g_d: float = 1.0):
+    """The scaled GEMM with its output quantized to NVFP4 at the given tensor
+    amax d_amax (device float): returns (codes [M, ceil(N/2)], scale bytes
+    [M, ceil(N/16)], s_global of D [1])."""
+    A = _gpu_2d(A, "A")
+    W = _gpu_2d(W, "W")
+    a_scales = _gpu_2d(a_scales, "a_scales")
+    w_scales = _gpu_2d(w_scales, "w_scales")
+    dev = A.device
+    M, N = A.shape[0], W.shape[0]
+    if A.shape[1] != K // 2 or W.shape[1] != K // 2:
+        raise ValueError("A and W must be [rows, K/2] packed codes")
+    if d_amax.dtype != torch.float32 or d_amax.device != dev:
+        raise TypeError("d_amax must be a float32 tensor on the operands' device")
+    q = torch.empty((M, (N + 1) // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((M, (N + 15) // 16), dtype=torch.uint8, device=dev)
+    gs = torch.empty(1, dtype=torch.float32, device=dev)
+    ga = None if g_a is None else g_a.reshape(1).contiguous()
+    gb = None if g_b is None else g_b.reshape(1).contiguous()
+    am = d_amax.reshape(1).contiguous()
+    st = load_library().fp4_scaled_gemm_nvfp4_out(fmt, _ptr(A), _ptr(a_scales), _ptr(ga), _ptr(W),
+                                                  _ptr(w_scales), _ptr(gb), float(g_d), M, N, K,
+                                                  _ptr(q), _ptr(sc), _ptr(am), _ptr(gs), _stream(dev))
+    _check(st, "fp4_scaled_gemm_nvfp4_out")
+    return q, sc, gs
 
 
 def gemv_workspace_bytes(B: int, K: int) -> int:

@@ -181,6 +181,41 @@ fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_sc
   return FP4_OK;
 }
 
+fp4_status fp4_scaled_gemm_nvfp4_out(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
+                                     const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                                     const float* g_b, float g_d, int64_t M, int64_t N, int64_t K,
+                                     uint8_t* Dq, uint8_t* d_scales, const float* d_amax,
+                                     float* d_global_scale, hipStream_t stream) {
+  if (fmt != FP4_NVFP4 && fmt != FP4_MXFP4) return FP4_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return FP4_ERR_SHAPE;
+  if (K % 32 != 0) return FP4_ERR_SHAPE;
+  if (fmt == FP4_MXFP4 && (g_a != nullptr || g_b != nullptr)) return FP4_ERR_DTYPE;
+  if (M == 0 || N == 0) return FP4_OK;
+  if (Dq == nullptr || d_scales == nullptr || d_amax == nullptr || d_global_scale == nullptr)
+    return FP4_ERR_NULL;
+  if (!aligned(d_amax, 4) || !aligned(d_global_scale, 4)) return FP4_ERR_ALIGN;
+  if (K == 0) {   // empty contraction: D = 0 encodes as codes 0 and scale bytes 0
+    fp4_status st = check_arch();
+    if (st != FP4_OK) return st;
+    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(Dq, M * ((N + 1) / 2), 1, stream), "fp4_scaled_gemm_nvfp4_out");
+    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(d_scales, M * ((N + 15) / 16), 1, stream),
+                   "fp4_scaled_gemm_nvfp4_out");
+    FP4_TRY_LAUNCH(fp4impl::launch_nv_global_scale(d_amax, d_global_scale, stream),
+                   "fp4_scaled_gemm_nvfp4_out");
+    return FP4_OK;
+  }
+  if (A == nullptr || a_scales == nullptr || W == nullptr || w_scales == nullptr) return FP4_ERR_NULL;
+  if (fmt == FP4_NVFP4 && (g_a == nullptr || g_b == nullptr)) return FP4_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(W, 16)) return FP4_ERR_ALIGN;
+  fp4_status st = check_arch();
+  if (st != FP4_OK) return st;
+  FP4_TRY_LAUNCH(fp4impl::launch_gemm_nvfp4_out(fmt == FP4_MXFP4, A, a_scales, g_a, W, w_scales, g_b,
+                                                g_d, M, N, K, Dq, 0, d_scales, d_amax,
+                                                d_global_scale, stream),
+                 "fp4_scaled_gemm_nvfp4_out");
+  return FP4_OK;
+}
+
 size_t fp4_gemv_workspace_bytes(int64_t B, int64_t K) {
   if (B < 0 || K < 0) return 0;
   return fp4impl::gemv_workspace_bytes(B, K);

@@ -53,5 +53,15 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
 hipError_t launch_gemm(bool mx, const uint8_t* A, const uint8_t* a_scales, const float* g_a,
                        const uint8_t* W, const uint8_t* w_scales, const float* g_b, float g_d,
                        int64_t M, int64_t N, int64_t K, void* D, int d_bytes, hipStream_t stream);
+// The same GEMM with d_bytes = 0: D receives NVFP4 codes [M, ceil(N/2)] and
+// d_scales the E4M3 bytes [M, ceil(N/16)] of fl(acc * alpha), quantized at the
+// given tensor amax *d_amax; *d_gscale receives its s_global.
+hipError_t launch_gemm_nvfp4_out(bool mx, const uint8_t* A, const uint8_t* a_scales,
+                                 const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                                 const float* g_b, float g_d, int64_t M, int64_t N, int64_t K,
+                                 void* D, int d_bytes, uint8_t* d_scales, const float* d_amax,
+                                 float* d_gscale, hipStream_t stream);
+// *out = s_global of the tensor amax *amax (one thread).
+hipError_t launch_nv_global_scale(const float* amax, float* out, hipStream_t stream);
 
 }  // namespace fp4impl

@@ -274,13 +274,121 @@ __device__ __forceinline__ v8h dq8(uint32_t codes, v2h s) {
   return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// ---------------------------------------------------------------- epilogue --
+// Writes a wave's outputs: lane (r16, g) holds D[mb + 16 j][nb + 16 i .. +3]
+// (before the multiply by alpha) in acc[i][j].  EDGE: the tile may cross M or
+// N, or rows may not take whole 4-output stores; otherwise every store is
+// whole and unconditional.
+template <int OUT, bool EDGE>
+__device__ __forceinline__ void store_outputs(v4f (&acc)[kTN][kTM], float alpha, float s_glob,
+                                              int mb, int nb, int M, int N, void* __restrict__ D,
+                                              uint8_t* __restrict__ d_scales, bool vec_out, int r16,
+                                              int g) {
+#pragma unroll
+  for (int j = 0; j < kTM; ++j) {
+    const int m = mb + 16 * j;
+    if (EDGE && m >= M) continue;
+    if constexpr (OUT == 0) {
+      // NVFP4.  The 16 columns of block (m, i) are held by the lanes r16 + 16 g'
+      // (g' = 0..3), which share m.  Per group of 4 tiles the lanes reduce the
+      // 4 block maxima, lane g computes the scale of block i4 + g (as the
+      // quantizer does) and stores its byte, and every lane takes each block's
+      // multiplier from the lane that computed it.
+      uint8_t* qrow = reinterpret_cast<uint8_t*>(D) + (int64_t)m * ((N + 1) / 2);
+      uint8_t* srow = d_scales + (int64_t)m * ((N + 15) / 16);
+#pragma unroll
+      for (int i4 = 0; i4 < kTN; i4 += 4) {
+        v4f x[4];
+        float a[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // (keeps the accumulator in its AGPRs until here: read tile by tile,
+          // the epilogue needs a few VGPRs, not 256)
+          asm volatile("" : "+a"(acc[i4 + k][j]));
+          x[k] = acc[i4 + k][j] * alpha;
+          if (EDGE) {
+            const int n = nb + 16 * (i4 + k);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n + q >= N) x[k][q] = 0.0f;
+          }
+          a[k] = fmaxf(fmaxf(fabsf(x[k].x), fabsf(x[k].y)), fmaxf(fabsf(x[k].z), fabsf(x[k].w)));
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = fmaxf(a[k], __shfl_xor(a[k], 16, 64));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = fmaxf(a[k], __shfl_xor(a[k], 32, 64));
+        const float ab = g == 0 ? a[0] : g == 1 ? a[1] : g == 2 ? a[2] : a[3];
+        uint32_t sc;
+        float r;
+        nv_block_scale(ab, s_glob, sc, r);
+        const int nblk = nb + 12 * g + 16 * i4;   // first column of block i4 + g
+        if (!EDGE || nblk < N) srow[nblk / 16] = (uint8_t)sc;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float rk = __shfl(r, r16 + 16 * k, 64);
+          uint32_t c = e2m1_pack2<0>(0u, x[k].x * rk, x[k].y * rk);
+          c = e2m1_pack2<1>(c, x[k].z * rk, x[k].w * rk);
+          const int n = nb + 16 * (i4 + k);
+          if (!EDGE || (vec_out && n + 3 < N)) {
+            *reinterpret_cast<uint16_t*>(qrow + n / 2) = (uint16_t)c;
+          } else {
+            if (n < N) qrow[n / 2] = (uint8_t)c;
+            if (n + 2 < N) qrow[n / 2 + 1] = (uint8_t)(c >> 8);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTN; ++i) {
+        const int n = nb + 16 * i;
+        asm volatile("" : "+a"(acc[i][j]));
+        const v4f v = acc[i][j] * alpha;
+        const bool whole = !EDGE || (vec_out && n + 3 < N);
+        if constexpr (OUT == 2) {
+          uint16_t* row = reinterpret_cast<uint16_t*>(D) + (int64_t)m * N;
+          const u32x2 h = u32x2{bf16_pack2(v.x, v.y), bf16_pack2(v.z, v.w)};
+          if (whole) {
+            *reinterpret_cast<u32x2*>(row + n) = h;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) row[n + q] = (uint16_t)(h[q >> 1] >> (16 * (q & 1)));
+          }
+        } else if constexpr (OUT == 1) {
+          uint8_t* row = reinterpret_cast<uint8_t*>(D) + (int64_t)m * N;
+          const uint32_t c = e4m3_pack4_signed(v.x, v.y, v.z, v.w);
+          if (whole) {
+            *reinterpret_cast<uint32_t*>(row + n) = c;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) row[n + q] = (uint8_t)(c >> (8 * q));
+          }
+        } else {
+          float* row = reinterpret_cast<float*>(D) + (int64_t)m * N;
+          if (whole) {
+            *reinterpret_cast<v4f*>(row + n) = v;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) row[n + q] = v[q];
+          }
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ kernel --
 template <bool MX, int OUT, bool SCALE_VEC>
 __global__ void __launch_bounds__(kThreads, 1)
     k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ as,
            const uint8_t* __restrict__ W, const uint8_t* __restrict__ ws,
            const float* __restrict__ g_a, const float* __restrict__ g_b, float g_d, int M, int N,
-           int K, void* __restrict__ D, int tiles_m, int tiles_n, bool vec_out) {
+           int K, void* __restrict__ D, uint8_t* __restrict__ d_scales,
+           const float* __restrict__ d_amax, float* __restrict__ d_gscale, int tiles_m, int tiles_n,
+           bool vec_out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -593,55 +701,32 @@ __global__ void __launch_bounds__(kThreads, 1)
   // epilogue: lane holds D[m][n .. n+3] for each tile pair; D = acc * ((g_a * g_b) * g_d)
   float alpha = g_d;
   if (!MX) alpha = ((*g_a) * (*g_b)) * g_d;
-#pragma unroll
-  for (int j = 0; j < kTM; ++j) {
-    const int m = m0 + wm * 16 * kTM + 16 * j + r16;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < kTN; ++i) {
-      const int n = n0 + wn * 16 * kTN + 16 * i + 4 * g;
-      // (keeps the accumulator in its AGPRs until here: read tile by tile, the
-      // epilogue needs a few VGPRs, not 256)
-      asm volatile("" : "+a"(acc[i][j]));
-      const v4f v = acc[i][j] * alpha;
-      if (OUT == 2) {
-        uint16_t* row = reinterpret_cast<uint16_t*>(D) + (int64_t)m * N;
-        const u32x2 h = u32x2{bf16_pack2(v.x, v.y), bf16_pack2(v.z, v.w)};
-        if (vec_out && n + 3 < N) {
-          *reinterpret_cast<u32x2*>(row + n) = h;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < N) row[n + q] = (uint16_t)(h[q >> 1] >> (16 * (q & 1)));
-        }
-      } else if (OUT == 1) {
-        uint8_t* row = reinterpret_cast<uint8_t*>(D) + (int64_t)m * N;
-        const uint32_t c = e4m3_pack4_signed(v.x, v.y, v.z, v.w);
-        if (vec_out && n + 3 < N) {
-          *reinterpret_cast<uint32_t*>(row + n) = c;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < N) row[n + q] = (uint8_t)(c >> (8 * q));
-        }
-      } else {
-        float* row = reinterpret_cast<float*>(D) + (int64_t)m * N;
-        if (vec_out && n + 3 < N) {
-          *reinterpret_cast<v4f*>(row + n) = v;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < N) row[n + q] = v[q];
-        }
-      }
-    }
+  // NVFP4 output: tensor scale of D from its given amax, as the quantizer's
+  float s_glob = 1.0f;
+  if (OUT == 0) {
+    s_glob = nv_global_scale(*d_amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *d_gscale = s_glob;
   }
+  const int mb = m0 + wm * 16 * kTM + r16, nb = n0 + wn * 16 * kTN + 4 * g;
+  if (vec_out && m0 + BM <= M && n0 + BN <= N)
+    store_outputs<OUT, false>(acc, alpha, s_glob, mb, nb, M, N, D, d_scales, true, r16, g);
+  else
+    store_outputs<OUT, true>(acc, alpha, s_glob, mb, nb, M, N, D, d_scales, vec_out, r16, g);
 }
+
+// Output of one GEMM call: D, plus the NVFP4 scale bytes, given amax and
+// written tensor scale when D holds NVFP4 codes.
+struct OutArgs {
+  void* D;
+  uint8_t* d_scales;
+  const float* d_amax;
+  float* d_gscale;
+};
 
 template <bool MX, int OUT, bool SCALE_VEC>
 hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
-                    const float* g_a, const float* g_b, float g_d, int M, int N, int K, void* D,
-                    hipStream_t stream) {
+                    const float* g_a, const float* g_b, float g_d, int M, int N, int K,
+                    const OutArgs& o, hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   constexpr int lds = Cfg<MX>::kLdsBytes;
   static bool attr_set = false;   // per process; the attribute is per function
@@ -652,33 +737,41 @@ hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const
     attr_set = true;
   }
   // 4 outputs per store when every row start is aligned to 4 outputs
-  const bool vec_out = N % 4 == 0 && reinterpret_cast<uintptr_t>(D) % (4 * OUT) == 0;
+  // (NVFP4: 4 outputs are 2 bytes)
+  const bool vec_out =
+      N % 4 == 0 && reinterpret_cast<uintptr_t>(o.D) % (OUT == 0 ? 2 : 4 * OUT) == 0;
   hipLaunchKernelGGL((k_gemm<MX, OUT, SCALE_VEC>), dim3(tiles_m * tiles_n), dim3(kThreads), lds,
-                     stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, D, tiles_m, tiles_n, vec_out);
+                     stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, o.D, o.d_scales, o.d_amax,
+                     o.d_gscale, tiles_m, tiles_n, vec_out);
   return hipGetLastError();
 }
 
 template <bool MX, int OUT>
 hipError_t launch_s(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
-                    const float* g_a, const float* g_b, float g_d, int M, int N, int K, void* D,
-                    hipStream_t stream) {
+                    const float* g_a, const float* g_b, float g_d, int M, int N, int K,
+                    const OutArgs& o, hipStream_t stream) {
   const bool vec = K % BK == 0 && (reinterpret_cast<uintptr_t>(as) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
-  return vec ? launch_t<MX, OUT, true>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream)
-             : launch_t<MX, OUT, false>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
+  return vec ? launch_t<MX, OUT, true>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream)
+             : launch_t<MX, OUT, false>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream);
 }
 
-// d_bytes: 4 float32, 2 bf16, 1 E4M3
+// d_bytes: 4 float32, 2 bf16, 1 E4M3, 0 NVFP4 codes
 template <bool MX>
 hipError_t launch_o(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
-                    const float* g_a, const float* g_b, float g_d, int M, int N, int K, void* D,
-                    int d_bytes, hipStream_t stream) {
+                    const float* g_a, const float* g_b, float g_d, int M, int N, int K,
+                    const OutArgs& o, int d_bytes, hipStream_t stream) {
   switch (d_bytes) {
-    case 4: return launch_s<MX, 4>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
-    case 2: return launch_s<MX, 2>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
-    case 1: return launch_s<MX, 1>(A, as, W, ws, g_a, g_b, g_d, M, N, K, D, stream);
+    case 4: return launch_s<MX, 4>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream);
+    case 2: return launch_s<MX, 2>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream);
+    case 1: return launch_s<MX, 1>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream);
+    case 0: return launch_s<MX, 0>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+__global__ void k_global_scale(const float* __restrict__ amax, float* __restrict__ out) {
+  if (threadIdx.x == 0) *out = nv_global_scale(*amax);
 }
 
 }  // namespace
@@ -688,12 +781,29 @@ namespace fp4impl {
 hipError_t launch_gemm(bool mx, const uint8_t* A, const uint8_t* a_scales, const float* g_a,
                        const uint8_t* W, const uint8_t* w_scales, const float* g_b, float g_d,
                        int64_t M, int64_t N, int64_t K, void* D, int d_bytes, hipStream_t stream) {
+  return launch_gemm_nvfp4_out(mx, A, a_scales, g_a, W, w_scales, g_b, g_d, M, N, K, D, d_bytes,
+                               nullptr, nullptr, nullptr, stream);
+}
+
+hipError_t launch_gemm_nvfp4_out(bool mx, const uint8_t* A, const uint8_t* a_scales,
+                                 const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                                 const float* g_b, float g_d, int64_t M, int64_t N, int64_t K,
+                                 void* D, int d_bytes, uint8_t* d_scales, const float* d_amax,
+                                 float* d_gscale, hipStream_t stream) {
   // buffer ranges cover one 256-row tile of an operand: 256 * K / 2 < 2^31
   if (M > (1 << 30) || N > (1 << 30) || K >= (1 << 23)) return hipErrorInvalidValue;
-  return mx ? launch_o<true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N, (int)K, D,
+  if (d_bytes == 0 && (d_scales == nullptr || d_amax == nullptr || d_gscale == nullptr))
+    return hipErrorInvalidValue;
+  const OutArgs o{D, d_scales, d_amax, d_gscale};
+  return mx ? launch_o<true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N, (int)K, o,
                              d_bytes, stream)
-            : launch_o<false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N, (int)K, D,
+            : launch_o<false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N, (int)K, o,
                               d_bytes, stream);
+}
+
+hipError_t launch_nv_global_scale(const float* amax, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_global_scale, dim3(1), dim3(64), 0, stream, amax, out);
+  return hipGetLastError();
 }
 
 }  // namespace fp4impl

@@ -111,3 +111,19 @@ def test_e4m3_dtype_is_a_gemm_output_only():
     assert lib.fp4_gemv_batched(P, 1, 4, P, P, P, 8, 512, 1.0, P, E4M3, P, need, None) == DTYPE
     assert lib.fp4_gemv_batched(P, E4M3, 4, P, P, P, 8, 512, 1.0, P, 1, P, need, None) == DTYPE
     assert lib.hadamard_quantize(P, E4M3, 4, 256, 128, 0, 0, P, P, P, 0, P, P, 4096, None) == DTYPE
+
+
+def test_gemm_nvfp4_out_argument_errors():
+    lib = m.load_library()
+    g = lib.fp4_scaled_gemm_nvfp4_out
+    assert g(2, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == DTYPE
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 48, P, P, P, P, None) == SHAPE      # K % 32
+    assert g(0, P, P, P, P, P, P, 1.0, -1, 8, 64, P, P, P, P, None) == SHAPE
+    assert g(1, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == DTYPE      # MX: no g_a/g_b
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, None, P, None) == NULL    # d_amax
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, None, P, P, None) == NULL    # d_scales
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, None, None) == NULL    # d_global_scale
+    assert g(0, P, P, None, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == NULL    # g_a
+    assert g(0, ctypes.c_void_p(4104), P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == ALIGN
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, ctypes.c_void_p(4098), P, None) == ALIGN
+    assert g(0, None, None, None, None, None, None, 1.0, 0, 8, 64, None, None, None, None, None) == OK

@@ -244,3 +244,84 @@ def test_gemm_e4m3_output_prefill_sampled():
     tr, tc = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
     _check_e4m3(D8[r0:r0 + 128, c0:c0 + 128], D32[r0:r0 + 128, c0:c0 + 128], "nv", ops, K, g_d,
                 rows=tr, cols=tc)
+
+
+def _gpu_gemm_nv_out(fmt, ops, K, g_d, amax):
+    qa, sa, ga, qw, sw, gw = ops
+    f = fp4.FP4_NVFP4 if fmt == "nv" else fp4.FP4_MXFP4
+    tga = None if ga is None else torch.tensor([ga], dtype=torch.float32, device="cuda:0")
+    tgw = None if gw is None else torch.tensor([gw], dtype=torch.float32, device="cuda:0")
+    tam = torch.tensor([amax], dtype=torch.float32, device="cuda:0")
+    return fp4.fp4_scaled_gemm_nvfp4_out(f, to_gpu_u8(qa), to_gpu_u8(sa), tga, to_gpu_u8(qw),
+                                         to_gpu_u8(sw), tgw, K, tam, g_d)
+
+
+def _check_nv_out(got, D32, amax, rows=None):
+    """NVFP4 output against the oracle's NVFP4 quantization (given amax) of the
+    kernel's own float32 result, bit for bit."""
+    q, sc, gs = got
+    qe, se, _, sge = o.gemm_nvfp4_output(D32, amax)
+    qn, sn = q.cpu().numpy(), sc.cpu().numpy()
+    if rows is not None:
+        qn, sn = qn[rows], sn[rows]
+    bad = np.argwhere(sn != se)
+    assert bad.size == 0, f"{len(bad)} scale bytes differ, first at {tuple(bad[0])}"
+    bad = np.argwhere(qn != qe)
+    assert bad.size == 0, f"{len(bad)} code bytes differ, first at {tuple(bad[0])}"
+    assert float(gs.item()) == float(sge)
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (17, 33, 96), (100, 300, 384), (300, 520, 4096),
+                                   (513, 257, 1056), (64, 301, 512)])
+def test_gemm_nvfp4_output(fmt, M, N, K):
+    """NVFP4 output at three given amaxes of D: its true max, 4x it (small
+    block scales) and a quarter of it (scales saturate at 448, codes at 6).
+    N = 33, 257, 301 take the byte-store path and partial last blocks; 300
+    has N % 16 != 0 with 4-value stores."""
+    announce(f"gemm nvfp4 out {fmt} {M}x{N}x{K}")
+    A = o.bf16_bits_to_f32(workloads.gemm_a(M, K, seed=190 + M))
+    W = o.bf16_bits_to_f32(workloads.gemm_w(N, K, seed=191 + N))
+    ops = _operands(fmt, M, N, K, 0, quantized_from=(A, W))
+    g_d = 0.5
+    D32 = _gpu_gemm(fmt, ops, K, g_d, torch.float32).cpu().numpy()
+    G = float(np.max(np.abs(D32)))
+    for amax in (G, 4.0 * G, 0.25 * G):
+        got = _gpu_gemm_nv_out(fmt, ops, K, g_d, amax)
+        assert got[0].shape == (M, (N + 1) // 2) and got[1].shape == (M, (N + 15) // 16)
+        _check_nv_out(got, D32, amax)
+
+
+def test_gemm_nvfp4_output_zero_amax_and_empty_k():
+    """amax 0 gives s_global 1 (the quantizer's rule); K = 0 encodes D = 0 as
+    codes 0 and scale bytes 0 without reading the operands."""
+    announce("gemm nvfp4 out: amax 0, K = 0")
+    M, N, K = 40, 48, 256
+    A = o.bf16_bits_to_f32(workloads.gemm_a(M, K, seed=195))
+    W = o.bf16_bits_to_f32(workloads.gemm_w(N, K, seed=196))
+    ops = _operands("nv", M, N, K, 0, quantized_from=(A, W))
+    D32 = _gpu_gemm("nv", ops, K, 1.0, torch.float32).cpu().numpy()
+    _check_nv_out(_gpu_gemm_nv_out("nv", ops, K, 1.0, 0.0), D32, 0.0)
+    dev = "cuda:0"
+    e = torch.empty((5, 0), dtype=torch.uint8, device=dev)
+    g = torch.ones(1, dtype=torch.float32, device=dev)
+    am = torch.tensor([10.0], dtype=torch.float32, device=dev)
+    e7 = torch.empty((7, 0), dtype=torch.uint8, device=dev)
+    q, sc, gs = fp4.fp4_scaled_gemm_nvfp4_out(fp4.FP4_NVFP4, e, e, g, e7, e7, g, 0, am)
+    assert q.shape == (5, 4) and sc.shape == (5, 1)
+    assert torch.count_nonzero(q).item() == 0 and torch.count_nonzero(sc).item() == 0
+    assert float(gs.item()) == float(o.nv_global_scale(np.float32(10.0)))
+
+
+def test_gemm_nvfp4_output_prefill_sampled():
+    """NVFP4 8192 x 28672 x 8192 with NVFP4 output at the float32 result's own
+    amax: 48 sampled full rows bit-exact against the oracle's quantization of
+    the same rows of the kernel's float32 output."""
+    announce("gemm prefill nv nvfp4 out")
+    M, N, K = 8192, 28672, 8192
+    ops = _operands("nv", M, N, K, 91)
+    D32 = _gpu_gemm("nv", ops, K, 1.0, torch.float32)
+    G = float(D32.abs().max().item())
+    got = _gpu_gemm_nv_out("nv", ops, K, 1.0, G)
+    rows = np.sort(np.random.default_rng(95).choice(M, 48, replace=False))
+    _check_nv_out(got, D32[torch.from_numpy(rows).cuda()].cpu().numpy(), G, rows=rows)
