@@ -304,6 +304,95 @@ def nvfp4_dequantize(packed, sbytes, s_global, cols: int) -> np.ndarray:
     return (s_el * v).astype(F32).reshape(R, cols)
 
 
+# ------------------------------------------------- NVFP4 scale variants ----
+# [MS] section 3.1: block sizes 8, 16 and 32, finer blocks recover local
+# dynamic range better at a higher scale overhead.  [NV] "高精度缩放": E4M3
+# block scales can be chosen so that the block's summed squared (or absolute)
+# error is as small as possible, rather than fixed by the block amax.
+E4M3_MAX_CODE = 126                     # 0x7E = 448; 0x7F is NaN
+
+
+def _search_order(window: int):
+    """Code offsets in the order the search visits them: 0, -1, +1, -2, +2, ..."""
+    out = [0]
+    for d in range(1, window + 1):
+        out += [-d, d]
+    return out
+
+
+def nv_block_sq_error(xb: np.ndarray, s_b: np.ndarray) -> np.ndarray:
+    """float32 squared error of encoding blocks xb [..., n] with scale s_b [...]:
+    r = fl(1/s_b) (0 when s_b == 0), v_i = E2M1 value of fl(x_i * r),
+    x_hat_i = fl(s_b * v_i), E = sum_i fl(fl(x_i - x_hat_i)^2), summed in index
+    order in float32 (the order and precision the search decides in)."""
+    xb = np.asarray(xb, dtype=F32)
+    s_b = np.asarray(s_b, dtype=F32)
+    nz = s_b != 0
+    r = np.where(nz, F32(1.0) / np.where(nz, s_b, F32(1.0)), F32(0.0)).astype(F32)
+    v = e2m1_decode(e2m1_encode_rne((xb * r[..., None]).astype(F32))).astype(F32)
+    xh = (s_b[..., None] * v).astype(F32)
+    d = (xb - xh).astype(F32)
+    sq = (d * d).astype(F32)
+    E = np.zeros(xb.shape[:-1], dtype=F32)
+    for i in range(xb.shape[-1]):
+        E = (E + sq[..., i]).astype(F32)
+    return E
+
+
+def nvfp4_quantize_ex(x: np.ndarray, block: int = NV_BLOCK, search: int = 0, amax=None):
+    """NVFP4 with blocks of `block` values (8, 16 or 32) along the last dim and
+    an optional search for the E4M3 scale byte.
+
+    search == 0: the amax rule of nvfp4_quantize (code0 = E4M3(fl(fl(A_b/6) /
+    s_global)), nearest, ties even).  search = W > 0: the candidates code0 + d
+    for d = 0, -1, +1, ..., -W, +W inside 0..126 are visited in that order and
+    a candidate replaces the current choice only when its float32 squared
+    error (nv_block_sq_error) is strictly smaller; the elements are then
+    encoded with the chosen scale exactly as nvfp4_quantize does.
+    Returns (packed codes [R, ceil(C/2)], scale bytes [R, ceil(C/block)], G,
+    s_global)."""
+    if block not in (8, 16, 32):
+        raise ValueError(block)
+    x = np.asarray(x, dtype=F32)
+    R, C = x.shape
+    G = global_amax(x) if amax is None else F32(amax)
+    s_global = nv_global_scale(G)
+    xb = _blocks(x, block)
+    A_b = np.max(np.abs(xb), axis=-1).astype(F32)
+    t = ((A_b / F32(6.0)).astype(F32) / s_global).astype(F32)
+    code = e4m3_encode_rne_sat(t).astype(np.int64)
+    if search > 0:
+        code0 = code.copy()
+        best = nv_block_sq_error(xb, (s_global * e4m3_decode(code0).astype(F32)).astype(F32))
+        for d in _search_order(search)[1:]:
+            c = code0 + d
+            ok = (c >= 0) & (c <= E4M3_MAX_CODE)
+            cc = np.clip(c, 0, E4M3_MAX_CODE)
+            E = nv_block_sq_error(xb, (s_global * e4m3_decode(cc).astype(F32)).astype(F32))
+            take = ok & (E < best)
+            code = np.where(take, cc, code)
+            best = np.where(take, E, best)
+    sbyte = code.astype(np.uint8)
+    s_b = (s_global * e4m3_decode(sbyte).astype(F32)).astype(F32)
+    nz = s_b != 0
+    r_b = np.where(nz, F32(1.0) / np.where(nz, s_b, F32(1.0)), F32(0.0)).astype(F32)
+    q = (xb * r_b[..., None]).astype(F32)
+    codes = e2m1_encode_rne(q)
+    codes = np.where(~nz[..., None], (np.signbit(xb).astype(np.uint8) << 3), codes)
+    codes = codes.reshape(R, -1)[:, :C]
+    return pack_nibbles(codes), sbyte, G, s_global
+
+
+def nvfp4_dequantize_ex(packed, sbytes, s_global, cols: int, block: int = NV_BLOCK) -> np.ndarray:
+    """nvfp4_dequantize for blocks of `block` values."""
+    codes = unpack_nibbles(packed, cols)
+    R = codes.shape[0]
+    v = e2m1_decode(codes).astype(F32)
+    s_b = (F32(s_global) * e4m3_decode(sbytes).astype(F32)).astype(F32)
+    s_el = np.repeat(s_b, block, axis=1)[:, :cols]
+    return (s_el * v).astype(F32).reshape(R, cols)
+
+
 # ----------------------------------------------------------------- MXFP4 ----
 def mxfp4_quantize(x: np.ndarray):
     """MXFP4: E2M1 values with one E8M0 power-of-two scale per 32 values and no

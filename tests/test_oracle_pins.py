@@ -496,3 +496,125 @@ def test_tolerance_rule_and_gemv_reference():
     xq, xs, xG, xg = o.nvfp4_quantize(A[:4])
     Dy, _ = o.scaled_gemm_ref(o.nv_operand_f64(xq, xs, xg, 256), Wh, 2.0)
     assert np.array_equal(y, Dy) and y.shape == (4, 64)
+
+
+# ------------------------------------------------ NVFP4 scale variants ------
+def test_nvfp4_ex_defaults_are_nvfp4_quantize():
+    x = np.random.default_rng(11).standard_normal((33, 200)).astype(F32)
+    for got, want in zip(o.nvfp4_quantize_ex(x, 16, 0), o.nvfp4_quantize(x)):
+        assert np.array_equal(got, want)
+
+
+def test_block_size_worked_row():
+    """Row [6]*8 + [3]*8 + [1.5]*8 + [0.75]*8 at amax 2688 (s_global = 1), by hand:
+    block 8: scales 6/6, 3/6, 1.5/6, 0.75/6 = 1, .5, .25, .125 -> 0x38, 0x30,
+             0x28, 0x20; every value is 6 * s_b -> code 7; exact;
+    block 16: A = 6, 1.5 -> 0x38, 0x28; 3 -> code 5, 0.75/0.25 = 3 -> code 5; exact;
+    block 32: A = 6 -> 0x38; 0.75 is the 0.5 / 1.0 tie -> even code 2 (1.0),
+             squared error 8 * 0.25^2 = 0.5 over 32 values."""
+    row = np.array([6.0] * 8 + [3.0] * 8 + [1.5] * 8 + [0.75] * 8, F32)[None, :]
+    q8, s8, _, g8 = o.nvfp4_quantize_ex(row, 8, 0, amax=2688.0)
+    assert s8.tolist() == [[0x38, 0x30, 0x28, 0x20]] and q8.tolist() == [[0x77] * 16]
+    q16, s16, _, g16 = o.nvfp4_quantize_ex(row, 16, 0, amax=2688.0)
+    assert s16.tolist() == [[0x38, 0x28]] and q16.tolist() == [[0x77] * 4 + [0x55] * 4 + [0x77] * 4 + [0x55] * 4]
+    q32, s32, _, g32 = o.nvfp4_quantize_ex(row, 32, 0, amax=2688.0)
+    assert s32.tolist() == [[0x38]]
+    assert q32.tolist() == [[0x77] * 4 + [0x55] * 4 + [0x33] * 4 + [0x22] * 4]
+    for q, s, g, bs, err in ((q8, s8, g8, 8, 0.0), (q16, s16, g16, 16, 0.0), (q32, s32, g32, 32, 0.5)):
+        y = o.nvfp4_dequantize_ex(q, s, g, 32, bs)
+        assert float(np.sum((y.astype(np.float64) - row) ** 2)) == err
+
+
+def test_scale_overhead_per_block_size():
+    """One E4M3 byte per block: 4 + 8/bs bits per value, i.e. 25%, 12.5% and
+    6.25% over the 4-bit data at bs = 8, 16, 32 (the [MS] section 3.1 table
+    prints half of each)."""
+    x = np.zeros((4, 96), F32)
+    for bs, over in ((8, 0.25), (16, 0.125), (32, 0.0625)):
+        q, s, _, _ = o.nvfp4_quantize_ex(x, bs)
+        assert s.shape == (4, 96 // bs) and q.shape == (4, 48)
+        assert s.size * 8 / (q.size * 8) == over
+
+
+def test_scale_search_worked_block():
+    """16 values of 5.0 at amax 2688 (s_global = 1), by hand: amax rule t = 5/6
+    -> nearest E4M3 0.8125 (0x35; 0.875 is further), q = 5/0.8125 = 6.15 -> 6,
+    x_hat = 4.875, error 16 * 0.125^2 = 0.25.  Its neighbours up to +-4
+    (0.6875 .. 1.125) decode 5 to 4.5 .. 5.5 or worse, so a window < 5 keeps
+    0x35; 0x3A = 1.25 (offset +5) gives x_hat = 1.25 * 4 = 5 exactly."""
+    row = np.full((1, 16), 5.0, F32)
+    # (window, scale byte, E2M1 code of every element: 7 is 6.0, 6 is 4.0)
+    for W, byte, code in ((0, 0x35, 7), (2, 0x35, 7), (4, 0x35, 7), (5, 0x3A, 6), (126, 0x3A, 6)):
+        q, s, _, g = o.nvfp4_quantize_ex(row, 16, W, amax=2688.0)
+        assert s.tolist() == [[byte]], W
+        assert set(o.unpack_nibbles(q, 16).ravel().tolist()) == {code}
+    assert float(o.nv_block_sq_error(row[0], np.float32(0.8125))) == 0.25
+    assert float(o.nv_block_sq_error(row[0], np.float32(1.25))) == 0.0
+
+
+def _e2m1_nearest_by_argmin(q):
+    """E2M1 value of q by brute force: argmin |q - v| over the 8 magnitudes,
+    ties to the even code, saturating (6 is the last magnitude)."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    m = abs(float(q))
+    best = min(range(8), key=lambda c: (abs(m - mags[c]), c & 1))
+    return np.float32(-mags[best] if np.signbit(q) else mags[best])
+
+
+def test_scale_search_brute_force_scalar():
+    """Per block, with float32 scalars and an argmin E2M1 encoder: the chosen
+    byte is the first, in the order 0, -1, +1, ..., of the codes with the least
+    float32 squared error within the window; with the window spanning every
+    code it is the global minimum over all 127 finite codes."""
+    rng = np.random.default_rng(12)
+    for bs in (8, 16, 32):
+        x = (rng.standard_normal((24, bs)) * np.exp(rng.uniform(-3, 3, (24, 1)))).astype(F32)
+        x[3, 2] *= 30
+        G = o.global_amax(x)
+        sg = o.nv_global_scale(G)
+        for W in (2, 126):
+            _, s, _, _ = o.nvfp4_quantize_ex(x, bs, W)
+            for b in range(x.shape[0]):
+                A = np.float32(np.max(np.abs(x[b])))
+                c0 = int(o.e4m3_encode_rne_sat(np.array([(A / np.float32(6)) / sg], F32))[0])
+                best, best_c = None, None
+                for d in [0] + [k * sgn for k in range(1, W + 1) for sgn in (-1, 1)]:
+                    c = c0 + d
+                    if not 0 <= c <= 126:
+                        continue
+                    sb = np.float32(sg * np.float32(o.e4m3_value(c)))
+                    r = np.float32(1) / sb if sb != 0 else np.float32(0)
+                    E = np.float32(0)
+                    for xi in x[b]:
+                        xh = np.float32(sb * _e2m1_nearest_by_argmin(np.float32(xi * r)))
+                        dd = np.float32(xi - xh)
+                        E = np.float32(E + np.float32(dd * dd))
+                    if best is None or E < best:
+                        best, best_c = E, c
+                assert s[b, 0] == best_c, (bs, W, b)
+
+
+def test_scale_variants_error_ordering():
+    """On N(0,1) rows with outlier channels: the search never raises a block's
+    float32 error, and the mean squared error falls with smaller blocks and
+    with a wider search window ([MS] section 3.1: finer blocks restore local
+    range better; [NV]: the E4M3 scale can minimise the block's error)."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((64, 512)).astype(F32)
+    x[:, ::97] *= 40
+    mse = {}
+    for bs in (8, 16, 32):
+        for W in (0, 1, 3):
+            q, s, G, g = o.nvfp4_quantize_ex(x, bs, W)
+            y = o.nvfp4_dequantize_ex(q, s, g, 512, bs)
+            mse[bs, W] = float(np.mean((y.astype(np.float64) - x) ** 2))
+        xb = o._blocks(x, bs)
+        s0 = o.nvfp4_quantize_ex(x, bs, 0)[1]
+        s3 = o.nvfp4_quantize_ex(x, bs, 3)[1]
+        e0 = o.nv_block_sq_error(xb, (g * o.e4m3_decode(s0).astype(F32)).astype(F32))
+        e3 = o.nv_block_sq_error(xb, (g * o.e4m3_decode(s3).astype(F32)).astype(F32))
+        assert np.all(e3 <= e0)
+    for W in (0, 1, 3):
+        assert mse[8, W] < mse[16, W] < mse[32, W]
+    for bs in (8, 16, 32):
+        assert mse[bs, 3] < mse[bs, 1] < mse[bs, 0]
