@@ -7,7 +7,9 @@ One step runs every call of the hot path once per input copy, each at its
 workload's shape:
   activation   8192x8192 bf16, N(0,1), 8 outlier channels x40:
                nvfp4_quantize (dynamic amax), nvfp4_quantize (static amax),
-               mxfp4_quantize, NVFP4 and MXFP4 dequantize to bf16
+               mxfp4_quantize, NVFP4 and MXFP4 dequantize to bf16;
+               NVFP4 scale variants (static amax): blocks of 8 and 32, and the
+               E4M3 scale search over +-2 codes, each with its round-trip MSE
   decode GEMV  W 27648x5120 NVFP4, x bf16 [B, 5120] quantized on the fly, B = 1, 4, 16
   prefill GEMM 8192 x 28672 x 8192, NVFP4 and MXFP4 operands, bf16 output;
                NVFP4 again with the output requantized in the epilogue to FP8 E4M3,
@@ -83,6 +85,7 @@ class Op:
         self.name, self.launch, self.n = name, launch, n_copies
         self.unit, self.per_call, self.peak, self.bound = unit, per_call, peak, bound
         self.kernel, self.src = kernel, src
+        self.extra = {}
         self.graph = None
         self.times_ms = []
 
@@ -193,6 +196,41 @@ def main():
         Op("mxfp4_dequantize_bf16", mx_deq, nA, "GB/s", b_mx, HBM_PEAK_GBS, "hbm",
            "k_dequant_fast<MX>", qsrc),
     ]
+
+    # NVFP4 scale variants on the same tensor (static amax: the encode pass
+    # alone, comparable with nvfp4_quantize_static): block sizes 8 and 32, and
+    # the least-squared-error E4M3 scale search over +-2 codes at block 16.
+    # Each reports the round-trip MSE of the whole tensor next to its rate.
+    def roundtrip_mse(block, W):
+        if block == 0:                                   # MXFP4
+            q, sc = fp4.mxfp4_quantize(xa)
+            y = fp4.fp4_dequantize(fp4.FP4_MXFP4, q, sc, None, C_A, torch.float32)
+        else:
+            q, sc, _, g = fp4.nvfp4_quantize_ex(xa, block, W, amax=static_amax)
+            y = fp4.nvfp4_dequantize_ex(q, sc, g, C_A, block, torch.float32)
+        d = y.double() - xa.double()
+        return float((d * d).mean())
+
+    for op in ops:
+        if op.name == "nvfp4_quantize_static":
+            op.extra["roundtrip_mse"] = roundtrip_mse(16, 0)
+        if op.name == "mxfp4_quantize":
+            op.extra["roundtrip_mse"] = roundtrip_mse(0, 0)
+    q_v = [torch.empty((R_A, C_A // 2), dtype=torch.uint8, device=dev) for _ in range(nA)]
+    g_v = torch.empty(1, dtype=torch.float32, device=dev)
+    for block, W in ((8, 0), (32, 0), (16, 2)):
+        s_v = [torch.empty((R_A, C_A // block), dtype=torch.uint8, device=dev) for _ in range(nA)]
+
+        def nv_var(i, block=block, W=W, s_v=s_v):
+            st = lib.nvfp4_quantize_ex(P(xa_c[i]), fp4.FP4_BF16, R_A, C_A, block, W, P(q_v[i]),
+                                       P(s_v[i]), P(static_amax), 1, P(g_v), None, 0, stream_of())
+            assert st == 0, st
+
+        name = f"nvfp4_quantize_block{block}" + (f"_search{W}" if W else "")
+        op = Op(name, nv_var, nA, "GB/s", elems * 2 + elems // 2 + elems // block + 8, HBM_PEAK_GBS,
+                "hbm", f"k_nv_quant_fast<block {block}{', scale search +-%d' % W if W else ''}>", qsrc)
+        op.extra["roundtrip_mse"] = roundtrip_mse(block, W)
+        ops.append(op)
 
     # --------------------------------------------------------- decode GEMV --
     Nv, Kv = 27648, 5120
@@ -364,6 +402,7 @@ def main():
             ("bytes_per_call" if op.unit == "GB/s" else "flop_per_call"): op.per_call,
             "kernels": op.kernel, "calls_per_replay": op.n, "traffic": tr_bytes,
         }
+        comps[op.name].update(op.extra)
         if op.name in ("gemm_nvfp4", "gemm_nvfp4_e4m3_out", "gemm_nvfp4_nvfp4_out"):
             comps[op.name]["frac_of_fp4_peak"] = round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4)
 
@@ -388,7 +427,8 @@ def main():
             "rows": R_A, "cols": C_A,
             "value_bytes_per_call": b_nv_dyn,
             "value_bytes_note": "x read twice (amax pass, encode pass) + codes + scale bytes + 2 floats",
-            "step_also_runs": "mxfp4_quantize, NV/MX dequantize (8192x8192); GEMV W 27648x5120 "
+            "step_also_runs": "mxfp4_quantize, NV/MX dequantize, NVFP4 block 8/32 and scale-search "
+                              "variants (8192x8192); GEMV W 27648x5120 "
                               "B=1,4,16; GEMM 8192x28672x8192 NVFP4 and MXFP4 (bf16 out), NVFP4 "
                               "(E4M3 out, NVFP4 out); FWHT+NVFP4 "
                               "16384x8192 RNE and SR",

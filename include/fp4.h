@@ -87,6 +87,35 @@ fp4_status nvfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t col
                           float* global_scale, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* Widest scale search of nvfp4_quantize_ex: +-126 codes covers every finite E4M3 byte. */
+#define FP4_MAX_SCALE_SEARCH 126
+
+/*
+ * nvfp4_quantize_ex -- nvfp4_quantize with a choice of block size and of how the
+ * E4M3 block scale is picked.
+ *  block         8, 16 or 32 values per E4M3 scale along cols ("NVIDIA NVFP4 与
+ *                Micro-Scaling" article, section 3.1 table: smaller blocks restore
+ *                local range better at a higher scale overhead); scales is
+ *                [rows, ceil(cols/block)].
+ *  scale_search  0: the amax rule of nvfp4_quantize (code0 = E4M3(t)).  W > 0: the
+ *                bytes code0 + d, d = -1, +1, -2, +2, ..., -W, +W inside 0..126, are
+ *                tried in that order, and one replaces the current choice only when
+ *                its float32 squared error is strictly smaller (NVIDIA "Introducing
+ *                NVFP4" blog, 高精度缩放: the E4M3 scale can be the one that makes the
+ *                block's summed error smallest).  The error of byte c, in float32
+ *                with s_b = s_global * E4M3(c), r = 1 / s_b (0 if s_b == 0):
+ *                  E = sum over the block, in index order, of (x_i - s_b * E2M1(x_i * r))^2
+ *                each product, difference, square and sum rounded to float32.
+ *                0 <= W <= FP4_MAX_SCALE_SEARCH.
+ * Everything else (global amax, element encode, outputs, workspace) as
+ * nvfp4_quantize; block 16 with scale_search 0 is nvfp4_quantize.  An invalid
+ * block or scale_search returns FP4_ERR_SHAPE.
+ */
+fp4_status nvfp4_quantize_ex(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, int block,
+                             int scale_search, uint8_t* q, uint8_t* scales, float* global_amax,
+                             int amax_given, float* global_scale, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 /*
  * mxfp4_quantize -- MXFP4: E2M1 values with one E8M0 power-of-two scale per 32
  * values and no tensor scale (10100.com data-type article, "mxFP4的技术局限";
@@ -111,6 +140,15 @@ fp4_status mxfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t col
 fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* q, const uint8_t* scales,
                           const float* global_scale, int64_t rows, int64_t cols,
                           void* y, fp4_dtype yt, hipStream_t stream);
+
+/*
+ * nvfp4_dequantize_ex -- fp4_dequantize of NVFP4 data written by
+ * nvfp4_quantize_ex with blocks of `block` (8, 16 or 32) values: scales is
+ * [rows, ceil(cols/block)].  An invalid block returns FP4_ERR_SHAPE.
+ */
+fp4_status nvfp4_dequantize_ex(const uint8_t* q, const uint8_t* scales, const float* global_scale,
+                               int64_t rows, int64_t cols, int block, void* y, fp4_dtype yt,
+                               hipStream_t stream);
 
 /*
  * fp4_scaled_gemm -- D = g_d * ((g_a s_a . A) @ (g_b s_b . W)^T), fp32 accumulate.

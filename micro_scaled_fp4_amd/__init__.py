@@ -34,6 +34,11 @@ _c_p = ctypes.c_void_p
 SIGNATURES = {
     "nvfp4_quantize": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p,
                                       ctypes.c_int, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "nvfp4_quantize_ex": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, ctypes.c_int,
+                                         ctypes.c_int, _c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_p,
+                                         ctypes.c_size_t, _c_p]),
+    "nvfp4_dequantize_ex": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, ctypes.c_int, _c_p,
+                                           ctypes.c_int, _c_p]),
     "mxfp4_quantize": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "fp4_dequantize": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p,
                                       ctypes.c_int, _c_p]),
@@ -148,6 +153,31 @@ def nvfp4_quantize(x: torch.Tensor, amax=None, workspace: Optional[torch.Tensor]
     return q, sc, a, g_scale
 
 
+def nvfp4_quantize_ex(x: torch.Tensor, block: int = NV_BLOCK, scale_search: int = 0, amax=None,
+                      workspace: Optional[torch.Tensor] = None):
+    """nvfp4_quantize with `block` (8, 16, 32) values per E4M3 scale and an
+    optional least-squared-error search over +-scale_search scale bytes.
+    Returns (codes, scales [rows, ceil(cols/block)], amax f32[1], s_global f32[1])."""
+    x = _gpu_2d(x, "x")
+    dev = x.device
+    rows, cols = x.shape
+    q = torch.empty((rows, (cols + 1) // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((rows, (cols + block - 1) // block), dtype=torch.uint8, device=dev)
+    g_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    a = _amax_arg(amax, dev)
+    given = a is not None
+    if not given:
+        a = torch.empty(1, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(AMAX_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    st = load_library().nvfp4_quantize_ex(
+        _ptr(x), _dtype_code(x.dtype), rows, cols, int(block), int(scale_search), _ptr(q), _ptr(sc),
+        _ptr(a), int(given), _ptr(g_scale), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "nvfp4_quantize_ex")
+    return q, sc, a, g_scale
+
+
 def mxfp4_quantize(x: torch.Tensor):
     """x [rows, cols] -> (codes u8 [rows, ceil(cols/2)], scales u8 [rows, ceil(cols/32)] E8M0)."""
     x = _gpu_2d(x, "x")
@@ -173,6 +203,21 @@ def fp4_dequantize(fmt: int, q: torch.Tensor, scales: torch.Tensor, global_scale
     st = load_library().fp4_dequantize(fmt, _ptr(q), _ptr(scales), _ptr(gs), rows, cols, _ptr(y),
                                        _dtype_code(out_dtype), _stream(dev))
     _check(st, "fp4_dequantize")
+    return y
+
+
+def nvfp4_dequantize_ex(q: torch.Tensor, scales: torch.Tensor, global_scale, cols: int,
+                        block: int = NV_BLOCK, out_dtype: torch.dtype = torch.float32):
+    """fp4_dequantize of NVFP4 data with `block` values per scale."""
+    q = _gpu_2d(q, "q")
+    scales = _gpu_2d(scales, "scales")
+    dev = q.device
+    rows = q.shape[0]
+    y = torch.empty((rows, cols), dtype=out_dtype, device=dev)
+    gs = global_scale.reshape(1).contiguous()
+    st = load_library().nvfp4_dequantize_ex(_ptr(q), _ptr(scales), _ptr(gs), rows, cols, int(block),
+                                            _ptr(y), _dtype_code(out_dtype), _stream(dev))
+    _check(st, "nvfp4_dequantize_ex")
     return y
 
 

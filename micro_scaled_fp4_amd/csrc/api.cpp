@@ -69,6 +69,25 @@ fp4_status check_quant_args(const void* x, fp4_dtype xt, int64_t rows, int64_t c
   return FP4_OK;
 }
 
+fp4_status dequantize_blocks(fp4_format fmt, int block, const uint8_t* q,
+                                    const uint8_t* scales, const float* global_scale, int64_t rows,
+                                    int64_t cols, void* y, fp4_dtype yt, hipStream_t stream) {
+  if (fmt != FP4_NVFP4 && fmt != FP4_MXFP4) return FP4_ERR_DTYPE;
+  if (!valid_dtype(yt)) return FP4_ERR_DTYPE;
+  if (rows < 0 || cols < 0) return FP4_ERR_SHAPE;
+  if (fmt == FP4_MXFP4 && global_scale != nullptr) return FP4_ERR_DTYPE;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (q == nullptr || scales == nullptr || y == nullptr) return FP4_ERR_NULL;
+  if (fmt == FP4_NVFP4 && global_scale == nullptr) return FP4_ERR_NULL;
+  if (!aligned(y, yt == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+  fp4_status st = check_arch();
+  if (st != FP4_OK) return st;
+  FP4_TRY_LAUNCH(fp4impl::launch_dequant(fmt == FP4_MXFP4, q, scales, global_scale, rows, cols, y,
+                                         yt == FP4_BF16, stream, block),
+                 "fp4_dequantize");
+  return FP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +111,16 @@ const char* fp4_last_hip_error(void) { return g_last_hip_error; }
 fp4_status nvfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, uint8_t* q,
                           uint8_t* scales, float* global_amax, int amax_given, float* global_scale,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return nvfp4_quantize_ex(x, xt, rows, cols, 16, 0, q, scales, global_amax, amax_given,
+                           global_scale, workspace, workspace_bytes, stream);
+}
+
+fp4_status nvfp4_quantize_ex(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, int block,
+                             int scale_search, uint8_t* q, uint8_t* scales, float* global_amax,
+                             int amax_given, float* global_scale, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (block != 8 && block != 16 && block != 32) return FP4_ERR_SHAPE;
+  if (scale_search < 0 || scale_search > FP4_MAX_SCALE_SEARCH) return FP4_ERR_SHAPE;
   fp4_status st = check_quant_args(x, xt, rows, cols, q, scales, global_amax, amax_given,
                                    global_scale, workspace, workspace_bytes);
   if (st != FP4_OK) return st;
@@ -112,7 +141,8 @@ fp4_status nvfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t col
   }
   FP4_TRY_LAUNCH(fp4impl::launch_nv_quant(x, bf16, rows, cols, q, scales,
                                           amax_given ? global_amax : nullptr, partials, npart,
-                                          amax_given ? nullptr : global_amax, global_scale, stream),
+                                          amax_given ? nullptr : global_amax, global_scale, stream,
+                                          block, scale_search),
                  "nvfp4_quantize/encode");
   return FP4_OK;
 }
@@ -134,21 +164,16 @@ fp4_status mxfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t col
 fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* q, const uint8_t* scales,
                           const float* global_scale, int64_t rows, int64_t cols, void* y,
                           fp4_dtype yt, hipStream_t stream) {
-  if (fmt != FP4_NVFP4 && fmt != FP4_MXFP4) return FP4_ERR_DTYPE;
-  if (!valid_dtype(yt)) return FP4_ERR_DTYPE;
-  if (rows < 0 || cols < 0) return FP4_ERR_SHAPE;
-  if (fmt == FP4_MXFP4 && global_scale != nullptr) return FP4_ERR_DTYPE;
-  if (rows == 0 || cols == 0) return FP4_OK;
-  if (q == nullptr || scales == nullptr || y == nullptr) return FP4_ERR_NULL;
-  if (fmt == FP4_NVFP4 && global_scale == nullptr) return FP4_ERR_NULL;
-  if (!aligned(y, yt == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
-  fp4_status st = check_arch();
-  if (st != FP4_OK) return st;
-  FP4_TRY_LAUNCH(fp4impl::launch_dequant(fmt == FP4_MXFP4, q, scales, global_scale, rows, cols, y,
-                                         yt == FP4_BF16, stream),
-                 "fp4_dequantize");
-  return FP4_OK;
+  return dequantize_blocks(fmt, 16, q, scales, global_scale, rows, cols, y, yt, stream);
 }
+
+fp4_status nvfp4_dequantize_ex(const uint8_t* q, const uint8_t* scales, const float* global_scale,
+                               int64_t rows, int64_t cols, int block, void* y, fp4_dtype yt,
+                               hipStream_t stream) {
+  if (block != 8 && block != 16 && block != 32) return FP4_ERR_SHAPE;
+  return dequantize_blocks(FP4_NVFP4, block, q, scales, global_scale, rows, cols, y, yt, stream);
+}
+
 
 fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
                            const float* g_a, const uint8_t* W, const uint8_t* w_scales,

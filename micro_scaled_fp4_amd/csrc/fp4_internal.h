@@ -18,16 +18,20 @@ hipError_t launch_amax(const void* x, bool bf16, int64_t n, uint32_t* partials, 
                        hipStream_t stream);
 
 // NVFP4 quantize.  Exactly one of (amax_in) or (partials, npart) gives G.
+// block: 8, 16 or 32 values per E4M3 scale; window > 0: the scale byte is
+// searched over +-window codes around the amax rule's (least squared error).
 hipError_t launch_nv_quant(const void* x, bool bf16, int64_t rows, int64_t cols, uint8_t* q,
                            uint8_t* scales, const float* amax_in, const uint32_t* partials,
-                           int npart, float* amax_out, float* scale_out, hipStream_t stream);
+                           int npart, float* amax_out, float* scale_out, hipStream_t stream,
+                           int block = 16, int window = 0);
 
 hipError_t launch_mx_quant(const void* x, bool bf16, int64_t rows, int64_t cols, uint8_t* q,
                            uint8_t* scales, hipStream_t stream);
 
+// block: NVFP4 values per scale (8, 16, 32); MXFP4 always 32.
 hipError_t launch_dequant(bool mx, const uint8_t* q, const uint8_t* scales,
                           const float* global_scale, int64_t rows, int64_t cols, void* y,
-                          bool bf16_out, hipStream_t stream);
+                          bool bf16_out, hipStream_t stream, int block = 16);
 
 // Writes G = 0 and s_global = 1 (empty tensors).
 hipError_t launch_empty_scales(float* amax_out, float* scale_out, hipStream_t stream);

@@ -161,13 +161,101 @@ __global__ void __launch_bounds__(kThreads) k_amax_scalar(const void* __restrict
 }
 
 // ------------------------------------------------------------ NV quantize --
-template <bool BF16>
+// Float32 squared error of encoding block v with scale s_b (multiplier r =
+// 1/s_b, or 0 when s_b is 0): E = sum_i fl(fl(v_i - fl(s_b * E2M1(v_i * r)))^2),
+// added in index order.  The scale search compares candidates by it.
+template <int N>
+__device__ __forceinline__ float block_sq_error(const float (&v)[N], float s_b, float r) {
+  float E = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i += 2) {
+    const uint32_t c = e2m1_pack2<0>(0u, v[i] * r, v[i + 1] * r);
+    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);   // exact E2M1 values
+    const float e0 = v[i] - s_b * d.x, e1 = v[i + 1] - s_b * d.y;
+    E = E + e0 * e0;
+    E = E + e1 * e1;
+  }
+  return E;
+}
+
+// E4M3 scale search ([NV] "高精度缩放": the block scale can be the one that
+// makes the block's summed error smallest).  On entry code / r hold the amax
+// rule's choice code0; the candidates code0 + d, d = -1, +1, ..., -W, +W, inside
+// 0..126, replace the current choice only when their error is strictly smaller.
+template <int N>
+__device__ __forceinline__ void nv_search_scale(const float (&v)[N], float s_global, int window,
+                                                uint32_t& code, float& r) {
+  const int c0 = (int)code;
+  float best = block_sq_error(v, s_global * e4m3_value(code), r);
+  for (int d = 1; d <= window; ++d) {
+#pragma unroll
+    for (int sgn = -1; sgn <= 1; sgn += 2) {
+      const int c = c0 + sgn * d;
+      if (c < 0 || c > 126) continue;
+      const float sb = s_global * e4m3_value((uint32_t)c);
+      const float rc = sb != 0.0f ? 1.0f / sb : 0.0f;
+      const float E = block_sq_error(v, sb, rc);
+      if (E < best) {
+        best = E;
+        code = (uint32_t)c;
+        r = rc;
+      }
+    }
+  }
+}
+
+// max|x| of a block held as VPB raw 16-byte vectors (bf16 or float32).
+template <bool BF16, int VPB>
+__device__ __forceinline__ float raw_amax(const u32x4 (&w)[VPB]) {
+  if (BF16) {
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int k = 0; k < VPB; ++k) {
+      m = pkmax_abs(m, w[k].x);
+      m = pkmax_abs(m, w[k].y);
+      m = pkmax_abs(m, w[k].z);
+      m = pkmax_abs(m, w[k].w);
+    }
+    return __uint_as_float((uint32_t)(m.x > m.y ? m.x : m.y) << 16);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < VPB; ++k) {
+    m = umax(m, w[k].x & 0x7fffffffu);
+    m = umax(m, w[k].y & 0x7fffffffu);
+    m = umax(m, w[k].z & 0x7fffffffu);
+    m = umax(m, w[k].w & 0x7fffffffu);
+  }
+  return __uint_as_float(m);
+}
+
+// Packed codes of one block of BS values (value 2j in the low nibble of byte j).
+template <int BS>
+struct CodeVec;
+template <> struct CodeVec<8> { typedef uint32_t T; };
+template <> struct CodeVec<16> { typedef u32x2 T; };
+template <> struct CodeVec<32> { typedef u32x4 T; };
+
+template <int BS>
+__device__ __forceinline__ typename CodeVec<BS>::T pack_block(const float (&v)[BS]) {
+  if constexpr (BS == 8) {
+    return e2m1_pack8(v);
+  } else if constexpr (BS == 16) {
+    return u32x2{e2m1_pack8(v), e2m1_pack8(v + 8)};
+  } else {
+    return u32x4{e2m1_pack8(v), e2m1_pack8(v + 8), e2m1_pack8(v + 16), e2m1_pack8(v + 24)};
+  }
+}
+
+// One lane per block of BS values (8, 16 or 32) of a flat run of blocks.
+// SEARCH: the block scale comes from nv_search_scale over +-window codes.
+template <bool BF16, int BS, bool SEARCH>
 __global__ void __launch_bounds__(kThreads)
     k_nv_quant_fast(const void* __restrict__ x, int64_t nblk, uint8_t* __restrict__ q,
                     uint8_t* __restrict__ scales, const float* __restrict__ amax_in,
                     const uint32_t* __restrict__ partials, int npart, float* __restrict__ amax_out,
-                    float* __restrict__ scale_out, bool reverse) {
-  constexpr int VPB = BF16 ? 2 : 4;
+                    float* __restrict__ scale_out, bool reverse, int window) {
+  constexpr int VPB = BS * (BF16 ? 2 : 4) / 16;   // 16-byte vectors per block
   __shared__ u32x4 lds[VPB * (kThreads + 1)];
   const float G = resolve_amax(amax_in, partials, npart);
   const float s_global = nv_global_scale(G);
@@ -183,17 +271,39 @@ __global__ void __launch_bounds__(kThreads)
     u32x4 w[VPB];
     stage_blocks<VPB, kThreads>(xv, base, nb, lds, w);
     if ((int)threadIdx.x >= nb) continue;
-    float v[16];
-    if (BF16) unpack_bf16<16>(w, v); else unpack_f32<16>(w, v);
     uint32_t sc;
     float r;
-    nv_block_scale(amax_of(v), s_global, sc, r);
+    typename CodeVec<BS>::T codes;
+    if (SEARCH) {
+      float v[BS];
+      if (BF16) unpack_bf16<BS>(w, v); else unpack_f32<BS>(w, v);
+      nv_block_scale(amax_of(v), s_global, sc, r);
+      nv_search_scale(v, s_global, window, sc, r);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
+      for (int j = 0; j < BS; ++j) v[j] = v[j] * r;
+      codes = pack_block<BS>(v);
+    } else {
+      // block amax from the raw words (bf16: packed 16-bit max of the
+      // magnitudes, same order as the values), then 8 values at a time, so
+      // the block is never held in registers as float32 all at once
+      nv_block_scale(raw_amax<BF16, VPB>(w), s_global, sc, r);
+      uint32_t d[BS / 8];
+#pragma unroll
+      for (int k = 0; k < BS / 8; ++k) {
+        float v[8];
+        if (BF16) unpack_bf16<8>(w + k, v); else unpack_f32<8>(w + 2 * k, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = v[j] * r;
+        d[k] = e2m1_pack8(v);
+      }
+      if constexpr (BS == 8) codes = d[0];
+      else if constexpr (BS == 16) codes = u32x2{d[0], d[1]};
+      else codes = u32x4{d[0], d[1], d[2], d[3]};
+    }
     const int64_t b = base + threadIdx.x;
     // (non-temporal: written once, read by another kernel; ~6% faster than
     // stores that allocate in L2)
-    __builtin_nontemporal_store(u32x2{e2m1_pack8(v), e2m1_pack8(v + 8)}, reinterpret_cast<u32x2*>(q) + b);
+    __builtin_nontemporal_store(codes, reinterpret_cast<typename CodeVec<BS>::T*>(q) + b);
     __builtin_nontemporal_store((uint8_t)sc, scales + b);
   }
 }
@@ -205,31 +315,33 @@ __device__ __forceinline__ float load_elem(const void* x, int64_t idx) {
   return reinterpret_cast<const float*>(x)[idx];
 }
 
-template <bool BF16>
+template <bool BF16, int BS, bool SEARCH>
 __global__ void __launch_bounds__(kThreads)
     k_nv_quant_generic(const void* __restrict__ x, int64_t rows, int64_t cols,
                        uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
                        const float* __restrict__ amax_in, const uint32_t* __restrict__ partials,
-                       int npart, float* __restrict__ amax_out, float* __restrict__ scale_out) {
+                       int npart, float* __restrict__ amax_out, float* __restrict__ scale_out,
+                       int window) {
   const float G = resolve_amax(amax_in, partials, npart);
   const float s_global = nv_global_scale(G);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (amax_out) *amax_out = G;
     *scale_out = s_global;
   }
-  const int64_t bpr = (cols + 15) / 16, qstride = (cols + 1) / 2;
+  const int64_t bpr = (cols + BS - 1) / BS, qstride = (cols + 1) / 2;
   const int64_t total = rows * bpr;
   for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < total;
        t += (int64_t)gridDim.x * kThreads) {
     const int64_t r = t / bpr, j = t - r * bpr;
-    const int64_t c0 = j * 16;
-    const int len = (int)((cols - c0) < 16 ? (cols - c0) : 16);
-    float v[16];
+    const int64_t c0 = j * BS;
+    const int len = (int)((cols - c0) < BS ? (cols - c0) : BS);
+    float v[BS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = i < len ? load_elem<BF16>(x, r * cols + c0 + i) : 0.0f;
+    for (int i = 0; i < BS; ++i) v[i] = i < len ? load_elem<BF16>(x, r * cols + c0 + i) : 0.0f;
     uint32_t sc;
     float rr;
     nv_block_scale(amax_of(v), s_global, sc, rr);
+    if (SEARCH) nv_search_scale(v, s_global, window, sc, rr);
     uint8_t* qrow = q + r * qstride + c0 / 2;
     for (int i = 0; i < len; i += 2) {
       const uint32_t lo = e2m1_code(v[i] * rr);
@@ -356,12 +468,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 // One lane per 8 values (bf16 out, 16-byte store) or 4 values (float32 out,
 // 16-byte store).  `unit` indexes those groups over the flat tensor.
-template <bool MX, bool BF16OUT>
+template <bool MX, bool BF16OUT, int BS>
 __global__ void __launch_bounds__(kThreads)
     k_dequant_fast(const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
                    const float* __restrict__ global_scale, int64_t nunits, void* __restrict__ y) {
   constexpr int kVals = BF16OUT ? 8 : 4;
-  constexpr int kBlock = MX ? 32 : 16;
+  constexpr int kBlock = BS;
   const float s_global = MX ? 1.0f : *global_scale;
   for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < nunits;
        u += (int64_t)gridDim.x * kThreads) {
@@ -399,10 +511,9 @@ __global__ void __launch_bounds__(kThreads)
 
 template <bool BF16OUT>
 __global__ void __launch_bounds__(kThreads)
-    k_dequant_generic(bool mx, const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
-                      const float* __restrict__ global_scale, int64_t rows, int64_t cols,
-                      void* __restrict__ y) {
-  const int bs = mx ? 32 : 16;
+    k_dequant_generic(bool mx, int bs, const uint8_t* __restrict__ q,
+                      const uint8_t* __restrict__ scales, const float* __restrict__ global_scale,
+                      int64_t rows, int64_t cols, void* __restrict__ y) {
   const float s_global = mx ? 1.0f : *global_scale;
   const int64_t bpr = (cols + bs - 1) / bs, qstride = (cols + 1) / 2;
   const int64_t total = rows * cols;
@@ -440,6 +551,43 @@ inline int grid_for(int64_t work_items) {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+template <bool BF16, int BS, bool SEARCH>
+void nv_quant_launch(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scales,
+                     const float* amax_in, const uint32_t* partials, int npart, float* amax_out,
+                     float* scale_out, int window, hipStream_t stream) {
+  const bool fast = (cols % BS == 0) && aligned16(x) && aligned16(q);
+  if (fast) {
+    const int64_t nblk = rows * (cols / BS);
+    const bool reverse = kReverseAfterAmax && amax_in == nullptr;
+    hipLaunchKernelGGL((k_nv_quant_fast<BF16, BS, SEARCH>), dim3(grid_for(nblk)), dim3(kThreads), 0,
+                       stream, x, nblk, q, scales, amax_in, partials, npart, amax_out, scale_out,
+                       reverse, window);
+  } else {
+    hipLaunchKernelGGL((k_nv_quant_generic<BF16, BS, SEARCH>),
+                       dim3(grid_for(rows * ((cols + BS - 1) / BS))), dim3(kThreads), 0, stream, x,
+                       rows, cols, q, scales, amax_in, partials, npart, amax_out, scale_out, window);
+  }
+}
+
+template <bool BF16>
+hipError_t nv_quant_dispatch(const void* x, int64_t rows, int64_t cols, int block, int window,
+                             uint8_t* q, uint8_t* scales, const float* amax_in,
+                             const uint32_t* partials, int npart, float* amax_out,
+                             float* scale_out, hipStream_t stream) {
+#define FP4_NVQ(BS, S)                                                                       \
+  nv_quant_launch<BF16, BS, S>(x, rows, cols, q, scales, amax_in, partials, npart, amax_out, \
+                               scale_out, window, stream)
+  const bool search = window > 0;
+  switch (block) {
+    case 8: if (search) FP4_NVQ(8, true); else FP4_NVQ(8, false); break;
+    case 16: if (search) FP4_NVQ(16, true); else FP4_NVQ(16, false); break;
+    case 32: if (search) FP4_NVQ(32, true); else FP4_NVQ(32, false); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef FP4_NVQ
+  return hipGetLastError();
+}
+
 }  // namespace
 
 namespace fp4impl {
@@ -471,28 +619,12 @@ hipError_t launch_amax(const void* x, bool bf16, int64_t n, uint32_t* partials, 
 
 hipError_t launch_nv_quant(const void* x, bool bf16, int64_t rows, int64_t cols, uint8_t* q,
                            uint8_t* scales, const float* amax_in, const uint32_t* partials,
-                           int npart, float* amax_out, float* scale_out, hipStream_t stream) {
-  const bool fast = (cols % 16 == 0) && aligned16(x) && aligned16(q);
-  if (fast) {
-    const int64_t nblk = rows * (cols / 16);
-    const bool reverse = kReverseAfterAmax && amax_in == nullptr;
-    const int g = grid_for(nblk);
-    if (bf16)
-      hipLaunchKernelGGL(k_nv_quant_fast<true>, dim3(g), dim3(kThreads), 0, stream, x, nblk, q,
-                         scales, amax_in, partials, npart, amax_out, scale_out, reverse);
-    else
-      hipLaunchKernelGGL(k_nv_quant_fast<false>, dim3(g), dim3(kThreads), 0, stream, x, nblk, q,
-                         scales, amax_in, partials, npart, amax_out, scale_out, reverse);
-  } else {
-    const int g = grid_for(rows * ((cols + 15) / 16));
-    if (bf16)
-      hipLaunchKernelGGL(k_nv_quant_generic<true>, dim3(g), dim3(kThreads), 0, stream, x, rows,
-                         cols, q, scales, amax_in, partials, npart, amax_out, scale_out);
-    else
-      hipLaunchKernelGGL(k_nv_quant_generic<false>, dim3(g), dim3(kThreads), 0, stream, x, rows,
-                         cols, q, scales, amax_in, partials, npart, amax_out, scale_out);
-  }
-  return hipGetLastError();
+                           int npart, float* amax_out, float* scale_out, hipStream_t stream,
+                           int block, int window) {
+  return bf16 ? nv_quant_dispatch<true>(x, rows, cols, block, window, q, scales, amax_in, partials,
+                                        npart, amax_out, scale_out, stream)
+              : nv_quant_dispatch<false>(x, rows, cols, block, window, q, scales, amax_in,
+                                         partials, npart, amax_out, scale_out, stream);
 }
 
 hipError_t launch_mx_quant(const void* x, bool bf16, int64_t rows, int64_t cols, uint8_t* q,
@@ -521,28 +653,33 @@ hipError_t launch_mx_quant(const void* x, bool bf16, int64_t rows, int64_t cols,
 
 hipError_t launch_dequant(bool mx, const uint8_t* q, const uint8_t* scales,
                           const float* global_scale, int64_t rows, int64_t cols, void* y,
-                          bool bf16_out, hipStream_t stream) {
-  const int bs = mx ? 32 : 16;
+                          bool bf16_out, hipStream_t stream, int block) {
+  const int bs = mx ? 32 : block;
+  if (bs != 8 && bs != 16 && bs != 32) return hipErrorInvalidValue;
   const bool fast = (cols % bs == 0) && aligned16(q) && aligned16(y);
   if (fast) {
     const int64_t nunits = rows * cols / (bf16_out ? 8 : 4);
     const int g = grid_for(nunits);
-#define FP4_DEQ_LAUNCH(M, B)                                                                    \
-  hipLaunchKernelGGL((k_dequant_fast<M, B>), dim3(g), dim3(kThreads), 0, stream, q, scales,     \
+#define FP4_DEQ_LAUNCH(M, B, S)                                                                 \
+  hipLaunchKernelGGL((k_dequant_fast<M, B, S>), dim3(g), dim3(kThreads), 0, stream, q, scales,  \
                      global_scale, nunits, y)
     if (mx) {
-      if (bf16_out) FP4_DEQ_LAUNCH(true, true); else FP4_DEQ_LAUNCH(true, false);
+      if (bf16_out) FP4_DEQ_LAUNCH(true, true, 32); else FP4_DEQ_LAUNCH(true, false, 32);
+    } else if (bs == 16) {
+      if (bf16_out) FP4_DEQ_LAUNCH(false, true, 16); else FP4_DEQ_LAUNCH(false, false, 16);
+    } else if (bs == 8) {
+      if (bf16_out) FP4_DEQ_LAUNCH(false, true, 8); else FP4_DEQ_LAUNCH(false, false, 8);
     } else {
-      if (bf16_out) FP4_DEQ_LAUNCH(false, true); else FP4_DEQ_LAUNCH(false, false);
+      if (bf16_out) FP4_DEQ_LAUNCH(false, true, 32); else FP4_DEQ_LAUNCH(false, false, 32);
     }
 #undef FP4_DEQ_LAUNCH
   } else {
     const int g = grid_for(rows * cols);
     if (bf16_out)
-      hipLaunchKernelGGL(k_dequant_generic<true>, dim3(g), dim3(kThreads), 0, stream, mx, q,
+      hipLaunchKernelGGL(k_dequant_generic<true>, dim3(g), dim3(kThreads), 0, stream, mx, bs, q,
                          scales, global_scale, rows, cols, y);
     else
-      hipLaunchKernelGGL(k_dequant_generic<false>, dim3(g), dim3(kThreads), 0, stream, mx, q,
+      hipLaunchKernelGGL(k_dequant_generic<false>, dim3(g), dim3(kThreads), 0, stream, mx, bs, q,
                          scales, global_scale, rows, cols, y);
   }
   return hipGetLastError();
