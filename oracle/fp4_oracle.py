@@ -523,6 +523,50 @@ def hadamard_quantize(x: np.ndarray, group: int = HADAMARD_GROUP, rounding: str 
     return nvfp4_quantize(y, amax=amax, rounding=rounding, sr_bits=bits)
 
 
+def hadamard_quantize_mx(x: np.ndarray, group: int = HADAMARD_GROUP, rounding: str = "rne",
+                         seed: int = 0):
+    """FWHT rotation fused with MXFP4 quantization ([MS] section 4.1 rotation,
+    then mxfp4_quantize's E8M0 rule per 32 rotated values).  MXFP4 has no
+    tensor scale, so nothing waits for a global amax.  Stochastic rounding, when
+    selected, rounds q_i = y_i * 2^-e with the same 16-bit draws per flat
+    element index as hadamard_quantize.
+    Returns (packed codes [R, C/2], E8M0 bytes [R, C/32])."""
+    y = fwht_orthonormal(x, group)
+    if rounding == "rne":
+        return mxfp4_quantize(y)
+    if rounding != "sr":
+        raise ValueError(rounding)
+    R, C = y.shape
+    yb = _blocks(y, MX_BLOCK)
+    sbyte = e8m0_exponent(np.max(np.abs(yb), axis=-1).astype(F32))
+    inv = np.ldexp(F32(1.0), 127 - sbyte.astype(np.int32)).astype(F32)
+    q = (yb * inv[..., None]).astype(F32)
+    codes = sr_round(q, _blocks(sr_bits(R, C, seed), MX_BLOCK)).reshape(R, -1)[:, :C]
+    return pack_nibbles(codes), sbyte
+
+
+def rotated_fp4_linear(x: np.ndarray, W: np.ndarray, group: int = HADAMARD_GROUP,
+                       fmt: str = "nv"):
+    """A linear layer y = x @ W^T run through the FP4 GEMM with both operands
+    rotated along K ([MS] section 4.1: the rotation of the activations can be
+    absorbed into the adjacent weights, so (x H)(W H)^T = x H H^T W^T = x W^T
+    for orthonormal H): x H and W H are each quantized as hadamard_quantize
+    (fmt "nv") or hadamard_quantize_mx (fmt "mx") does (W H once, offline),
+    then multiplied exactly.  Returns (D_ref float64 [M, N], the tolerance
+    magnitude, the two quantized operands)."""
+    K = x.shape[1]
+    if fmt == "nv":
+        qx = hadamard_quantize(x, group)
+        qw = hadamard_quantize(W, group)
+        D, mag = scaled_gemm_ref(nv_operand_f64(qx[0], qx[1], qx[3], K),
+                                 nv_operand_f64(qw[0], qw[1], qw[3], K), 1.0)
+    else:
+        qx = hadamard_quantize_mx(x, group)
+        qw = hadamard_quantize_mx(W, group)
+        D, mag = scaled_gemm_ref(mx_operand_f64(qx[0], qx[1], K), mx_operand_f64(qw[0], qw[1], K), 1.0)
+    return D, mag, qx, qw
+
+
 # -------------------------------------------------------------- GEMM/GEMV ---
 def nv_operand_f64(packed, sbytes, g, cols: int) -> np.ndarray:
     """Exact float64 value of an NVFP4 operand: g * E4M3(s_b) * E2M1(v)."""

@@ -405,6 +405,78 @@ def test_hadamard_quantize_is_rotation_then_nvfp4():
     assert np.sqrt(np.mean((back - x) ** 2)) <= 0.2 * np.sqrt(np.mean(y ** 2))
 
 
+def test_rotation_invariant_of_a_linear_layer():
+    """(x H)(W H)^T = x W^T for orthonormal H ([MS] section 4.1: the rotation
+    is absorbed into the adjacent weights): exactly in float64 with scipy's
+    Hadamard matrix, and to float32 rounding with the oracle's FWHT."""
+    import scipy.linalg
+    Hb = scipy.linalg.hadamard(128) / math.sqrt(128)
+    H = np.kron(np.eye(4), Hb)                                   # block diagonal, K = 512
+    x = workloads.normal((16, 512), 19).astype(np.float64)
+    W = workloads.normal((24, 512), 20, std=0.02).astype(np.float64)
+    ref = x @ W.T
+    assert np.max(np.abs((x @ H) @ (W @ H).T - ref)) <= 1e-12 * np.max(np.abs(x)) * np.max(np.abs(W)) * 512
+    xr = o.fwht_orthonormal(x.astype(F32)).astype(np.float64)
+    wr = o.fwht_orthonormal(W.astype(F32)).astype(np.float64)
+    mag = np.abs(x) @ np.abs(W).T
+    assert np.all(np.abs(xr @ wr.T - x.astype(F32).astype(np.float64) @ W.astype(F32).astype(np.float64).T)
+                  <= 1e-5 * mag)
+
+
+def _outlier_inputs():
+    """Three outlier patterns: 5 channels x40 of N(0,1), Student-t(2) entries,
+    and 0.5% random entries x50."""
+    rng = np.random.default_rng(21)
+    a = workloads.normal((96, 1024), 21)
+    workloads.with_outlier_channels(a, 5, 40.0, 21)
+    b = rng.standard_t(2, (96, 1024)).astype(F32)
+    c = rng.standard_normal((96, 1024))
+    c[rng.random((96, 1024)) < 0.005] *= 50
+    return [a.astype(F32), b, c.astype(F32)]
+
+
+def _rel(a, ref):
+    return np.linalg.norm(np.asarray(a, np.float64) - ref) / np.linalg.norm(ref)
+
+
+def test_rotation_lowers_mxfp4_error_on_outliers():
+    """[MS] section 4.1: rotation spreads the outlier energy over the channels
+    so a block's absmax is no longer set by one outlier.  With MXFP4's
+    power-of-two scales per 32 values this lowers the quantization error of
+    the rotated tensor (an orthonormal rotation keeps error norms), and the
+    rotated FP4 linear layer is closer to x W^T."""
+    W = o.bf16_bits_to_f32(workloads.gemm_w(64, 1024, seed=22))
+    for x in _outlier_inputs():
+        q, s = o.mxfp4_quantize(x)
+        e_plain = _rel(o.mxfp4_dequantize(q, s, 1024), x)
+        y = o.fwht_orthonormal(x)
+        qr, sr = o.hadamard_quantize_mx(x)
+        e_rot = _rel(o.mxfp4_dequantize(qr, sr, 1024), y.astype(np.float64))
+        assert e_rot < 0.85 * e_plain, (e_rot, e_plain)
+        exact = x.astype(np.float64) @ W.astype(np.float64).T
+        D_rot, _, _, _ = o.rotated_fp4_linear(x, W, fmt="mx")
+        qw, sw = o.mxfp4_quantize(W)
+        D_plain, _ = o.scaled_gemm_ref(o.mx_operand_f64(q, s, 1024), o.mx_operand_f64(qw, sw, 1024), 1.0)
+        assert _rel(D_rot, exact) < _rel(D_plain, exact)
+
+
+def test_hadamard_quantize_mx_is_rotation_then_mxfp4():
+    x = workloads.normal((16, 512), 23)
+    q, s = o.hadamard_quantize_mx(x)
+    q2, s2 = o.mxfp4_quantize(o.fwht_orthonormal(x))
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    # stochastic rounding: grid values never move, and the codes average to q
+    qs, ss = o.hadamard_quantize_mx(x, rounding="sr", seed=5)
+    assert np.array_equal(ss, s)
+    y = o.fwht_orthonormal(x)
+    inv = np.ldexp(1.0, 127 - np.repeat(s.astype(np.int64), 32, axis=1))
+    v_sr = o.e2m1_decode(o.unpack_nibbles(qs, 512))
+    v_rne = o.e2m1_decode(o.unpack_nibbles(q, 512))
+    qv = y * inv
+    assert np.all(np.abs(v_sr - qv) <= np.abs(v_rne - qv) + 2.0)      # one grid step at most
+    assert abs(np.mean(v_sr - np.clip(qv, -6, 6))) < 0.01
+
+
 # ------------------------------------------------------ stochastic rounding --
 def test_philox_known_answers():
     for row in read_golden("philox4x32_10_kat.txt"):
