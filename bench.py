@@ -267,6 +267,8 @@ def main():
     del gw_bits
     wq_nv, wsc_nv, _, gw_nv = fp4.nvfp4_quantize(wt)
     wq_mx, wsc_mx = fp4.mxfp4_quantize(wt)
+    rotation_error = rotation_error_report(torch, fp4, bf16_from_bits(workloads.gemm_a(Mg, Kg)[:1024]),
+                                           wt, (wq_nv, wsc_nv, gw_nv), (wq_mx, wsc_mx))
     del wt
     Dg = torch.empty((Mg, Ng), dtype=torch.bfloat16, device=dev)
     flops = 2 * Mg * Ng * Kg
@@ -334,6 +336,28 @@ def main():
             assert st == 0, st
         ops.append(Op(f"hadamard_quantize_{nm}", had, nH, "GB/s", b_h, HBM_PEAK_GBS, "hbm",
                       "k_had_amax + k_had_quant", hsrc))
+
+    # rotation alone (offline W H, bf16 -> bf16) and rotation + MXFP4 (one pass)
+    yh = torch.empty((R_H, C_H), dtype=torch.bfloat16, device=dev)
+    qhm = torch.empty((R_H, C_H // 2), dtype=torch.uint8, device=dev)
+    shm = torch.empty((R_H, C_H // 32), dtype=torch.uint8, device=dev)
+
+    def had_rot(i):
+        st = lib.hadamard_rotate(P(xh_c[i]), fp4.FP4_BF16, R_H, C_H, 128, P(yh), fp4.FP4_BF16,
+                                 stream_of())
+        assert st == 0, st
+
+    def had_mx(i):
+        st = lib.hadamard_quantize_mx(P(xh_c[i]), fp4.FP4_BF16, R_H, C_H, 128, fp4.FP4_RNE,
+                                      ctypes.c_uint64(0), P(qhm), P(shm), stream_of())
+        assert st == 0, st
+
+    ops += [
+        Op("hadamard_rotate_bf16", had_rot, nH, "GB/s", eh * 4, HBM_PEAK_GBS, "hbm",
+           "k_had_rotate (FWHT-128 alone)", hsrc),
+        Op("hadamard_quantize_mx", had_mx, nH, "GB/s", eh * 2 + eh // 2 + eh // 32, HBM_PEAK_GBS,
+           "hbm", "k_had_quant_mx (FWHT-128 + MXFP4, one pass)", hsrc),
+    ]
 
     if only:
         ops = [op for op in ops if op.name in only]
@@ -441,6 +465,7 @@ def main():
             "avg_launch_us": enc["us_per_call"],
         },
         "components": comps,
+        "rotation_error": rotation_error,
         "context": {"device_copy_GBs_read_plus_write": round(copy_gbs, 1),
                     "note": "torch copy_ of 512 MiB, for reference against the 8 TB/s peak"},
         "setup_s": round(setup_s, 1),
@@ -449,6 +474,35 @@ def main():
     if not args.no_cpu_baseline and (not only or "nvfp4_quantize_dynamic" in only):
         result["cpu_baseline"] = cpu_baseline(xa, args.cpu_seconds, b_nv / elems)
     print(json.dumps(result), flush=True)
+
+
+def rotation_error_report(torch, fp4, x, w, w_nv, w_mx):
+    """Relative Frobenius error against x W^T (float32 product of the bf16
+    inputs) of the FP4 linear layer, unrotated and with both operands rotated
+    ((x H)(W H)^T = x W^T), for NVFP4 and MXFP4, on 1024 rows of the prefill
+    activations (outlier channels x40) and the full 28672 x 8192 weight.
+    Information only: not timed."""
+    K = x.shape[1]
+    exact = torch.mm(x.float(), w.float().t().contiguous()).double()
+    ref = float(exact.norm())
+
+    def rel(D):
+        return round(float((D.double() - exact).norm()) / ref, 5)
+
+    def gemm(fmt, a, w_ops):
+        if fmt == fp4.FP4_NVFP4:
+            return fp4.fp4_scaled_gemm(fmt, a[0], a[1], a[3], w_ops[0], w_ops[1], w_ops[2], K, 1.0,
+                                       torch.float32)
+        return fp4.fp4_scaled_gemm(fmt, a[0], a[1], None, w_ops[0], w_ops[1], None, K, 1.0,
+                                   torch.float32)
+
+    out = {"shape": [x.shape[0], w.shape[0], K]}
+    out["nvfp4_plain"] = rel(gemm(fp4.FP4_NVFP4, fp4.nvfp4_quantize(x), w_nv))
+    rw = fp4.hadamard_quantize(w)
+    out["nvfp4_rotated"] = rel(gemm(fp4.FP4_NVFP4, fp4.hadamard_quantize(x), (rw[0], rw[1], rw[3])))
+    out["mxfp4_plain"] = rel(gemm(fp4.FP4_MXFP4, fp4.mxfp4_quantize(x), w_mx))
+    out["mxfp4_rotated"] = rel(gemm(fp4.FP4_MXFP4, fp4.hadamard_quantize_mx(x), fp4.hadamard_quantize_mx(w)))
+    return out
 
 
 def cpu_baseline(xa, seconds, bytes_per_elem):

@@ -251,6 +251,36 @@ fp4_status hadamard_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t 
                              float* global_amax, int amax_given, float* global_scale,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * hadamard_quantize_mx -- the rotation of hadamard_quantize, then MXFP4 as
+ * mxfp4_quantize does (E8M0 per 32 rotated values, no tensor scale).  The
+ * article of hadamard_quantize (section 4.1) rotates so that a block's absmax is
+ * no longer set by one outlier channel; MXFP4's power-of-two block scales gain
+ * from that, and the rotation can be absorbed into the adjacent layer's
+ * weights: the GEMM of hadamard_quantize_mx(x) and hadamard_quantize_mx(W)
+ * approximates x W^T, since (x H)(W H)^T = x W^T.
+ *   mode FP4_SR: element codes of q = y * 2^-e rounded stochastically with the
+ *   random bits of hadamard_quantize (same seed and element index -> same bits).
+ *   q out [rows, cols/2]; scales out [rows, cols/32] E8M0 bytes.
+ * One pass (no global amax, no workspace).  cols % group == 0, group == 128;
+ * x and q 16-byte aligned (FP4_ERR_ALIGN).  rows == 0 or cols == 0 is a no-op.
+ */
+fp4_status hadamard_quantize_mx(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, int group,
+                                fp4_rounding mode, uint64_t seed, uint8_t* q, uint8_t* scales,
+                                hipStream_t stream);
+
+/*
+ * hadamard_rotate -- y = x H for every `group` (= 128) contiguous channels,
+ * the rotation of hadamard_quantize alone (same float32 steps), so that a
+ * weight can be rotated once, offline, and stored (W H), or H absorbed into a
+ * neighbouring layer (article of hadamard_quantize, section 4.1).
+ *   x [rows, cols] FP4_F32 or FP4_BF16;  y out [rows, cols] FP4_F32 or FP4_BF16
+ *   (nearest-even from the float32 result).  cols % group == 0, group == 128,
+ *   x and y 16-byte aligned.  rows == 0 or cols == 0 is a no-op.
+ */
+fp4_status hadamard_rotate(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, int group,
+                           void* y, fp4_dtype yt, hipStream_t stream);
+
 /* Human-readable text of a status (static storage). */
 const char* fp4_status_string(fp4_status s);
 

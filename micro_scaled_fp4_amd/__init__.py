@@ -55,6 +55,10 @@ SIGNATURES = {
     "hadamard_quantize": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_uint64, _c_p, _c_p, _c_p,
                                          ctypes.c_int, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "hadamard_quantize_mx": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_uint64, _c_p, _c_p, _c_p]),
+    "hadamard_rotate": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, ctypes.c_int, _c_p,
+                                       ctypes.c_int, _c_p]),
     "fp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp4_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -325,3 +329,28 @@ def hadamard_quantize(x: torch.Tensor, group: int = 128, mode: int = FP4_RNE, se
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st, "hadamard_quantize")
     return q, sc, a, g_scale
+
+
+def hadamard_quantize_mx(x: torch.Tensor, group: int = 128, mode: int = FP4_RNE, seed: int = 0):
+    """FWHT over 128-channel groups fused with MXFP4 quantization (RNE or SR).
+    Returns (codes u8 [rows, cols/2], E8M0 bytes u8 [rows, cols/32])."""
+    x = _gpu_2d(x, "x")
+    dev = x.device
+    rows, cols = x.shape
+    q = torch.empty((rows, (cols + 1) // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((rows, (cols + MX_BLOCK - 1) // MX_BLOCK), dtype=torch.uint8, device=dev)
+    st = load_library().hadamard_quantize_mx(_ptr(x), _dtype_code(x.dtype), rows, cols, group, mode,
+                                             ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(q), _ptr(sc),
+                                             _stream(dev))
+    _check(st, "hadamard_quantize_mx")
+    return q, sc
+
+
+def hadamard_rotate(x: torch.Tensor, group: int = 128, out_dtype: torch.dtype = torch.float32):
+    """y = x H over 128-channel groups (orthonormal FWHT), float32 or bf16."""
+    x = _gpu_2d(x, "x")
+    y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    st = load_library().hadamard_rotate(_ptr(x), _dtype_code(x.dtype), x.shape[0], x.shape[1], group,
+                                        _ptr(y), _dtype_code(out_dtype), _stream(x.device))
+    _check(st, "hadamard_rotate")
+    return y

@@ -312,4 +312,36 @@ fp4_status hadamard_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t 
   return FP4_OK;
 }
 
+fp4_status hadamard_quantize_mx(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, int group,
+                                fp4_rounding mode, uint64_t seed, uint8_t* q, uint8_t* scales,
+                                hipStream_t stream) {
+  if (!valid_dtype(xt)) return FP4_ERR_DTYPE;
+  if (mode != FP4_RNE && mode != FP4_SR) return FP4_ERR_DTYPE;
+  if (group != 128 || rows < 0 || cols < 0 || cols % group != 0) return FP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (x == nullptr || q == nullptr || scales == nullptr) return FP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16)) return FP4_ERR_ALIGN;
+  fp4_status st = check_arch();
+  if (st != FP4_OK) return st;
+  FP4_TRY_LAUNCH(fp4impl::launch_hadamard_quant_mx(x, xt == FP4_BF16, rows, cols, mode == FP4_SR,
+                                                   seed, q, scales, stream),
+                 "hadamard_quantize_mx");
+  return FP4_OK;
+}
+
+fp4_status hadamard_rotate(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, int group,
+                           void* y, fp4_dtype yt, hipStream_t stream) {
+  if (!valid_dtype(xt) || !valid_dtype(yt)) return FP4_ERR_DTYPE;
+  if (group != 128 || rows < 0 || cols < 0 || cols % group != 0) return FP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (x == nullptr || y == nullptr) return FP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return FP4_ERR_ALIGN;
+  fp4_status st = check_arch();
+  if (st != FP4_OK) return st;
+  FP4_TRY_LAUNCH(fp4impl::launch_hadamard_rotate(x, xt == FP4_BF16, rows, cols, y, yt == FP4_BF16,
+                                                 stream),
+                 "hadamard_rotate");
+  return FP4_OK;
+}
+
 }  // extern "C"

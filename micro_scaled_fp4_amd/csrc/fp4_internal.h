@@ -44,6 +44,14 @@ hipError_t launch_hadamard_quant(const void* x, bool bf16, int64_t rows, int64_t
                                  const uint32_t* partials, int npart, float* amax_out,
                                  float* scale_out, hipStream_t stream);
 
+// y = x H per 128-channel group, float32 or bf16 (cols % 128 == 0, 16-byte aligned).
+hipError_t launch_hadamard_rotate(const void* x, bool bf16, int64_t rows, int64_t cols, void* y,
+                                  bool y_bf16, hipStream_t stream);
+// x H per 128-channel group, then MXFP4 (one pass; RNE or stochastic codes).
+hipError_t launch_hadamard_quant_mx(const void* x, bool bf16, int64_t rows, int64_t cols, bool sr,
+                                    uint64_t seed, uint8_t* q, uint8_t* scales,
+                                    hipStream_t stream);
+
 // ---- gemv.hip -------------------------------------------------------------
 // Writes n zeros of elem_bytes (4: float, 2: bf16, 1: E4M3) each to y: the result
 // of a contraction over K = 0.

@@ -274,6 +274,123 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// Writes the VPB vectors out[] of slot base + t (t = threadIdx.x < nb) to
+// dst through LDS, so each store instruction covers consecutive 16-byte
+// vectors (the inverse of chunk_deal's exchange).  Every thread must call it.
+template <int VPB, int NT>
+__device__ __forceinline__ void chunk_store(const u32x4 (&out)[VPB], int nb, u32x4* lds,
+                                            u32x4* __restrict__ dst, int64_t base) {
+  if ((int)threadIdx.x < nb) {
+#pragma unroll
+    for (int k = 0; k < VPB; ++k) lds[k * (NT + 1) + threadIdx.x] = out[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < VPB; ++k) {
+    const int i = threadIdx.x + NT * k;
+    if (i < VPB * nb)
+      __builtin_nontemporal_store(lds[(i % VPB) * (NT + 1) + i / VPB], dst + base * VPB + i);
+  }
+  __syncthreads();
+}
+
+// y = x H per 128-channel group (the rotation alone), float32 or bf16 out.
+template <bool BF16, bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads)
+    k_had_rotate(const void* __restrict__ x, int64_t nslots, void* __restrict__ y) {
+  constexpr int VPB = BF16 ? 4 : 8;
+  constexpr int VPO = OUT_BF16 ? 4 : 8;
+  __shared__ u32x4 lds[(VPB > VPO ? VPB : VPO) * (kThreads + 1)];
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  const int p = threadIdx.x & 3;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  auto chunk_nb = [&](int64_t b) { return (int)(nslots - b < kThreads ? nslots - b : kThreads); };
+  u32x4 raw[VPB];
+  int64_t base = (int64_t)blockIdx.x * kThreads;
+  if (base < nslots) chunk_load<VPB, kThreads>(xv, base, chunk_nb(base), raw);
+  for (; base < nslots; base += stride) {
+    const int nb = chunk_nb(base);
+    u32x4 w[VPB];
+    chunk_deal<VPB, kThreads>(raw, nb, lds, w);
+    if (base + stride < nslots) chunk_load<VPB, kThreads>(xv, base + stride, chunk_nb(base + stride), raw);
+    u32x4 out[VPO];
+    if ((int)threadIdx.x < nb) {
+      float v[kPer];
+      unpack32<BF16>(w, v);
+      fwht128(v, p);
+#pragma unroll
+      for (int k = 0; k < VPO; ++k) {
+        if (OUT_BF16) {
+          out[k] = u32x4{bf16_pack2(v[8 * k], v[8 * k + 1]), bf16_pack2(v[8 * k + 2], v[8 * k + 3]),
+                         bf16_pack2(v[8 * k + 4], v[8 * k + 5]), bf16_pack2(v[8 * k + 6], v[8 * k + 7])};
+        } else {
+          out[k] = u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                         __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
+        }
+      }
+    }
+    chunk_store<VPO, kThreads>(out, nb, lds, reinterpret_cast<u32x4*>(y), base);
+  }
+}
+
+// Rotation + MXFP4: the 32 rotated channels a lane holds are one MXFP4 block,
+// so there is no cross-lane work after the FWHT and no global amax (one pass).
+template <bool BF16, bool SR>
+__global__ void __launch_bounds__(kThreads)
+    k_had_quant_mx(const void* __restrict__ x, int64_t nslots, uint64_t seed,
+                   uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
+  constexpr int VPB = BF16 ? 4 : 8;
+  __shared__ u32x4 lds[VPB * (kThreads + 1)];
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  const int p = threadIdx.x & 3;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  auto chunk_nb = [&](int64_t b) { return (int)(nslots - b < kThreads ? nslots - b : kThreads); };
+  u32x4 raw[VPB];
+  int64_t base = (int64_t)blockIdx.x * kThreads;
+  if (base < nslots) chunk_load<VPB, kThreads>(xv, base, chunk_nb(base), raw);
+  for (; base < nslots; base += stride) {
+    const int nb = chunk_nb(base);
+    u32x4 wv[VPB];
+    chunk_deal<VPB, kThreads>(raw, nb, lds, wv);
+    if (base + stride < nslots) chunk_load<VPB, kThreads>(xv, base + stride, chunk_nb(base + stride), raw);
+    if ((int)threadIdx.x >= nb) continue;
+    const int64_t s = base + threadIdx.x;
+    float v[kPer];
+    unpack32<BF16>(wv, v);
+    fwht128(v, p);
+    uint32_t am = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
+    const uint32_t sc = e8m0_code(am);
+    const float inv = e8m0_inv(sc);
+    uint32_t w[4];
+#pragma unroll
+    for (int g8 = 0; g8 < 4; ++g8) {
+      float qv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[j] = v[8 * g8 + j] * inv;     // exact power-of-two multiply
+      if (SR) {
+        // elements 32 s + 8 g8 .. +7 share Philox counter 4 s + g8
+        const uint64_t g = (uint64_t)(4 * s + g8);
+        uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), 0u, 0u};
+        philox4x32_10(ctr, k0, k1);
+        uint32_t c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t u = (j & 1) ? (ctr[j >> 1] >> 16) : (ctr[j >> 1] & 0xffffu);
+          c[j] = e2m1_code_sr(qv[j], u);
+        }
+        w[g8] = pack8(c);
+      } else {
+        w[g8] = e2m1_pack8(qv);
+      }
+    }
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(q) + s);
+    __builtin_nontemporal_store((uint8_t)sc, scales + s);
+  }
+}
+
 inline int grid_for(int64_t slots) {
   int64_t g = (slots + kThreads - 1) / kThreads;
   if (g < 1) g = 1;
@@ -312,6 +429,38 @@ hipError_t launch_hadamard_quant(const void* x, bool bf16, int64_t rows, int64_t
     if (sr) FP4_HAD_LAUNCH(false, true); else FP4_HAD_LAUNCH(false, false);
   }
 #undef FP4_HAD_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard_rotate(const void* x, bool bf16, int64_t rows, int64_t cols, void* y,
+                                  bool y_bf16, hipStream_t stream) {
+  const int64_t nslots = rows * cols / kPer;
+  const int g = grid_for(nslots);
+#define FP4_ROT_LAUNCH(B, O) \
+  hipLaunchKernelGGL((k_had_rotate<B, O>), dim3(g), dim3(kThreads), 0, stream, x, nslots, y)
+  if (bf16) {
+    if (y_bf16) FP4_ROT_LAUNCH(true, true); else FP4_ROT_LAUNCH(true, false);
+  } else {
+    if (y_bf16) FP4_ROT_LAUNCH(false, true); else FP4_ROT_LAUNCH(false, false);
+  }
+#undef FP4_ROT_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard_quant_mx(const void* x, bool bf16, int64_t rows, int64_t cols, bool sr,
+                                    uint64_t seed, uint8_t* q, uint8_t* scales,
+                                    hipStream_t stream) {
+  const int64_t nslots = rows * cols / kPer;
+  const int g = grid_for(nslots);
+#define FP4_HMX_LAUNCH(B, S)                                                                     \
+  hipLaunchKernelGGL((k_had_quant_mx<B, S>), dim3(g), dim3(kThreads), 0, stream, x, nslots, seed, \
+                     q, scales)
+  if (bf16) {
+    if (sr) FP4_HMX_LAUNCH(true, true); else FP4_HMX_LAUNCH(true, false);
+  } else {
+    if (sr) FP4_HMX_LAUNCH(false, true); else FP4_HMX_LAUNCH(false, false);
+  }
+#undef FP4_HMX_LAUNCH
   return hipGetLastError();
 }
 
