@@ -593,6 +593,23 @@ def scaled_gemm_ref(A_hat: np.ndarray, W_hat: np.ndarray, g_d: float):
     return D, mag
 
 
+def grouped_gemm_ref(A_hat: np.ndarray, W_hat: np.ndarray, offsets, g_d: float):
+    """Grouped GEMM (one launch over E GEMMs, e.g. the experts of an MoE layer;
+    [MS] section 6.1 names MoE expert weights as the NVFP4 candidates): rows
+    offsets[e] .. offsets[e+1] of A_hat [M, K] times W_hat[e] [N, K] transposed,
+    each exactly as scaled_gemm_ref.  Rows outside every group stay NaN (not
+    written).  Returns (D [M, N], magnitude [M, N]) in float64."""
+    A_hat = np.asarray(A_hat, dtype=F64)
+    E, N, _ = W_hat.shape
+    D = np.full((A_hat.shape[0], N), np.nan)
+    mag = np.full((A_hat.shape[0], N), np.nan)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            D[lo:hi], mag[lo:hi] = scaled_gemm_ref(A_hat[lo:hi], W_hat[e], g_d)
+    return D, mag
+
+
 GEMM_REL_TOL = 1e-5            # |D - D_ref| <= 1e-5 * |g_d| * sum |a*b|
 BF16_UNIT_ROUNDOFF = 2.0 ** -8
 

@@ -690,3 +690,29 @@ def test_scale_variants_error_ordering():
         assert mse[8, W] < mse[16, W] < mse[32, W]
     for bs in (8, 16, 32):
         assert mse[bs, 3] < mse[bs, 1] < mse[bs, 0]
+
+
+# ----------------------------------------------------------- grouped GEMM ---
+def test_grouped_gemm_equals_block_diagonal_product():
+    """Grouped GEMM against a different formulation: one dense product with
+    every group's weights side by side, A_hat @ [W_0; W_1; ...]^T, then for each
+    row the N columns of its group.  Empty groups and a single group included."""
+    rng = np.random.default_rng(31)
+    E, N, K = 5, 24, 64
+    sizes = [3, 0, 17, 1, 9]
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    M = int(offs[-1])
+    A = rng.standard_normal((M, K))
+    W = rng.standard_normal((E, N, K))
+    D, mag = o.grouped_gemm_ref(A, W, offs, -1.5)
+    full = -1.5 * A @ W.reshape(E * N, K).T
+    grp = np.repeat(np.arange(E), sizes)
+    want = full.reshape(M, E, N)[np.arange(M), grp]
+    assert np.allclose(D, want, rtol=1e-12, atol=1e-12)
+    mag_full = 1.5 * np.abs(A) @ np.abs(W.reshape(E * N, K)).T
+    assert np.allclose(mag, mag_full.reshape(M, E, N)[np.arange(M), grp], rtol=1e-12)
+    D1, _ = o.grouped_gemm_ref(A, W[:1], [0, M], 2.0)
+    assert np.allclose(D1, 2.0 * A @ W[0].T, rtol=1e-12, atol=1e-12)
+    # rows outside every group are not written
+    Dp, _ = o.grouped_gemm_ref(A, W, [0, 2, 2, 5, 5, 20], 1.0)
+    assert np.all(np.isnan(Dp[20:])) and not np.any(np.isnan(Dp[:20]))
