@@ -14,6 +14,8 @@ workload's shape:
   prefill GEMM 8192 x 28672 x 8192, NVFP4 and MXFP4 operands, bf16 output;
                NVFP4 again with the output requantized in the epilogue to FP8 E4M3,
                and to NVFP4 at a given (calibrated) amax
+  MoE          grouped GEMM, 64 experts x (N 2048, K 7168), 32768 routed rows with
+               uneven expert loads, NVFP4, bf16 output, one launch
   rotate       16384x8192 bf16, 16 outlier channels x60: FWHT-128 + NVFP4, RNE and SR
 Each call kind is captured in its own HIP graph of R back-to-back calls that
 cycle through input copies totalling >= 1 GiB (more than the 256 MiB Infinity
@@ -315,6 +317,40 @@ def main():
            "mfma", "k_gemm<NV, NVFP4 out> (output requantized to NVFP4 at a given amax)", msrc),
     ]
 
+    # ------------------------------------------------------ MoE grouped GEMM --
+    # 64 experts with N = 2048, K = 7168 (one launch); 32768 routed rows
+    # (4096 tokens x top-8) with uneven expert loads; NVFP4, bf16 output
+    E_m, N_m, K_m = 64, 2048, 7168
+    sizes_m = workloads.moe_group_sizes(E_m, 32768)
+    M_m = sum(sizes_m)
+    am_bits = workloads.gemm_a(M_m, K_m, seed=workloads.SEED_MOE)
+    aq_m, as_m, _, ga_m = fp4.nvfp4_quantize(bf16_from_bits(am_bits))
+    del am_bits
+    # 8 distinct expert weights (N(0, 0.02^2), each quantized with its own
+    # tensor scale), stored 8 times over: the values do not change the work
+    wq_m = torch.empty((E_m * N_m, K_m // 2), dtype=torch.uint8, device=dev)
+    ws_m = torch.empty((E_m * N_m, K_m // 16), dtype=torch.uint8, device=dev)
+    gb_m = torch.empty(E_m, dtype=torch.float32, device=dev)
+    for e8 in range(8):
+        wt8 = bf16_from_bits(workloads.gemm_w(N_m, K_m, seed=workloads.SEED_MOE + 1 + e8))
+        q, sc, _, g = fp4.nvfp4_quantize(wt8)
+        for e in range(e8, E_m, 8):
+            wq_m[e * N_m:(e + 1) * N_m] = q
+            ws_m[e * N_m:(e + 1) * N_m] = sc
+            gb_m[e] = g[0]
+        del wt8
+    offs_m = torch.tensor([0] + list(np.cumsum(sizes_m)), dtype=torch.int32, device=dev)
+    D_m = torch.empty((M_m, N_m), dtype=torch.bfloat16, device=dev)
+
+    def moe(i):
+        st = lib.fp4_grouped_gemm(fp4.FP4_NVFP4, P(aq_m), P(as_m), P(ga_m), P(wq_m), P(ws_m), P(gb_m),
+                                  1.0, E_m, P(offs_m), M_m, N_m, K_m, P(D_m), fp4.FP4_BF16, stream_of())
+        assert st == 0, st
+
+    ops.append(Op("grouped_gemm_moe_nvfp4", moe, 3, "TFLOP/s", 2 * M_m * N_m * K_m,
+                  MFMA_PEAK_TFLOPS["fp16"], "mfma", "k_gemm<NV, grouped> (64 experts, one launch)",
+                  msrc))
+
     # -------------------------------------------------------------- rotate --
     R_H, C_H = 16384, 8192
     xh = bf16_from_bits(workloads.rotate_input(R_H, C_H))
@@ -454,7 +490,7 @@ def main():
             "step_also_runs": "mxfp4_quantize, NV/MX dequantize, NVFP4 block 8/32 and scale-search "
                               "variants (8192x8192); GEMV W 27648x5120 "
                               "B=1,4,16; GEMM 8192x28672x8192 NVFP4 and MXFP4 (bf16 out), NVFP4 "
-                              "(E4M3 out, NVFP4 out); FWHT+NVFP4 "
+                              "(E4M3 out, NVFP4 out); MoE grouped GEMM 64x2048x7168 (32768 rows); FWHT+NVFP4 "
                               "16384x8192 RNE and SR",
         },
         "roofline": {

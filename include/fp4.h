@@ -205,6 +205,33 @@ fp4_status fp4_scaled_gemm_nvfp4_out(fp4_format fmt, const uint8_t* A, const uin
                                      uint8_t* Dq, uint8_t* d_scales, const float* d_amax,
                                      float* d_global_scale, hipStream_t stream);
 
+/*
+ * fp4_grouped_gemm -- many GEMMs with one K and N in one launch, e.g. the expert
+ * FFNs of a mixture-of-experts layer, whose weights the "NVIDIA NVFP4 与
+ * Micro-Scaling" article (section 6.1) names as the first NVFP4 candidates.
+ * Group e (0 <= e < num_groups) computes, as fp4_scaled_gemm does,
+ *   D[r, :] = g_d * (A_hat[r, :] @ W_hat_e^T)   for r in [offsets[e], offsets[e+1])
+ * where the rows of all groups are stored back to back (tokens sorted by group).
+ *   A [M_total, K/2], a_scales [M_total, K/bs]; g_a one device float (NVFP4: the
+ *       s_global of the whole A) or NULL (MXFP4);
+ *   W [num_groups, N, K/2], w_scales [num_groups, N, K/bs]; g_b device floats
+ *       [num_groups] (NVFP4: each group's s_global) or NULL (MXFP4);
+ *   offsets  device int32 [num_groups + 1], non-decreasing, offsets[0] = 0,
+ *       offsets[num_groups] = M_total.  Read on the device (no host sync, so the
+ *       call can be captured in a graph).  Offsets outside that contract are
+ *       clamped into [0, M_total]: no memory outside A, W and D is touched, but
+ *       D is then unspecified;
+ *   D  out [M_total, N], FP4_F32, FP4_BF16 or FP4_E4M3 (as fp4_scaled_gemm).
+ * Each group's result equals fp4_scaled_gemm of its rows, bit for bit.  Rows
+ * of D outside every group are not written.  num_groups >= 1; K % 32 == 0;
+ * A, W 16-byte aligned.  M_total == 0 or N == 0 is a no-op; K == 0 writes D = 0.
+ */
+fp4_status fp4_grouped_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
+                            const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                            const float* g_b, float g_d, int64_t num_groups,
+                            const int32_t* offsets, int64_t M_total, int64_t N, int64_t K,
+                            void* D, fp4_dtype dt, hipStream_t stream);
+
 /* Bytes of workspace fp4_gemv_batched needs for a batch of B rows of length K. */
 size_t fp4_gemv_workspace_bytes(int64_t B, int64_t K);
 

@@ -48,6 +48,9 @@ SIGNATURES = {
     "fp4_scaled_gemm_nvfp4_out": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                                  ctypes.c_float, _c_i64, _c_i64, _c_i64, _c_p,
                                                  _c_p, _c_p, _c_p, _c_p]),
+    "fp4_grouped_gemm": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                        ctypes.c_float, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p,
+                                        ctypes.c_int, _c_p]),
     "fp4_gemv_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "fp4_gemv_batched": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_p, _c_p, _c_p, _c_i64,
                                         _c_i64, ctypes.c_float, _c_p, ctypes.c_int, _c_p,
@@ -354,3 +357,33 @@ def hadamard_rotate(x: torch.Tensor, group: int = 128, out_dtype: torch.dtype = 
                                         _ptr(y), _dtype_code(out_dtype), _stream(x.device))
     _check(st, "hadamard_rotate")
     return y
+
+
+def fp4_grouped_gemm(fmt: int, A: torch.Tensor, a_scales: torch.Tensor, g_a, W: torch.Tensor,
+                     w_scales: torch.Tensor, g_b, offsets: torch.Tensor, K: int, g_d: float = 1.0,
+                     out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """One launch over E GEMMs: rows offsets[e] .. offsets[e+1] of A times W[e]^T.
+    A [M_total, K/2], W [E, N, K/2] (or [E*N, K/2]), w_scales [E, N, K/bs],
+    g_b [E] (NVFP4) or None, offsets int32 [E+1] on the device."""
+    A = _gpu_2d(A, "A")
+    a_scales = _gpu_2d(a_scales, "a_scales")
+    dev = A.device
+    if W.dim() != 3 or not W.is_cuda:
+        raise ValueError("W must be a [E, N, K/2] GPU tensor")
+    E, N = W.shape[0], W.shape[1]
+    if A.shape[1] != K // 2 or W.shape[2] != K // 2:
+        raise ValueError("A and W must hold K/2 packed bytes per row")
+    if offsets.dtype != torch.int32 or offsets.numel() != E + 1 or offsets.device != dev:
+        raise ValueError("offsets must be int32 [E+1] on the operands' device")
+    W = W.contiguous()
+    w_scales = w_scales.contiguous()
+    M = A.shape[0]
+    D = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
+    ga = None if g_a is None else g_a.reshape(1).contiguous()
+    gb = None if g_b is None else g_b.reshape(E).contiguous()
+    st = load_library().fp4_grouped_gemm(fmt, _ptr(A), _ptr(a_scales), _ptr(ga), _ptr(W),
+                                         _ptr(w_scales), _ptr(gb), float(g_d), E,
+                                         _ptr(offsets.contiguous()), M, N, K, _ptr(D),
+                                         _dtype_code(D.dtype), _stream(dev))
+    _check(st, "fp4_grouped_gemm")
+    return D

@@ -241,6 +241,39 @@ fp4_status fp4_scaled_gemm_nvfp4_out(fp4_format fmt, const uint8_t* A, const uin
   return FP4_OK;
 }
 
+fp4_status fp4_grouped_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
+                            const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                            const float* g_b, float g_d, int64_t num_groups,
+                            const int32_t* offsets, int64_t M_total, int64_t N, int64_t K,
+                            void* D, fp4_dtype dt, hipStream_t stream) {
+  if (fmt != FP4_NVFP4 && fmt != FP4_MXFP4) return FP4_ERR_DTYPE;
+  if (!valid_dtype(dt) && dt != FP4_E4M3) return FP4_ERR_DTYPE;
+  const int d_bytes = dt == FP4_F32 ? 4 : dt == FP4_BF16 ? 2 : 1;
+  if (num_groups < 1 || M_total < 0 || N < 0 || K < 0 || K % 32 != 0) return FP4_ERR_SHAPE;
+  if (fmt == FP4_MXFP4 && (g_a != nullptr || g_b != nullptr)) return FP4_ERR_DTYPE;
+  if (M_total == 0 || N == 0) return FP4_OK;
+  if (D == nullptr) return FP4_ERR_NULL;
+  if (!aligned(D, d_bytes)) return FP4_ERR_ALIGN;
+  if (K == 0) {   // every group's contraction is empty: D = 0
+    fp4_status st = check_arch();
+    if (st != FP4_OK) return st;
+    FP4_TRY_LAUNCH(fp4impl::launch_zero_fill(D, M_total * N, d_bytes, stream), "fp4_grouped_gemm");
+    return FP4_OK;
+  }
+  if (A == nullptr || a_scales == nullptr || W == nullptr || w_scales == nullptr ||
+      offsets == nullptr)
+    return FP4_ERR_NULL;
+  if (fmt == FP4_NVFP4 && (g_a == nullptr || g_b == nullptr)) return FP4_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(W, 16) || !aligned(offsets, 4)) return FP4_ERR_ALIGN;
+  fp4_status st = check_arch();
+  if (st != FP4_OK) return st;
+  FP4_TRY_LAUNCH(fp4impl::launch_grouped_gemm(fmt == FP4_MXFP4, A, a_scales, g_a, W, w_scales, g_b,
+                                              g_d, num_groups, offsets, M_total, N, K, D, d_bytes,
+                                              stream),
+                 "fp4_grouped_gemm");
+  return FP4_OK;
+}
+
 size_t fp4_gemv_workspace_bytes(int64_t B, int64_t K) {
   if (B < 0 || K < 0) return 0;
   return fp4impl::gemv_workspace_bytes(B, K);

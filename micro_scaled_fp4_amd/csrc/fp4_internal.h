@@ -73,6 +73,14 @@ hipError_t launch_gemm_nvfp4_out(bool mx, const uint8_t* A, const uint8_t* a_sca
                                  const float* g_b, float g_d, int64_t M, int64_t N, int64_t K,
                                  void* D, int d_bytes, uint8_t* d_scales, const float* d_amax,
                                  float* d_gscale, hipStream_t stream);
+// One launch over ngroups GEMMs: group e multiplies rows offsets[e] ..
+// offsets[e+1] of A (and writes those rows of D) by W + e N K/2 with tensor
+// scale g_b[e] (NVFP4).  d_bytes 4 / 2 / 1 (float32, bf16, E4M3).
+hipError_t launch_grouped_gemm(bool mx, const uint8_t* A, const uint8_t* a_scales,
+                               const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                               const float* g_b, float g_d, int64_t ngroups,
+                               const int32_t* offsets, int64_t M, int64_t N, int64_t K, void* D,
+                               int d_bytes, hipStream_t stream);
 // *out = s_global of the tensor amax *amax (one thread).
 hipError_t launch_nv_global_scale(const float* amax, float* out, hipStream_t stream);
 

@@ -97,6 +97,46 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = r / gsize;
 }
 
+// Grouped GEMM (one launch over E groups, e.g. the experts of an MoE layer):
+// row tile `row_tile` of the concatenation of the groups' row tiles -> group
+// e, its first row lo and one past its last row hi (offsets clamped into
+// [0, M], so rows never leave A or D), and the tile's index tm inside the
+// group.  Each wave walks the offsets 64 groups at a time with a lane prefix
+// sum; the waves of a workgroup reach the same result, so no barrier is
+// needed.  False when row_tile is past the last group's tiles.
+__device__ __forceinline__ bool group_tile_of(const int32_t* __restrict__ goff, int ngroups, int M,
+                                              int row_tile, int& e_out, int& tm, int& lo, int& hi) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int c = 0; c < ngroups; c += 64) {
+    const int e = c + lane;
+    int l0 = 0, l1 = 0, tl = 0;
+    if (e < ngroups) {
+      l0 = min(max(goff[e], 0), M);
+      l1 = min(max(goff[e + 1], l0), M);
+      tl = (l1 - l0 + BM - 1) / BM;
+    }
+    int inc = tl;   // inclusive prefix sum of the tile counts over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += v;
+    }
+    const int start = base + inc - tl;
+    const uint64_t hit = __ballot(e < ngroups && row_tile >= start && row_tile < start + tl);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      e_out = c + src;
+      tm = row_tile - __shfl(start, src, 64);
+      lo = __shfl(l0, src, 64);
+      hi = __shfl(l1, src, 64);
+      return true;
+    }
+    base += __shfl(inc, 63, 64);
+  }
+  return false;
+}
+
 // D += W x A with block scales, FP4 operands (16 bytes of codes per lane):
 // v_mfma_scale_f32_16x16x128_f8f6f4, accumulating in place in AGPRs.  SW / SA
 // select the scale byte of sw / sa.  Written as inline asm because the
@@ -381,17 +421,40 @@ __device__ __forceinline__ void store_outputs(v4f (&acc)[kTN][kTM], float alpha,
 }
 
 // ------------------------------------------------------------------ kernel --
-template <bool MX, int OUT, bool SCALE_VEC>
+// GROUPED: A and D hold the groups' rows back to back (group e: rows goff[e] ..
+// goff[e+1]), W and w_scales one [N, K] operand per group, g_b one tensor
+// scale per group; the grid is an upper bound on the groups' tiles.
+template <bool MX, int OUT, bool SCALE_VEC, bool GROUPED>
 __global__ void __launch_bounds__(kThreads, 1)
     k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ as,
            const uint8_t* __restrict__ W, const uint8_t* __restrict__ ws,
            const float* __restrict__ g_a, const float* __restrict__ g_b, float g_d, int M, int N,
            int K, void* __restrict__ D, uint8_t* __restrict__ d_scales,
            const float* __restrict__ d_amax, float* __restrict__ d_gscale, int tiles_m, int tiles_n,
-           bool vec_out) {
+           bool vec_out, const int32_t* __restrict__ goff, int ngroups) {
+  static_assert(!GROUPED || OUT != 0, "grouped launches write float32, bf16 or E4M3");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  if constexpr (GROUPED) {
+    // consecutive tiles on one XCD; the column tile runs fastest, so the
+    // workgroups of an XCD share the row tile of A in its L2
+    const int T = gridDim.x;
+    const int bid = blockIdx.x;
+    const int t = T % kXcds == 0 ? (bid % kXcds) * (T / kXcds) + bid / kXcds : bid;
+    int e, lo, hi;
+    if (!group_tile_of(goff, ngroups, M, t / tiles_n, e, tm, lo, hi)) return;
+    tn = t % tiles_n;
+    const int kb = MX ? 32 : 16;
+    A += (int64_t)lo * (K / 2);
+    as += (int64_t)lo * (K / kb);
+    W += (int64_t)e * N * (K / 2);
+    ws += (int64_t)e * N * (K / kb);
+    if (!MX) g_b += e;
+    D = reinterpret_cast<uint8_t*>(D) + (int64_t)lo * N * OUT;
+    M = hi - lo;
+  } else {
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -723,15 +786,23 @@ struct OutArgs {
   float* d_gscale;
 };
 
-template <bool MX, int OUT, bool SCALE_VEC>
+// Groups of a grouped launch: ngroups > 0 selects the grouped kernel.
+struct Groups {
+  const int32_t* offsets;
+  int ngroups;
+};
+
+template <bool MX, int OUT, bool SCALE_VEC, bool GROUPED = false>
 hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
                     const float* g_a, const float* g_b, float g_d, int M, int N, int K,
-                    const OutArgs& o, hipStream_t stream) {
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+                    const OutArgs& o, hipStream_t stream, const Groups& gr = Groups{nullptr, 0}) {
+  const int tiles_n = (N + BN - 1) / BN;
+  // grouped: each group adds at most one partial row tile to ceil(M / BM)
+  const int tiles_m = (M + BM - 1) / BM + (GROUPED ? gr.ngroups : 0);
   constexpr int lds = Cfg<MX>::kLdsBytes;
   static bool attr_set = false;   // per process; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MX, OUT, SCALE_VEC>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MX, OUT, SCALE_VEC, GROUPED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -740,9 +811,9 @@ hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const
   // (NVFP4: 4 outputs are 2 bytes)
   const bool vec_out =
       N % 4 == 0 && reinterpret_cast<uintptr_t>(o.D) % (OUT == 0 ? 2 : 4 * OUT) == 0;
-  hipLaunchKernelGGL((k_gemm<MX, OUT, SCALE_VEC>), dim3(tiles_m * tiles_n), dim3(kThreads), lds,
-                     stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, o.D, o.d_scales, o.d_amax,
-                     o.d_gscale, tiles_m, tiles_n, vec_out);
+  hipLaunchKernelGGL((k_gemm<MX, OUT, SCALE_VEC, GROUPED>), dim3(tiles_m * tiles_n), dim3(kThreads),
+                     lds, stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, o.D, o.d_scales, o.d_amax,
+                     o.d_gscale, tiles_m, tiles_n, vec_out, gr.offsets, gr.ngroups);
   return hipGetLastError();
 }
 
@@ -768,6 +839,25 @@ hipError_t launch_o(const uint8_t* A, const uint8_t* as, const uint8_t* W, const
     case 0: return launch_s<MX, 0>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <bool MX>
+hipError_t launch_grouped_o(const uint8_t* A, const uint8_t* as, const uint8_t* W, const uint8_t* ws,
+                            const float* g_a, const float* g_b, float g_d, int M, int N, int K,
+                            void* D, int d_bytes, const Groups& gr, hipStream_t stream) {
+  const bool vec = K % BK == 0 && (reinterpret_cast<uintptr_t>(as) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
+  const OutArgs o{D, nullptr, nullptr, nullptr};
+#define FP4_GG(OUTV)                                                                          \
+  return vec ? launch_t<MX, OUTV, true, true>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream, gr) \
+             : launch_t<MX, OUTV, false, true>(A, as, W, ws, g_a, g_b, g_d, M, N, K, o, stream, gr)
+  switch (d_bytes) {
+    case 4: FP4_GG(4);
+    case 2: FP4_GG(2);
+    case 1: FP4_GG(1);
+    default: return hipErrorInvalidValue;
+  }
+#undef FP4_GG
 }
 
 __global__ void k_global_scale(const float* __restrict__ amax, float* __restrict__ out) {
@@ -799,6 +889,22 @@ hipError_t launch_gemm_nvfp4_out(bool mx, const uint8_t* A, const uint8_t* a_sca
                              d_bytes, stream)
             : launch_o<false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N, (int)K, o,
                               d_bytes, stream);
+}
+
+hipError_t launch_grouped_gemm(bool mx, const uint8_t* A, const uint8_t* a_scales,
+                               const float* g_a, const uint8_t* W, const uint8_t* w_scales,
+                               const float* g_b, float g_d, int64_t ngroups,
+                               const int32_t* offsets, int64_t M, int64_t N, int64_t K, void* D,
+                               int d_bytes, hipStream_t stream) {
+  // buffer ranges cover one 256-row tile of an operand: 256 * K / 2 < 2^31
+  if (M > (1 << 30) || N > (1 << 30) || K >= (1 << 23) || ngroups > (1 << 20))
+    return hipErrorInvalidValue;
+  if (((M + BM - 1) / BM + ngroups) * ((N + BN - 1) / BN) >= (int64_t)1 << 31) return hipErrorInvalidValue;
+  const Groups gr{offsets, (int)ngroups};
+  return mx ? launch_grouped_o<true>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N, (int)K,
+                                     D, d_bytes, gr, stream)
+            : launch_grouped_o<false>(A, a_scales, W, w_scales, g_a, g_b, g_d, (int)M, (int)N,
+                                      (int)K, D, d_bytes, gr, stream);
 }
 
 hipError_t launch_nv_global_scale(const float* amax, float* out, hipStream_t stream) {

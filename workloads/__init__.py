@@ -117,6 +117,18 @@ def rotate_input(rows: int = 16384, cols: int = 8192, n_outlier: int = 16, facto
     return f32_to_bf16_bits(a)
 
 
+SEED_MOE = 1006
+
+
+def moe_group_sizes(num_experts: int = 64, rows: int = 32768, seed: int = SEED_MOE) -> list:
+    """Rows routed to each expert of an MoE layer (tokens x top-k assignments):
+    a multinomial draw of `rows` over expert popularities exp(N(0, 0.5^2)), so
+    the loads are uneven and some experts may get none.  Sums to rows."""
+    rng = _rng(seed)
+    p = np.exp(rng.normal(0.0, 0.5, num_experts))
+    return [int(c) for c in rng.multinomial(rows, p / p.sum())]
+
+
 def random_codes(shape, seed: int) -> np.ndarray:
     """Uniform random 4-bit codes packed two per byte (any byte value is valid)."""
     return _rng(seed).integers(0, 256, size=shape, dtype=np.uint8)
