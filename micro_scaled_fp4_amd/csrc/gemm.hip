@@ -84,10 +84,21 @@ struct Cfg {
 };
 
 // ----------------------------------------------------------- tile mapping --
+// Workgroup bid -> tile t in [0, T): the hardware deals workgroups round-robin
+// to the kXcds XCDs, so XCD x runs workgroups x, x + kXcds, ...; of those below
+// T it takes the contiguous tiles [start_x, start_x + n_x).  A bijection on
+// [0, T) for any T; false for bid >= T.
+__device__ __forceinline__ bool xcd_tile(int bid, int T, int& t) {
+  if (bid >= T) return false;
+  const int x = bid % kXcds, k = bid / kXcds;
+  const int q = T / kXcds, rem = T % kXcds;
+  t = x * q + min(x, rem) + k;
+  return true;
+}
+
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
-  int t = bid;
-  if (T % kXcds == 0) t = (bid % kXcds) * (T / kXcds) + bid / kXcds;
+  int t;
+  xcd_tile(bid, tiles_m * tiles_n, t);   // the grid is exactly the tile count
   const int in_group = kGroupM * tiles_n;
   const int group = t / in_group;
   const int first_m = group * kGroupM;
@@ -97,33 +108,54 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = r / gsize;
 }
 
-// Grouped GEMM (one launch over E groups, e.g. the experts of an MoE layer):
-// row tile `row_tile` of the concatenation of the groups' row tiles -> group
-// e, its first row lo and one past its last row hi (offsets clamped into
-// [0, M], so rows never leave A or D), and the tile's index tm inside the
-// group.  Each wave walks the offsets 64 groups at a time with a lane prefix
-// sum; the waves of a workgroup reach the same result, so no barrier is
-// needed.  False when row_tile is past the last group's tiles.
+// Grouped GEMM (one launch over E groups, e.g. the experts of an MoE layer).
+// Group e's rows are goff[e] .. goff[e+1] (clamped into [0, M], so rows never
+// leave A or D); it has ceil(rows / BM) row tiles.  Each wave walks the
+// offsets 64 groups at a time with a lane prefix sum; the waves of a
+// workgroup reach the same results, so no barrier is needed.
+
+// Tile count of the groups c .. c + 63 held one per lane: (first row, one past
+// the last row, row tiles) of lane's group, and the inclusive prefix sum.
+__device__ __forceinline__ void group_chunk(const int32_t* __restrict__ goff, int ngroups, int M,
+                                            int c, int& l0, int& l1, int& tl, int& inc) {
+  const int lane = threadIdx.x & 63;
+  const int e = c + lane;
+  l0 = l1 = tl = 0;
+  if (e < ngroups) {
+    l0 = min(max(goff[e], 0), M);
+    l1 = min(max(goff[e + 1], l0), M);
+    tl = (l1 - l0 + BM - 1) / BM;
+  }
+  inc = tl;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(inc, d, 64);
+    if ((threadIdx.x & 63) >= d) inc += v;
+  }
+}
+
+// Total row tiles over all groups.
+__device__ __forceinline__ int group_row_tiles(const int32_t* __restrict__ goff, int ngroups, int M) {
+  int total = 0;
+  for (int c = 0; c < ngroups; c += 64) {
+    int l0, l1, tl, inc;
+    group_chunk(goff, ngroups, M, c, l0, l1, tl, inc);
+    total += __shfl(inc, 63, 64);
+  }
+  return total;
+}
+
+// Row tile `row_tile` -> group e, its first row lo, one past its last row hi,
+// and the tile's index tm inside the group.  False past the last group's tiles.
 __device__ __forceinline__ bool group_tile_of(const int32_t* __restrict__ goff, int ngroups, int M,
                                               int row_tile, int& e_out, int& tm, int& lo, int& hi) {
-  const int lane = threadIdx.x & 63;
   int base = 0;
   for (int c = 0; c < ngroups; c += 64) {
-    const int e = c + lane;
-    int l0 = 0, l1 = 0, tl = 0;
-    if (e < ngroups) {
-      l0 = min(max(goff[e], 0), M);
-      l1 = min(max(goff[e + 1], l0), M);
-      tl = (l1 - l0 + BM - 1) / BM;
-    }
-    int inc = tl;   // inclusive prefix sum of the tile counts over the lanes
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += v;
-    }
+    int l0, l1, tl, inc;
+    group_chunk(goff, ngroups, M, c, l0, l1, tl, inc);
     const int start = base + inc - tl;
-    const uint64_t hit = __ballot(e < ngroups && row_tile >= start && row_tile < start + tl);
+    const uint64_t hit = __ballot(c + (int)(threadIdx.x & 63) < ngroups && row_tile >= start &&
+                                  row_tile < start + tl);
     if (hit) {
       const int src = __ffsll((unsigned long long)hit) - 1;
       e_out = c + src;
@@ -436,12 +468,11 @@ __global__ void __launch_bounds__(kThreads, 1)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   if constexpr (GROUPED) {
-    // consecutive tiles on one XCD; the column tile runs fastest, so the
-    // workgroups of an XCD share the row tile of A in its L2
-    const int T = gridDim.x;
-    const int bid = blockIdx.x;
-    const int t = T % kXcds == 0 ? (bid % kXcds) * (T / kXcds) + bid / kXcds : bid;
-    int e, lo, hi;
+    // the groups' tiles (the grid is an upper bound) dealt to the XCDs in
+    // contiguous ranges; the column tile runs fastest, so the workgroups of an
+    // XCD share the row tile of A in its L2
+    int t, e, lo, hi;
+    if (!xcd_tile(blockIdx.x, group_row_tiles(goff, ngroups, M) * tiles_n, t)) return;
     if (!group_tile_of(goff, ngroups, M, t / tiles_n, e, tm, lo, hi)) return;
     tn = t % tiles_n;
     const int kb = MX ? 32 : 16;
