@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the NVFP4 / MXFP4 hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]   (defaults 10 / 5)
 
 One step runs every call of the hot path once per input copy, each at its
 workload's shape:
@@ -53,8 +53,8 @@ GiB = 1 << 30
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=5)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", default="", help="comma list of call names to run (profiling)")
@@ -213,6 +213,7 @@ def main():
         d = y.double() - xa.double()
         return float((d * d).mean())
 
+    block_mse = block_error_report(torch, fp4, xa, static_amax)
     for op in ops:
         if op.name == "nvfp4_quantize_static":
             op.extra["roundtrip_mse"] = roundtrip_mse(16, 0)
@@ -455,6 +456,7 @@ def main():
         tr_bytes = tr["bytes_per_call"] if tr and tr.get("src") == op.src else None
         comps[op.name] = {
             "us_per_call": round(t_ms * 1e3, 2),
+            "us_median": round(float(np.median(op.times_ms)) * 1e3, 2),
             "us_p10": round(float(np.percentile(op.times_ms, 10)) * 1e3, 2),
             "us_p90": round(float(np.percentile(op.times_ms, 90)) * 1e3, 2),
             "achieved": round(achieved, 1), "unit": op.unit, "peak": op.peak,
@@ -463,6 +465,8 @@ def main():
             "kernels": op.kernel, "calls_per_replay": op.n, "traffic": tr_bytes,
         }
         comps[op.name].update(op.extra)
+        if op.unit == "GB/s":
+            comps[op.name]["frac_of_copy"] = round(achieved / copy_gbs, 4)
         if op.name in ("gemm_nvfp4", "gemm_nvfp4_e4m3_out", "gemm_nvfp4_nvfp4_out"):
             comps[op.name]["frac_of_fp4_peak"] = round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4)
 
@@ -486,6 +490,10 @@ def main():
                         "nvfp4_quantize with dynamic (computed) amax",
             "rows": R_A, "cols": C_A,
             "value_bytes_per_call": b_nv_dyn,
+            "seeds": {"tiny": workloads.SEED_TINY, "activation": workloads.SEED_ACTIVATION,
+                      "gemv": workloads.SEED_GEMV, "gemm": workloads.SEED_GEMM,
+                      "rotate": workloads.SEED_ROTATE, "stochastic_rounding": workloads.SEED_SR,
+                      "moe": workloads.SEED_MOE},
             "value_bytes_note": "x read twice (amax pass, encode pass) + codes + scale bytes + 2 floats",
             "step_also_runs": "mxfp4_quantize, NV/MX dequantize, NVFP4 block 8/32 and scale-search "
                               "variants (8192x8192); GEMV W 27648x5120 "
@@ -501,6 +509,7 @@ def main():
             "avg_launch_us": enc["us_per_call"],
         },
         "components": comps,
+        "block_mse": block_mse,
         "rotation_error": rotation_error,
         "context": {"device_copy_GBs_read_plus_write": round(copy_gbs, 1),
                     "note": "torch copy_ of 512 MiB, for reference against the 8 TB/s peak"},
@@ -510,6 +519,34 @@ def main():
     if not args.no_cpu_baseline and (not only or "nvfp4_quantize_dynamic" in only):
         result["cpu_baseline"] = cpu_baseline(xa, args.cpu_seconds, b_nv / elems)
     print(json.dumps(result), flush=True)
+
+
+def block_error_report(torch, fp4, x, amax):
+    """Squared error per 16-value block of the activation after an NVFP4 and an
+    MXFP4 round trip (the same 16-value blocks for both): mean, p99, and the
+    means over blocks that hold an outlier channel (columns with mean |x| > 10,
+    the x40 channels) and over the other blocks; NV / MX ratio of the means.
+    Information only: not timed."""
+    R, C = x.shape
+    xf = x.float()
+    outlier_cols = (xf.abs().mean(dim=0) > 10.0)
+    outlier_blocks = outlier_cols.reshape(C // 16, 16).any(dim=1)          # [C/16]
+
+    def stats(y):
+        e = ((y.double() - xf.double()) ** 2).reshape(R, C // 16, 16).mean(dim=2)
+        o = e[:, outlier_blocks]
+        c = e[:, ~outlier_blocks]
+        p99 = float(torch.quantile(e.flatten().float(), 0.99))    # 4.2 M blocks
+        return {"mean": float(e.mean()), "p99": p99, "outlier_blocks_mean": float(o.mean()),
+                "clean_blocks_mean": float(c.mean())}
+
+    q, sc, _, g = fp4.nvfp4_quantize(x, amax=amax)
+    nv = stats(fp4.fp4_dequantize(fp4.FP4_NVFP4, q, sc, g, C, torch.float32))
+    qm, sm = fp4.mxfp4_quantize(x)
+    mx = stats(fp4.fp4_dequantize(fp4.FP4_MXFP4, qm, sm, None, C, torch.float32))
+    return {"nvfp4": nv, "mxfp4": mx, "nv_over_mx_mean": round(nv["mean"] / mx["mean"], 4),
+            "outlier_block_fraction": round(float(outlier_blocks.float().mean()), 5),
+            "block": 16, "workload": "activation 8192x8192 (static amax for NVFP4)"}
 
 
 def rotation_error_report(torch, fp4, x, w, w_nv, w_mx):
@@ -561,6 +598,7 @@ def cpu_baseline(xa, seconds, bytes_per_elem):
     dt = time.perf_counter() - t0
     return {"value": round(n_el * bytes_per_elem / dt / 1e9, 4), "unit": "GB/s",
             "cores": 1, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0)),
             "sample": f"{n_el // xf.shape[1]} rows (256-row slices of the first 2048 rows) of the "
                       f"8192x8192 activation, nvfp4_quantize at the full tensor's amax, {dt:.1f} s"}
 
