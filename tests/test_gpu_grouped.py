@@ -164,3 +164,28 @@ def test_moe_workload_sampled_groups():
         ref, mag = o.scaled_gemm_ref(Ah, Wh, 1.0)
         ok, err, bound = o.gemm_within_tolerance(D[lo:hi], ref, mag, True)
         assert ok, (int(e), float(np.max(err / np.maximum(bound, 1e-300))))
+
+
+def test_all_products_are_deterministic():
+    """Every kernel with a reduction (GEMM, grouped GEMM, GEMV, rotation with a
+    computed amax) gives the same bytes when run twice: no atomics, fixed
+    summation orders."""
+    announce("determinism of GEMM / grouped / GEMV / rotation")
+    dev = "cuda:0"
+    M, N, K = 300, 520, 2048
+    A = o.bf16_bits_to_f32(workloads.gemm_a(M, K, seed=90))
+    W = o.bf16_bits_to_f32(workloads.gemm_w(N, K, seed=91))
+    Ag, Wg = torch.from_numpy(A).to(dev), torch.from_numpy(W).to(dev)
+    qa, sa, _, ga = fp4.nvfp4_quantize(Ag)
+    qw, sw, _, gw = fp4.nvfp4_quantize(Wg)
+    runs = []
+    for _ in range(2):
+        out = [fp4.fp4_scaled_gemm(fp4.FP4_NVFP4, qa, sa, ga, qw, sw, gw, K, 1.0, torch.float32),
+               fp4.fp4_gemv_batched(Ag[:16].contiguous(), qw, sw, gw, K, 1.0, torch.float32),
+               fp4.fp4_grouped_gemm(fp4.FP4_NVFP4, qa, sa, ga, torch.stack([qw, qw]), torch.stack([sw, sw]),
+                                    torch.cat([gw, gw]), torch.tensor([0, 123, M], dtype=torch.int32, device=dev),
+                                    K, 1.0, torch.float32)]
+        out += list(fp4.hadamard_quantize(Ag))
+        runs.append(out)
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
