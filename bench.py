@@ -117,8 +117,8 @@ class Op:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
-                                   "part of it (see the sharding notes in DESIGN.md)",
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus above 1 is not supported "
+                                   "(the library runs on one device per process)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
