@@ -570,10 +570,13 @@ __global__ void __launch_bounds__(kThreads, 1)
     return *reinterpret_cast<const uint32_t*>(tile + swz(row, 2 * g + (u >> 2)) + 4 * (u & 3));
   };
   // f16 pair (h(b0), h(b1)) of the two E4M3 scale bytes of k-step ks in a tile's
-  // scale dword, h(b) = E4M3(b) * 2^-8 exactly (see e4m3_h2)
+  // scale dword, h(b) = E4M3(b) * 2^-8: one v_cvt_scalef32_pk_f16_fp8 with the
+  // scale 2^-8 (exact for every finite E4M3 byte, subnormals included; a NaN
+  // byte gives NaN)
   auto scale_pair = [&](uint32_t scale_dw, int ks) {
-    const uint32_t y = (scale_dw >> (16 * ks)) & 0xffffu;
-    return ((y & 0x80u) << 8) | ((y & 0x7fu) << 7) | ((y & 0x8000u) << 16) | ((y & 0x7f00u) << 15);
+    const v2h p = ks ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scale_dw, 0x1p-8f, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scale_dw, 0x1p-8f, false);
+    return __builtin_bit_cast(uint32_t, p);
   };
   // values 2k, 2k + 1 (k = part) of the 8 dequantized values of sub-step u: the
   // E2M1 codes scaled by 2^8, times the scale of block half (u % 4) / 2

@@ -331,6 +331,14 @@ __device__ __forceinline__ v2h e4m3_h2(uint32_t byte) {
   return __builtin_bit_cast(v2h, h | (h << 16));
 }
 
+// f16 pair (h(b0), h(b1)) of the two E4M3 bytes of 16-bit word SEL of w, the
+// same h as e4m3_h2 for every finite byte (v_cvt_scalef32_pk_f16_fp8 with the
+// scale 2^-8, one instruction for two bytes; a NaN byte gives NaN).
+template <bool SEL>
+__device__ __forceinline__ v2h e4m3_pair_h(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 0x1p-8f, SEL);
+}
+
 // The 8 values E2M1(code) * E4M3 of one dword of codes: the conversion scales
 // by 2^8 (exact), and the f16 product with E4M3 * 2^-8 is exact (at most 6
 // significant bits, magnitude in [2^-10, 2688]).
@@ -616,14 +624,15 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
         } else {
           const u32x4 xc = *reinterpret_cast<const u32x4*>(lds + xrow * xc_row + v0 / 2);
           const uint32_t xsb = *reinterpret_cast<const uint16_t*>(xs_base + xrow * bpr + v0 / 16);
-          const v2h h0 = e4m3_h2(xsb & 0xffu), h1 = e4m3_h2(xsb >> 8);
+          const v2h hp = e4m3_pair_h<false>(xsb);
+          const v2h h0 = v2h{hp.x, hp.x}, h1 = v2h{hp.y, hp.y};
           xq[0] = dq8(xc.x, h0);
           xq[1] = dq8(xc.y, h0);
           xq[2] = dq8(xc.z, h1);
           xq[3] = dq8(xc.w, h1);
         }
-        const v2h w0 = e4m3_h2((sw >> (16 * st)) & 0xffu);
-        const v2h w1 = e4m3_h2((sw >> (16 * st + 8)) & 0xffu);
+        const v2h wp = st ? e4m3_pair_h<true>(sw) : e4m3_pair_h<false>(sw);
+        const v2h w0 = v2h{wp.x, wp.x}, w1 = v2h{wp.y, wp.y};
         v4f& acc = st ? acc1 : acc0;
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[0], dq8(codes.x, w0), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xq[1], dq8(codes.y, w0), acc, 0, 0, 0);
