@@ -59,6 +59,17 @@ typedef enum { FP4_RNE = 0, FP4_SR = 1 } fp4_rounding;
  * partial maxima of the first pass. */
 #define FP4_AMAX_WORKSPACE_BYTES 4096
 
+/* Size limits of the contractions.  The GEMM kernels address one 256-row tile
+ * of an operand, and the GEMV one 16-row strip of W, with 32-bit byte offsets;
+ * shapes beyond these return FP4_ERR_SHAPE before anything is launched.  The
+ * quantizers, the dequantizer and the rotations index in 64 bits and have no
+ * limit of their own. */
+#define FP4_GEMM_MAX_MN (1LL << 30)           /* M, N (M_total) of the GEMMs */
+#define FP4_GEMM_MAX_K ((1LL << 23) - 32)     /* K of the GEMMs */
+#define FP4_GROUPED_MAX_GROUPS (1LL << 20)    /* num_groups of fp4_grouped_gemm */
+#define FP4_GEMV_MAX_N (1LL << 30)
+#define FP4_GEMV_MAX_K (1LL << 30)
+
 /*
  * nvfp4_quantize -- two-level NVFP4 quantization of x [rows, cols].
  *
@@ -171,6 +182,7 @@ fp4_status nvfp4_dequantize_ex(const uint8_t* q, const uint8_t* scales, const fl
  * rounding for bf16 output).  K must be a multiple of bs (FP4_ERR_SHAPE);
  * A, W must be 16-byte aligned and K a multiple of 32 (FP4_ERR_ALIGN / SHAPE).
  * M == 0 or N == 0 is a no-op; K == 0 writes D = 0 without reading the operands.
+ * M, N <= FP4_GEMM_MAX_MN and K <= FP4_GEMM_MAX_K, else FP4_ERR_SHAPE.
  */
 fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
                            const float* g_a, const uint8_t* W, const uint8_t* w_scales,
@@ -225,6 +237,9 @@ fp4_status fp4_scaled_gemm_nvfp4_out(fp4_format fmt, const uint8_t* A, const uin
  * Each group's result equals fp4_scaled_gemm of its rows, bit for bit.  Rows
  * of D outside every group are not written.  num_groups >= 1; K % 32 == 0;
  * A, W 16-byte aligned.  M_total == 0 or N == 0 is a no-op; K == 0 writes D = 0.
+ * M_total, N <= FP4_GEMM_MAX_MN, K <= FP4_GEMM_MAX_K, num_groups <=
+ * FP4_GROUPED_MAX_GROUPS and (ceil(M_total/256) + num_groups) * ceil(N/256) <
+ * 2^31 (the launch's tile bound), else FP4_ERR_SHAPE.
  */
 fp4_status fp4_grouped_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_scales,
                             const float* g_a, const uint8_t* W, const uint8_t* w_scales,
@@ -246,6 +261,7 @@ size_t fp4_gemv_workspace_bytes(int64_t B, int64_t K);
  *   workspace  >= fp4_gemv_workspace_bytes(B, K) bytes (holds quantized x).
  * N == 0 is a no-op; K == 0 writes y = 0 without reading x, W or the workspace.
  * x, W and workspace must be 16-byte aligned, w_scales 2-byte aligned (FP4_ERR_ALIGN).
+ * N <= FP4_GEMV_MAX_N and K <= FP4_GEMV_MAX_K, else FP4_ERR_SHAPE.
  * Accuracy as for fp4_scaled_gemm.
  */
 fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_t* W,

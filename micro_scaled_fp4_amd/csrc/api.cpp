@@ -184,6 +184,7 @@ fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_sc
   const int d_bytes = dt == FP4_F32 ? 4 : dt == FP4_BF16 ? 2 : 1;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_SHAPE;
   if (K % 32 != 0) return FP4_ERR_SHAPE;
+  if (M > FP4_GEMM_MAX_MN || N > FP4_GEMM_MAX_MN || K > FP4_GEMM_MAX_K) return FP4_ERR_SHAPE;
   if (fmt == FP4_MXFP4 && (g_a != nullptr || g_b != nullptr)) return FP4_ERR_DTYPE;
   if (M == 0 || N == 0) return FP4_OK;
   if (K == 0) {   // empty contraction: D = 0, operands are not read
@@ -214,6 +215,7 @@ fp4_status fp4_scaled_gemm_nvfp4_out(fp4_format fmt, const uint8_t* A, const uin
   if (fmt != FP4_NVFP4 && fmt != FP4_MXFP4) return FP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_SHAPE;
   if (K % 32 != 0) return FP4_ERR_SHAPE;
+  if (M > FP4_GEMM_MAX_MN || N > FP4_GEMM_MAX_MN || K > FP4_GEMM_MAX_K) return FP4_ERR_SHAPE;
   if (fmt == FP4_MXFP4 && (g_a != nullptr || g_b != nullptr)) return FP4_ERR_DTYPE;
   if (M == 0 || N == 0) return FP4_OK;
   if (Dq == nullptr || d_scales == nullptr || d_amax == nullptr || d_global_scale == nullptr)
@@ -250,6 +252,10 @@ fp4_status fp4_grouped_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_s
   if (!valid_dtype(dt) && dt != FP4_E4M3) return FP4_ERR_DTYPE;
   const int d_bytes = dt == FP4_F32 ? 4 : dt == FP4_BF16 ? 2 : 1;
   if (num_groups < 1 || M_total < 0 || N < 0 || K < 0 || K % 32 != 0) return FP4_ERR_SHAPE;
+  if (M_total > FP4_GEMM_MAX_MN || N > FP4_GEMM_MAX_MN || K > FP4_GEMM_MAX_K ||
+      num_groups > FP4_GROUPED_MAX_GROUPS)
+    return FP4_ERR_SHAPE;
+  if (((M_total + 255) / 256 + num_groups) * ((N + 255) / 256) >= (int64_t)1 << 31) return FP4_ERR_SHAPE;
   if (fmt == FP4_MXFP4 && (g_a != nullptr || g_b != nullptr)) return FP4_ERR_DTYPE;
   if (M_total == 0 || N == 0) return FP4_OK;
   if (D == nullptr) return FP4_ERR_NULL;
@@ -285,6 +291,7 @@ fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_
                             size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(xt) || !valid_dtype(yt)) return FP4_ERR_DTYPE;
   if (B < 1 || B > 16 || N < 0 || K < 0 || K % 32 != 0) return FP4_ERR_SHAPE;
+  if (N > FP4_GEMV_MAX_N || K > FP4_GEMV_MAX_K) return FP4_ERR_SHAPE;
   if (N == 0) return FP4_OK;
   if (K == 0) {   // empty contraction: y = 0, x, W and the workspace are not read
     if (y == nullptr) return FP4_ERR_NULL;

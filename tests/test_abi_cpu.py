@@ -127,3 +127,81 @@ def test_gemm_nvfp4_out_argument_errors():
     assert g(0, ctypes.c_void_p(4104), P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == ALIGN
     assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, ctypes.c_void_p(4098), P, None) == ALIGN
     assert g(0, None, None, None, None, None, None, 1.0, 0, 8, 64, None, None, None, None, None) == OK
+
+
+def test_variant_grouped_and_rotation_argument_errors():
+    """nvfp4_quantize_ex / nvfp4_dequantize_ex, fp4_grouped_gemm,
+    hadamard_quantize_mx and hadamard_rotate reject bad arguments on the host.
+    Every call here fails a host check, so none reaches a device."""
+    lib = m.load_library()
+    qx = lib.nvfp4_quantize_ex
+    assert qx(P, 1, 4, 64, 12, 0, P, P, P, 0, P, P, 4096, None) == SHAPE       # block 8/16/32 only
+    assert qx(P, 1, 4, 64, 16, -1, P, P, P, 0, P, P, 4096, None) == SHAPE
+    assert qx(P, 1, 4, 64, 16, 127, P, P, P, 0, P, P, 4096, None) == SHAPE     # search > 126
+    assert qx(P, 1, 4, 64, 8, 126, P, P, P, 0, None, P, 4096, None) == NULL    # global_scale
+    assert qx(P, 1, 4, 64, 32, 5, P, P, P, 0, P, P, 4095, None) == WORKSPACE
+    assert qx(P, 2, 4, 64, 32, 5, P, P, P, 0, P, P, 4096, None) == DTYPE      # E4M3 is no input
+    dx = lib.nvfp4_dequantize_ex
+    assert dx(P, P, P, 4, 64, 4, P, 0, None) == SHAPE
+    assert dx(P, P, P, 4, 64, 8, P, 2, None) == DTYPE                        # E4M3 is no output
+    assert dx(None, P, P, 4, 64, 8, P, 0, None) == NULL
+    gg = lib.fp4_grouped_gemm
+    assert gg(0, P, P, P, P, P, P, 1.0, 0, P, 8, 8, 64, P, 1, None) == SHAPE   # no groups
+    assert gg(0, P, P, P, P, P, P, 1.0, 2, P, 8, 8, 48, P, 1, None) == SHAPE   # K % 32
+    assert gg(1, P, P, P, P, P, P, 1.0, 2, P, 8, 8, 64, P, 1, None) == DTYPE   # MX: no g_a / g_b
+    assert gg(0, P, P, P, P, P, P, 1.0, 2, P, 8, 8, 64, P, 9, None) == DTYPE
+    assert gg(0, P, P, P, P, P, P, 1.0, 2, None, 8, 8, 64, P, 1, None) == NULL
+    assert gg(0, P, P, P, P, P, None, 1.0, 2, P, 8, 8, 64, P, 1, None) == NULL
+    assert gg(0, P, P, P, P, P, P, 1.0, 2, ctypes.c_void_p(4098), 8, 8, 64, P, 1, None) == ALIGN
+    assert gg(0, P, P, P, P, P, P, 1.0, 2, P, 0, 8, 64, P, 1, None) == OK       # no rows: no-op
+    hm = lib.hadamard_quantize_mx
+    assert hm(P, 1, 4, 256, 64, 0, 0, P, P, None) == SHAPE                     # group must be 128
+    assert hm(P, 1, 4, 200, 128, 0, 0, P, P, None) == SHAPE
+    assert hm(P, 1, 4, 256, 128, 2, 0, P, P, None) == DTYPE                    # rounding mode
+    assert hm(P, 2, 4, 256, 128, 0, 0, P, P, None) == DTYPE
+    assert hm(P, 1, 4, 256, 128, 1, 0, P, None, None) == NULL
+    assert hm(ctypes.c_void_p(4104), 1, 4, 256, 128, 1, 0, P, P, None) == ALIGN
+    assert hm(None, 1, 0, 256, 128, 1, 0, None, None, None) == OK             # no rows: no-op
+    hr = lib.hadamard_rotate
+    assert hr(P, 1, 4, 256, 256, P, 0, None) == SHAPE
+    assert hr(P, 1, 4, 256, 128, P, 2, None) == DTYPE
+    assert hr(P, 1, 4, 256, 128, None, 0, None) == NULL
+    assert hr(P, 1, 4, 256, 128, ctypes.c_void_p(4104), 0, None) == ALIGN
+
+
+def header_limit(name):
+    """Value of one of the header's size-limit macros."""
+    text = open(HEADER).read()
+    expr = re.search(rf"#define {name} (.+?)(?:/\*|$)", text, flags=re.M).group(1)
+    return int(eval(expr.replace("LL", "")))
+
+
+def test_contraction_size_limits_are_shape_errors():
+    """Shapes past the documented limits of the GEMMs and the GEMV return
+    FP4_ERR_SHAPE before any launch; the limits themselves pass the host checks
+    (shown by a later check failing instead)."""
+    lib = m.load_library()
+    mn, kmax = header_limit("FP4_GEMM_MAX_MN"), header_limit("FP4_GEMM_MAX_K")
+    assert mn == 1 << 30 and kmax == (1 << 23) - 32 and kmax % 32 == 0
+    g = lib.fp4_scaled_gemm
+    assert g(0, P, P, P, P, P, P, 1.0, mn + 1, 8, 64, P, 1, None) == SHAPE
+    assert g(0, P, P, P, P, P, P, 1.0, 8, mn + 1, 64, P, 1, None) == SHAPE
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, kmax + 32, P, 1, None) == SHAPE
+    assert g(0, P, P, P, P, P, P, 1.0, mn + 1, 8, 0, P, 1, None) == SHAPE       # also for K = 0
+    assert g(0, P, P, None, P, P, P, 1.0, mn, mn, kmax, P, 1, None) == NULL     # at the limits
+    n = lib.fp4_scaled_gemm_nvfp4_out
+    assert n(0, P, P, P, P, P, P, 1.0, 8, 8, kmax + 32, P, P, P, P, None) == SHAPE
+    assert n(0, P, P, P, P, P, P, 1.0, mn + 1, 8, 64, P, P, P, P, None) == SHAPE
+    gg = lib.fp4_grouped_gemm
+    emax = header_limit("FP4_GROUPED_MAX_GROUPS")
+    assert gg(0, P, P, P, P, P, P, 1.0, 2, P, mn + 1, 8, 64, P, 1, None) == SHAPE
+    assert gg(0, P, P, P, P, P, P, 1.0, 2, P, 8, 8, kmax + 32, P, 1, None) == SHAPE
+    assert gg(0, P, P, P, P, P, P, 1.0, emax + 1, P, 8, 8, 64, P, 1, None) == SHAPE
+    # tile bound: (ceil(M/256) + E) * ceil(N/256) < 2^31
+    assert gg(0, P, P, P, P, P, P, 1.0, 1, P, mn, mn, 64, P, 1, None) == SHAPE
+    assert gg(0, P, P, P, P, P, None, 1.0, emax, P, 1 << 20, 1 << 16, kmax, P, 1, None) == NULL
+    v = lib.fp4_gemv_batched
+    nv, kv = header_limit("FP4_GEMV_MAX_N"), header_limit("FP4_GEMV_MAX_K")
+    assert v(P, 1, 4, P, P, P, nv + 1, 512, 1.0, P, 1, P, 1 << 20, None) == SHAPE
+    assert v(P, 1, 4, P, P, P, 8, kv + 32, 1.0, P, 1, P, 1 << 40, None) == SHAPE
+    assert v(P, 1, 4, P, P, None, nv, kv, 1.0, P, 1, P, 1 << 40, None) == NULL   # at the limits
