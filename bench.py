@@ -114,6 +114,29 @@ class Op:
         return e0, e1
 
 
+def same_size_copy_gbs(torch, dev, traffic_bytes, steps):
+    """Read + write GB/s of a plain device copy moving traffic_bytes per call,
+    timed as the calls are: a graph of back-to-back copies over >= 1 GiB of
+    buffers (so no copy is served from the on-die cache), median per copy."""
+    half = traffic_bytes // 2
+    n = max(2, -(-GiB // traffic_bytes))
+    srcs = [torch.zeros(half, dtype=torch.uint8, device=dev) for _ in range(n)]
+    dsts = [torch.empty_like(t) for t in srcs]
+
+    def copy(i):
+        dsts[i].copy_(srcs[i])
+
+    op = Op("copy", copy, n, "GB/s", 2 * half, HBM_PEAK_GBS, "hbm", "copy", None)
+    op.capture(torch)
+    times = []
+    for _ in range(steps):
+        e0, e1 = op.replay_timed(torch)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / n)
+    del op, srcs, dsts
+    return 2 * half / (float(np.median(times)) * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -443,6 +466,13 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * src.numel() * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
+    # and a copy moving as many bytes per call as the decode GEMV (W 27648x5120),
+    # captured and replayed like the calls above: the rate a kernel of that size
+    # reaches, launch ramp and tail included
+    gemv_ops = [op for op in ops if op.name.startswith("gemv_b")]
+    copy_small_gbs = None
+    if gemv_ops:
+        copy_small_gbs = same_size_copy_gbs(torch, dev, gemv_ops[0].per_call, max(args.steps, 3))
 
     traffic = load_traffic()
     comps = {}
@@ -467,6 +497,8 @@ def main():
         comps[op.name].update(op.extra)
         if op.unit == "GB/s":
             comps[op.name]["frac_of_copy"] = round(achieved / copy_gbs, 4)
+        if op in gemv_ops:
+            comps[op.name]["frac_of_same_size_copy"] = round(achieved / copy_small_gbs, 4)
         if op.name in ("gemm_nvfp4", "gemm_nvfp4_e4m3_out", "gemm_nvfp4_nvfp4_out"):
             comps[op.name]["frac_of_fp4_peak"] = round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4)
 
@@ -512,7 +544,10 @@ def main():
         "block_mse": block_mse,
         "rotation_error": rotation_error,
         "context": {"device_copy_GBs_read_plus_write": round(copy_gbs, 1),
-                    "note": "torch copy_ of 512 MiB, for reference against the 8 TB/s peak"},
+                    "note": "torch copy_ of 512 MiB, for reference against the 8 TB/s peak",
+                    "device_copy_gemv_size_GBs": None if copy_small_gbs is None else round(copy_small_gbs, 1),
+                    "gemv_size_note": "torch copy_ moving the GEMV's bytes per call (half read, half "
+                                      "written), as a graph cycling over >= 1 GiB of buffers"},
         "setup_s": round(setup_s, 1),
     }
 
