@@ -75,7 +75,8 @@ constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 
 // Orthonormal 128-point FWHT of the group held by this lane's quad; p = lane's
 // position (0..3) in the quad.
-__device__ __forceinline__ void fwht128(float (&v)[kPer], int p) {
+// Stages h = 1 ... 16: the lane's own 32 channels.
+__device__ __forceinline__ void fwht_in_lane(float (&v)[kPer]) {
 #pragma unroll
   for (int h = 1; h < kPer; h <<= 1) {
 #pragma unroll
@@ -87,6 +88,10 @@ __device__ __forceinline__ void fwht128(float (&v)[kPer], int p) {
       }
     }
   }
+}
+
+__device__ __forceinline__ void fwht128(float (&v)[kPer], int p) {
+  fwht_in_lane(v);
   // h = 32: partner lane p ^ 1.  Lower lane keeps a + b, upper lane a - b,
   // computed as partner + (-own) (the same IEEE operation as a - b).
   {
@@ -107,6 +112,27 @@ __device__ __forceinline__ void fwht128(float (&v)[kPer], int p) {
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) v[j] = v[j] * kNorm;
+}
+
+// max |y| over the lane's 32 outputs of the 128-point transform BEFORE the
+// final multiply by kNorm (the multiply is monotone, so the caller scales the
+// maximum once: max fl(|y| c) = fl(max|y| c)).  Stages up to h = 32 as in
+// fwht128.  At h = 64 only magnitudes are needed: of the two outputs a + b and
+// a - b of a lane pair, the larger magnitude is |a| + |b| exactly before
+// rounding, so max(|fl(a + b)|, |fl(a - b)|) = fl(|a| + |b|), computed by both
+// lanes of the pair.
+__device__ __forceinline__ float fwht128_absmax_unscaled(float (&v)[kPer], int p) {
+  fwht_in_lane(v);
+  const uint32_t neg = (p & 1) ? 0x80000000u : 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const float other = dpp_f<kQuadXor1>(v[j]);
+    v[j] = other + __uint_as_float(__float_as_uint(v[j]) ^ neg);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) m = fmaxf(m, fabsf(dpp_f<kQuadXor2>(v[j])) + fabsf(v[j]));
+  return m;
 }
 
 // ---------------------------------------------------------- Philox4x32-10 --
@@ -188,12 +214,10 @@ __global__ void __launch_bounds__(kThreads)
     if ((int)threadIdx.x >= nb) continue;
     float v[kPer];
     unpack32<BF16>(w, v);
-    fwht128(v, p);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) m = umax(m, __float_as_uint(v[j]) & 0x7fffffffu);
+    m = umax(m, __float_as_uint(fwht128_absmax_unscaled(v, p)));
   }
-  m = block_max_u32(m);
-  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+  m = block_max_u32(m);   // non-negative floats order as their bit patterns
+  if (threadIdx.x == 0) partials[blockIdx.x] = __float_as_uint(__uint_as_float(m) * kNorm);
 }
 
 template <bool BF16, bool SR>
