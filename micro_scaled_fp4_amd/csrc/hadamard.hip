@@ -264,11 +264,13 @@ __global__ void __launch_bounds__(kThreads)
     uint32_t sc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      uint32_t am = 0;
+      // max |v| of the block (float max of magnitudes: the abs folds into the
+      // max instruction's operand modifiers)
+      float am = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[16 * blk + j]) & 0x7fffffffu);
+      for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(v[16 * blk + j]));
       float r;
-      nv_block_scale(__uint_as_float(am), s_global, sc[blk], r);
+      nv_block_scale(am, s_global, sc[blk], r);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int base = 16 * blk + 8 * half;
@@ -383,10 +385,10 @@ __global__ void __launch_bounds__(kThreads)
     float v[kPer];
     unpack32<BF16>(wv, v);
     fwht128(v, p);
-    uint32_t am = 0;
+    float am = 0.0f;   // max |v| (abs folded into the max instruction)
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
-    const uint32_t sc = e8m0_code(am);
+    for (int j = 0; j < kPer; ++j) am = fmaxf(am, fabsf(v[j]));
+    const uint32_t sc = e8m0_code(__float_as_uint(am));
     const float inv = e8m0_inv(sc);
     uint32_t w[4];
 #pragma unroll
