@@ -1,0 +1,83 @@
+"""GPU: every entry point captured in one HIP graph (torch.cuda.CUDAGraph) and
+replayed several times, with new input and unrelated eager work between the
+replays.  Each replay must give exactly the bytes the same calls give eagerly
+on the same input: the calls enqueue no memset nodes, allocate nothing and
+keep no state between calls, so a captured graph is reusable.
+"""
+import numpy as np
+import pytest
+import torch
+
+import micro_scaled_fp4_amd as fp4
+import workloads
+from oracle import fp4_oracle as o
+from gpu_util import announce, to_gpu_bf16
+
+pytestmark = pytest.mark.gpu
+
+R, C = 256, 1024          # activation
+N, K = 520, 1024          # weight: N rows of K
+
+
+def _weights(dev):
+    W = torch.from_numpy(o.bf16_bits_to_f32(workloads.gemm_w(N, K, seed=1201))).to(dev)
+    qw, sw, _, gw = fp4.nvfp4_quantize(W)
+    mq, ms = fp4.mxfp4_quantize(W)
+    return qw, sw, gw, mq, ms
+
+
+def _calls(x, w, offsets, d_amax):
+    """One pass over the entry points on input x (device bf16 [R, C])."""
+    qw, sw, gw, mq, ms = w
+    out = []
+    q, s, G, sg = fp4.nvfp4_quantize(x)                                   # computed amax
+    out += [q, s, G, sg]
+    out += list(fp4.nvfp4_quantize_ex(x, 8, 2))                           # block 8, scale search
+    qm, sm = fp4.mxfp4_quantize(x)
+    out += [qm, sm]
+    out.append(fp4.fp4_dequantize(fp4.FP4_NVFP4, q, s, sg, C, torch.bfloat16))
+    out.append(fp4.fp4_dequantize(fp4.FP4_MXFP4, qm, sm, None, C, torch.float32))
+    out += list(fp4.hadamard_quantize(x, mode=fp4.FP4_SR, seed=77))
+    out += list(fp4.hadamard_quantize_mx(x, mode=fp4.FP4_RNE))
+    out.append(fp4.hadamard_rotate(x, 128, torch.bfloat16))
+    out.append(fp4.fp4_scaled_gemm(fp4.FP4_NVFP4, q, s, sg, qw, sw, gw, K, 1.0, torch.bfloat16))
+    out.append(fp4.fp4_scaled_gemm(fp4.FP4_MXFP4, qm, sm, None, mq, ms, None, K, 0.5, torch.float32))
+    out.append(fp4.fp4_scaled_gemm(fp4.FP4_NVFP4, q, s, sg, qw, sw, gw, K, 0.25, torch.float8_e4m3fn))
+    out += list(fp4.fp4_scaled_gemm_nvfp4_out(fp4.FP4_NVFP4, q, s, sg, qw, sw, gw, K, d_amax))
+    out.append(fp4.fp4_grouped_gemm(fp4.FP4_NVFP4, q, s, sg, torch.stack([qw, qw]), torch.stack([sw, sw]),
+                                    torch.cat([gw, gw]), offsets, K, 1.0, torch.float32))
+    out.append(fp4.fp4_gemv_batched(x[:5], qw, sw, gw, K, 1.0, torch.float32))
+    return out
+
+
+def test_every_call_replays_in_a_graph():
+    announce("graph capture and replay of every entry point")
+    dev = "cuda:0"
+    w = _weights(dev)
+    inputs = [to_gpu_bf16(workloads.activation(R, C, seed=1210 + k)) for k in range(4)]
+    x = inputs[0].clone()                       # the graph's static input buffer
+    offsets = torch.tensor([0, 100, R], dtype=torch.int32, device=dev)
+    d_amax = torch.tensor([3000.0], dtype=torch.float32, device=dev)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):               # first calls outside the capture
+        _calls(x, w, offsets, d_amax)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = _calls(x, w, offsets, d_amax)
+
+    for k in (1, 2, 3, 1):
+        x.copy_(inputs[k])
+        junk = torch.randn(1 << 20, device=dev).sum()   # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        eager = _calls(inputs[k], w, offsets, d_amax)
+        torch.cuda.synchronize()
+        assert len(eager) == len(captured)
+        for i, (a, b) in enumerate(zip(captured, eager)):
+            assert a.dtype == b.dtype and a.shape == b.shape, i
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {k}, output {i}"
+        del junk
