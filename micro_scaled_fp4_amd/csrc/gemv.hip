@@ -23,6 +23,8 @@
 //   scale's power of two, v_pk_mul_f16 its 3-bit mantissa); the K order inside
 //   a step is permuted identically for x' and W.  The waves' partial 16x16
 //   tiles are summed through LDS in a fixed order.
+#include <atomic>
+
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
@@ -665,7 +667,24 @@ __global__ void __launch_bounds__(256) k_zero_fill(int64_t n, T* __restrict__ y)
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) y[i] = 0;
 }
 
-int g_num_cus = 0;
+// Compute units per device (0: not queried yet), cached per device so that
+// calls from several host threads, or on devices of different sizes (compute
+// partitions), each see their own device's count.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];
+
+int num_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_num_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0;
+    n = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0
+            ? cus : 256;
+    g_num_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 struct StreamArgs {
   const void* x;
@@ -716,14 +735,7 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
                        const uint8_t* w_scales, const float* g_w, int64_t N, int64_t K, float g_d,
                        void* y, bool y_bf16, void* workspace, hipStream_t stream) {
   if (N > (1 << 30) || K > (1 << 30)) return hipErrorInvalidValue;
-  if (g_num_cus == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      g_num_cus = cus;
-    else
-      g_num_cus = 256;
-  }
+  const int ncu = num_cus();
   if (K == 0) return launch_zero_fill(y, B * N, y_bf16 ? 2 : 4, stream);
   const int nstrips = (int)((N + 15) / 16);
   // fused streaming kernel when the quantized x fits in LDS
@@ -741,7 +753,7 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   if ((xf16 || lds_fp4 + lds_fixed <= lds_max) && K < (1 << 27)) {
     const int lds_x = (int)(((xf16 ? lds_f16 : lds_fp4) + 15) / 16 * 16);
     const int lds = lds_x + (int)lds_fixed;
-    const int grid = nstrips < g_num_cus ? nstrips : g_num_cus;
+    const int grid = nstrips < ncu ? nstrips : ncu;
     const StreamArgs sa{x, (int)B, W, w_scales, g_w, (int)N, (int)K, (int)Kq, lds_x, g_d, y, y_bf16};
     const int sel = (x_bf16 ? 4 : 0) | (xf16 ? 2 : 0);
     switch (sel * 3 + scm) {
@@ -776,7 +788,7 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   if (spw < 1) spw = 1;
   const int nwaves = (T + spw - 1) / spw;
   const bool resident = spw <= kMaxSteps;
-  const int grid = nstrips < g_num_cus ? nstrips : g_num_cus;
+  const int grid = nstrips < ncu ? nstrips : ncu;
   const dim3 blk(64 * nwaves);
 #define FP4_GEMV_LAUNCH(YB, RES)                                                               \
   hipLaunchKernelGGL((k_gemv_mfma<YB, RES>), dim3(grid), blk, 0, stream, W, w_scales, g_w,     \

@@ -1,9 +1,15 @@
-"""GPU: every entry point captured in one HIP graph (torch.cuda.CUDAGraph) and
-replayed several times, with new input and unrelated eager work between the
-replays.  Each replay must give exactly the bytes the same calls give eagerly
-on the same input: the calls enqueue no memset nodes, allocate nothing and
-keep no state between calls, so a captured graph is reusable.
+"""GPU: the calls' execution model.
+
+- Every entry point captured in one HIP graph (torch.cuda.CUDAGraph) and
+  replayed several times, with new input and unrelated eager work between the
+  replays.  Each replay must give exactly the bytes the same calls give eagerly
+  on the same input: the calls enqueue no memset nodes, allocate nothing and
+  keep no state between calls, so a captured graph is reusable.
+- Calls issued at the same time from two host threads, each on its own
+  stream, give exactly the bytes of the same calls made one after another.
 """
+import threading
+
 import numpy as np
 import pytest
 import torch
@@ -81,3 +87,46 @@ def test_every_call_replays_in_a_graph():
             assert a.dtype == b.dtype and a.shape == b.shape, i
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {k}, output {i}"
         del junk
+
+
+def test_concurrent_calls_from_two_threads_on_two_streams():
+    announce("two host threads, two streams")
+    dev = "cuda:0"
+    w = _weights(dev)
+    qw, sw, gw = w[0], w[1], w[2]
+    xs = [to_gpu_bf16(workloads.activation(R, C, seed=1300 + i)) for i in range(2)]
+
+    def work(x):
+        q, s, G, sg = fp4.nvfp4_quantize(x)
+        out = [q, s, G, sg, fp4.fp4_gemv_batched(x[:8], qw, sw, gw, K, 1.0, torch.float32)]
+        out += list(fp4.hadamard_quantize(x, mode=fp4.FP4_SR, seed=5))
+        out.append(fp4.fp4_scaled_gemm(fp4.FP4_NVFP4, q, s, sg, qw, sw, gw, K, 1.0, torch.float32))
+        return out
+
+    serial = [work(x) for x in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    results, errors = [None, None], []
+    barrier = threading.Barrier(2, timeout=30)
+
+    def run(i):
+        try:
+            torch.cuda.set_device(0)
+            barrier.wait()
+            with torch.cuda.stream(streams[i]):
+                for _ in range(8):
+                    results[i] = work(xs[i])
+            streams[i].synchronize()
+        except Exception as e:          # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,), daemon=True) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    assert all(not t.is_alive() for t in threads)
+    for i in range(2):
+        for j, (a, b) in enumerate(zip(results[i], serial[i])):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (i, j)
