@@ -205,3 +205,22 @@ def test_contraction_size_limits_are_shape_errors():
     assert v(P, 1, 4, P, P, P, nv + 1, 512, 1.0, P, 1, P, 1 << 20, None) == SHAPE
     assert v(P, 1, 4, P, P, P, 8, kv + 32, 1.0, P, 1, P, 1 << 40, None) == SHAPE
     assert v(P, 1, 4, P, P, None, nv, kv, 1.0, P, 1, P, 1 << 40, None) == NULL   # at the limits
+
+
+def test_no_cpu_fallback():
+    """The binding has no CPU path: host tensors are rejected, and a missing
+    library is an error at the first call, not a silent fallback."""
+    import subprocess
+    import sys
+    import torch
+    with pytest.raises(ValueError):
+        m.nvfp4_quantize(torch.zeros(4, 16))
+    with pytest.raises(ValueError):
+        m.mxfp4_quantize(torch.zeros(4, 32, dtype=torch.bfloat16))
+    with pytest.raises(RuntimeError):
+        m.load_library("/nonexistent/libfp4.so")
+    code = ("import micro_scaled_fp4_amd as m\n"
+            "try:\n    m.load_library()\nexcept RuntimeError as e:\n    print('raised', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120,
+                       env={**os.environ, "FP4_LIBRARY": "/nonexistent/libfp4.so"})
+    assert r.returncode == 0 and r.stdout.startswith("raised"), (r.stdout, r.stderr)
