@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", default="", help="comma list of call names to run (profiling)")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the step: throughput against size of the GEMV (B = 1, K = 5120) "
+                        "and the static NVFP4 quantize (8192 columns), one JSON line per size")
     return p.parse_args()
 
 
@@ -114,6 +117,55 @@ class Op:
         return e0, e1
 
 
+def size_sweep(torch, fp4, dev, reps):
+    """Throughput against size: each size timed as the step's calls are (a
+    graph of back-to-back calls over >= 1 GiB of inputs, median per call), on
+    uniformly random valid codes and scale bytes (GEMV) or N(0,1) bf16 (quantize)."""
+    def timed(fn, n):
+        op = Op("sweep", fn, n, "GB/s", 0, HBM_PEAK_GBS, "hbm", "", None)
+        op.capture(torch)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = op.replay_timed(torch)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / n)
+        return float(np.median(ts)) * 1e3
+
+    def line(d, nbytes, us):
+        d.update({"bytes_per_call": nbytes, "us_median": round(us, 2),
+                  "GB_per_s": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        print(json.dumps(d), flush=True)
+
+    seed = 1400
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    K = 5120
+    gw = torch.tensor([0.02], dtype=torch.float32, device=dev)
+    x = torch.randn(1, K, device=dev, dtype=torch.bfloat16, generator=gen)
+    ws = torch.empty(fp4.gemv_workspace_bytes(1, K), dtype=torch.uint8, device=dev)
+    for N in (6912, 13824, 27648, 55296, 110592, 221184):
+        wbytes = N * (K // 2 + K // 16)
+        n = max(2, -(-GiB // wbytes))
+        Ws = [torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=gen) for _ in range(n)]
+        Ss = [torch.randint(0x18, 0x58, (N, K // 16), dtype=torch.uint8, device=dev, generator=gen)
+              for _ in range(n)]
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+        us = timed(lambda i: fp4.fp4_gemv_batched(x, Ws[i], Ss[i], gw, K, 1.0, torch.bfloat16,
+                                                  workspace=ws, out=y), n)
+        line({"call": "gemv_b1", "N": N, "K": K, "seed": seed}, wbytes + 4 + 2 * K + 2 * N, us)
+        del Ws, Ss
+        torch.cuda.empty_cache()
+    C = 8192
+    amax = torch.tensor([40.0], dtype=torch.float32, device=dev)
+    for R in (256, 1024, 4096, 8192, 32768):
+        n = max(2, -(-GiB // (2 * R * C)))
+        Xs = [torch.randn(R, C, device=dev, dtype=torch.bfloat16, generator=gen) for _ in range(n)]
+        us = timed(lambda i: fp4.nvfp4_quantize(Xs[i], amax=amax), n)
+        line({"call": "nvfp4_quantize_static", "rows": R, "cols": C, "seed": seed},
+             2 * R * C + R * C // 2 + R * C // 16 + 8, us)
+        del Xs
+        torch.cuda.empty_cache()
+
+
 def same_size_copy_gbs(torch, dev, traffic_bytes, steps):
     """Read + write GB/s of a plain device copy moving traffic_bytes per call,
     timed as the calls are: a graph of back-to-back copies over >= 1 GiB of
@@ -150,6 +202,9 @@ def main():
     import workloads
 
     lib = fp4.load_library()
+    if args.sweep:
+        size_sweep(torch, fp4, "cuda:0", max(args.steps, 5))
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     only = set(filter(None, args.only.split(",")))
