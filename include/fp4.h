@@ -46,7 +46,8 @@ typedef enum {
   FP4_ERR_ALIGN = 4,     /* a pointer misses the alignment the call states    */
   FP4_ERR_ARCH = 5,      /* current device is not gfx950                      */
   FP4_ERR_WORKSPACE = 6, /* workspace missing or smaller than required        */
-  FP4_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed        */
+  FP4_ERR_HIP = 7,       /* a HIP runtime call or kernel launch failed        */
+  FP4_ERR_ALIAS = 8      /* an output aliases an input the call reads         */
 } fp4_status;
 
 /* FP4_E4M3 (one FP8 E4M3 byte per value) is valid only as fp4_scaled_gemm's output. */
@@ -207,7 +208,7 @@ fp4_status fp4_scaled_gemm(fp4_format fmt, const uint8_t* A, const uint8_t* a_sc
  * Dq, d_scales and d_global_scale are exactly what nvfp4_quantize with
  * amax_given writes for the float32 result D = fl(acc * alpha) that
  * fp4_scaled_gemm produces for the same operands, bit for bit.  d_amax must not
- * alias d_global_scale.  M == 0 or N == 0 is a no-op; K == 0 encodes D = 0
+ * alias d_global_scale (FP4_ERR_ALIAS).  M == 0 or N == 0 is a no-op; K == 0 encodes D = 0
  * (codes 0, scale bytes 0) without reading the operands.  Errors as for
  * fp4_scaled_gemm; NULL d_amax, d_scales or d_global_scale -> FP4_ERR_NULL.
  */

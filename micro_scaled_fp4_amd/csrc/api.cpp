@@ -102,6 +102,7 @@ const char* fp4_status_string(fp4_status s) {
     case FP4_ERR_ARCH: return "current device is not gfx950 (MI355X)";
     case FP4_ERR_WORKSPACE: return "workspace missing or too small";
     case FP4_ERR_HIP: return "HIP runtime error";
+    case FP4_ERR_ALIAS: return "an output aliases an input it must not alias";
   }
   return "unknown status";
 }
@@ -221,6 +222,9 @@ fp4_status fp4_scaled_gemm_nvfp4_out(fp4_format fmt, const uint8_t* A, const uin
   if (Dq == nullptr || d_scales == nullptr || d_amax == nullptr || d_global_scale == nullptr)
     return FP4_ERR_NULL;
   if (!aligned(d_amax, 4) || !aligned(d_global_scale, 4)) return FP4_ERR_ALIGN;
+  // workgroup 0 writes *d_global_scale while the others still read *d_amax
+  if (static_cast<const void*>(d_amax) == static_cast<const void*>(d_global_scale))
+    return FP4_ERR_ALIAS;
   if (K == 0) {   // empty contraction: D = 0 encodes as codes 0 and scale bytes 0
     fp4_status st = check_arch();
     if (st != FP4_OK) return st;

@@ -16,6 +16,10 @@ namespace fp4dev {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------- bf16 --
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -124,6 +128,35 @@ __device__ __forceinline__ void nv_block_scale(float Ab, float s_global, uint32_
   code = e4m3_code(t);
   float sb = s_global * e4m3_value(code);
   r = sb != 0.0f ? 1.0f / sb : 0.0f;
+}
+
+// f16 pair (h, h), h = E4M3 value * 2^-8 exactly: the byte's exponent and
+// mantissa fields drop into the f16 fields (bias 7 against 15 gives the 2^-8;
+// E4M3 subnormals land on f16 subnormals), its sign on the sign.  Bytes
+// 0x7f / 0xff (NaN) read as +-480; quantizers never emit them.
+__device__ __forceinline__ f16x2 e4m3_h2(uint32_t byte) {
+  const uint32_t h = ((byte & 0x80u) << 8) | ((byte & 0x7fu) << 7);
+  return __builtin_bit_cast(f16x2, h | (h << 16));
+}
+
+// f16 pair (h(b0), h(b1)) of the two E4M3 bytes of 16-bit word SEL of w, the
+// same h as e4m3_h2 for every finite byte (v_cvt_scalef32_pk_f16_fp8 with the
+// scale 2^-8, one instruction for two bytes; a NaN byte gives NaN).
+template <bool SEL>
+__device__ __forceinline__ f16x2 e4m3_pair_h(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 0x1p-8f, SEL);
+}
+
+// The 8 values E2M1(code) * E4M3 of one dword of codes (value 2j in the low
+// nibble of byte j), given s = e4m3_h2 of the scale byte: the conversion
+// scales the codes by 2^8 (exact) and the f16 product with E4M3 * 2^-8 is
+// exact (at most 6 significant bits, magnitude in [2^-10, 2688]).
+__device__ __forceinline__ f16x8 dq8(uint32_t codes, f16x2 s) {
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s;
+  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // ---------------------------------------------------------------- E8M0 --

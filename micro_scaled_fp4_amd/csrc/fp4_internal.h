@@ -7,7 +7,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fp4impl {
+
+// Raises kernel fn's dynamic-LDS limit to `bytes` on the current device, once
+// per device: `done` is the caller's set of devices (bit d for device d < 64)
+// on which that kernel's limit is already set.  Thread-safe: two first calls
+// racing may both set the attribute, which is idempotent, and a device bit is
+// published only after its attribute call succeeded.  Devices >= 64 set it on
+// every call.
+inline hipError_t set_lds_limit_once(std::atomic<uint64_t>& done, const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 constexpr int kAmaxPartials = 1024;  // FP4_AMAX_WORKSPACE_BYTES / 4
 

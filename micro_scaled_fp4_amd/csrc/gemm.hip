@@ -41,6 +41,7 @@
 // each XCD is given a contiguous range of tiles; tiles are visited in groups
 // of 8 row-tiles so concurrently running workgroups of an XCD share operand
 // rows in its L2.
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -280,7 +281,7 @@ __device__ __forceinline__ void load_scales(StageScales<MX>& r, __amdgpu_buffer_
   const int kb = k0 / bs;
   const int sr = threadIdx.x;
   if (SCALE_VEC) {   // K % 256 == 0 and 16-byte aligned scale rows
-    if (MX) {
+    if constexpr (MX) {
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(scales, sr * nsc + kb, 0, 0);
       r.s[0] = v.x;
       r.s[1] = v.y;
@@ -323,27 +324,6 @@ __device__ __forceinline__ void store_scales(const StageScales<MX>& r, uint8_t* 
     else
       reinterpret_cast<uint32_t*>(sc)[e] = r.s[g];
   }
-}
-
-// --------------------------------------------------------- NV fragment dequant --
-// f16 pair (h, h), h = E4M3 value * 2^-8 exactly: the byte's exponent and
-// mantissa fields drop into the f16 fields (bias 7 against 15 gives the 2^-8;
-// E4M3 subnormals land on f16 subnormals), its sign on the sign.  Bytes
-// 0x7f / 0xff (NaN) read as +-480; quantizers never emit them.
-__device__ __forceinline__ v2h e4m3_h2(uint32_t byte) {
-  const uint32_t h = ((byte & 0x80u) << 8) | ((byte & 0x7fu) << 7);
-  return __builtin_bit_cast(v2h, h | (h << 16));
-}
-
-// The 8 values E2M1(code) * E4M3 of one dword of codes: the conversion scales by
-// 2^8 (exact) and the f16 product with E4M3 * 2^-8 is exact (at most 6
-// significant bits, magnitude in [2^-10, 2688]).
-__device__ __forceinline__ v8h dq8(uint32_t codes, v2h s) {
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s;
-  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // ---------------------------------------------------------------- epilogue --
@@ -490,7 +470,6 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int r16 = lane & 15, g = lane >> 4;
-  constexpr int spr = Cfg<MX>::kScaleRow;
   constexpr int bs = MX ? 32 : 16;
   const int rowb = K / 2, nsc = K / bs;
 
@@ -834,13 +813,10 @@ hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const
   // grouped: each group adds at most one partial row tile to ceil(M / BM)
   const int tiles_m = (M + BM - 1) / BM + (GROUPED ? gr.ngroups : 0);
   constexpr int lds = Cfg<MX>::kLdsBytes;
-  static bool attr_set = false;   // per process; the attribute is per function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MX, OUT, SCALE_VEC, GROUPED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};   // devices on which this kernel's LDS limit is set
+  const hipError_t e = fp4impl::set_lds_limit_once(
+      lds_set, reinterpret_cast<const void*>(&k_gemm<MX, OUT, SCALE_VEC, GROUPED>), lds);
+  if (e != hipSuccess) return e;
   // 4 outputs per store when every row start is aligned to 4 outputs
   // (NVFP4: 4 outputs are 2 bytes)
   const bool vec_out =

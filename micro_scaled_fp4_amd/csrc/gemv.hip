@@ -44,8 +44,6 @@ constexpr int kMaxSteps = 3;           // 128-value steps per wave kept in regis
 
 inline int64_t kpad(int64_t K) { return (K + 127) / 128 * 128; }
 
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
 // -------------------------------------------------------------- x prologue --
 template <bool BF16>
 __global__ void __launch_bounds__(kPrepThreads)
@@ -307,6 +305,7 @@ constexpr int kSlots = kStreamWaves / kSplit;   // strips per workgroup and roun
 constexpr int kPairs = 4;                       // pairs of steps in flight per wave
 constexpr int kXRegVecs = 4;                    // 16-byte x vectors per thread held in registers
 constexpr int kRedBytes = 2 * kSlots * 64 * 16; // double-buffered partial tiles
+constexpr int kStreamLdsMax = 160 * 1024 - 256;  // dynamic LDS (the kernel's static LDS is 64 bytes)
 
 __host__ __device__ inline int xf16_row_bytes(int Kq) {
   const int base = Kq * 2 + Kq / 4;
@@ -322,34 +321,6 @@ __device__ __forceinline__ uint32_t block_max_1024(uint32_t v, uint32_t* red) {
   for (int i = 0; i < kStreamWaves; ++i) r = umax(r, red[i]);
   __syncthreads();
   return r;
-}
-
-// f16 pair (h, h) for one E4M3 byte, h = E4M3 value * 2^-8 exactly: the byte's
-// exponent and mantissa fields drop into the f16 fields (bias 7 against 15
-// gives the 2^-8, E4M3 subnormals land on f16 subnormals) and its sign bit on
-// the sign.  Bytes 0x7f / 0xff (NaN) read as +-480; quantizers never emit them.
-__device__ __forceinline__ v2h e4m3_h2(uint32_t byte) {
-  const uint32_t h = ((byte & 0x80u) << 8) | ((byte & 0x7fu) << 7);
-  return __builtin_bit_cast(v2h, h | (h << 16));
-}
-
-// f16 pair (h(b0), h(b1)) of the two E4M3 bytes of 16-bit word SEL of w, the
-// same h as e4m3_h2 for every finite byte (v_cvt_scalef32_pk_f16_fp8 with the
-// scale 2^-8, one instruction for two bytes; a NaN byte gives NaN).
-template <bool SEL>
-__device__ __forceinline__ v2h e4m3_pair_h(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 0x1p-8f, SEL);
-}
-
-// The 8 values E2M1(code) * E4M3 of one dword of codes: the conversion scales
-// by 2^8 (exact), and the f16 product with E4M3 * 2^-8 is exact (at most 6
-// significant bits, magnitude in [2^-10, 2688]).
-__device__ __forceinline__ v8h dq8(uint32_t codes, v2h s) {
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s;
-  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // K order inside a pair (256 values of a 16-row strip): lane (b = l % 16,
@@ -700,9 +671,12 @@ struct StreamArgs {
 
 template <bool XB, bool XF, int SCM>
 hipError_t launch_stream(const StreamArgs& a, int grid, int lds, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&k_gemv_stream<XB, XF, SCM>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  // the limit is set once per device to the most any call of this kernel uses
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = fp4impl::set_lds_limit_once(
+      lds_set, reinterpret_cast<const void*>(&k_gemv_stream<XB, XF, SCM>), kStreamLdsMax);
   if (e != hipSuccess) return e;
+  if (lds > kStreamLdsMax) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_gemv_stream<XB, XF, SCM>), dim3(grid), dim3(kStreamThreads), lds, stream,
                      a.x, a.B, a.W, a.w_scales, a.g_w, a.N, a.K, a.Kq, a.lds_x, a.g_d, a.y, a.y_bf16);
   return hipGetLastError();
@@ -746,7 +720,7 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   if (K % 64 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 4 == 0) scm = kScaleDword;
   if (K % 256 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 16 == 0) scm = kScaleGroup;
   const int64_t lds_fixed = kStreamWaves * 2048 + kRedBytes + kStreamWaves * 1024;
-  const int64_t lds_max = 160 * 1024 - 256;
+  const int64_t lds_max = kStreamLdsMax;
   const bool xf16 = lds_f16 + lds_fixed <= lds_max;
   // (the strip-relative buffer offsets need 16 rows of W to span < 2^31 bytes;
   // the x' sizes above already keep K far below that)

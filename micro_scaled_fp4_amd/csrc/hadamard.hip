@@ -27,8 +27,6 @@ constexpr int kMaxGrid = 2048;
 constexpr int kPer = 32;             // channels per lane
 constexpr float kNorm = 0x1.6a09e6p-4f;  // fl32(1/sqrt(128)) = 0.0883883461...
 
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
   __shared__ uint32_t red[kThreads / 64];
   v = wave_max_u32(v);

@@ -29,8 +29,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
 // Workgroup max of a u32 (every thread gets the result).
 template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {

@@ -632,6 +632,71 @@ def gemm_nvfp4_output(D_f32: np.ndarray, amax):
     return nvfp4_quantize(np.asarray(D_f32, dtype=F32), amax=amax)
 
 
+def f32_interval(D_ref, tol):
+    """Every float32 value v with |v - D_ref| <= tol lies in [lo, hi], with lo, hi
+    the float32 roundings of D_ref -+ tol (rounding to float32 is monotone, and
+    v is its own rounding).  tol is widened by a relative 1e-6 so that neither
+    the float64 rounding of D_ref -+ tol nor the float64 summation error of a
+    reference dot product can move an end inside.  Returns float32 (lo, hi)."""
+    D = np.asarray(D_ref, dtype=F64)
+    t = np.asarray(tol, dtype=F64) * (1.0 + 1e-6)
+    return (D - t).astype(F32), (D + t).astype(F32)
+
+
+def e4m3_output_range(D_ref, tol):
+    """Values the GEMM's E4M3 output can take when its float32 result lies within
+    tol of the exact D_ref ([MS] section 五: the scaled-mm output written as
+    float8_e4m3fn after g_d): [E4M3(lo), E4M3(hi)] decoded, (lo, hi) =
+    f32_interval(D_ref, tol).  The encoder (sign, then the nearest magnitude,
+    saturating) never decreases with its input, so every float32 in [lo, hi]
+    encodes to a value inside the range; equal ends fix the output value (a
+    zero's sign is fixed only when lo and hi have one sign).
+    Returns float64 (v_lo, v_hi)."""
+    lo, hi = f32_interval(D_ref, tol)
+    return e4m3_decode(e4m3_encode_signed(lo)), e4m3_decode(e4m3_encode_signed(hi))
+
+
+def _nv_scale_byte(block_amax, s_global):
+    """E4M3 block-scale byte of nvfp4_quantize's step 2 for block amaxes A_b."""
+    A_b = np.asarray(block_amax, dtype=F32)
+    t = ((A_b / F32(6.0)).astype(F32) / F32(s_global)).astype(F32)
+    return e4m3_encode_rne_sat(t)
+
+
+def nvfp4_output_range(D_ref, tol, amax):
+    """NVFP4 encodings ([LPF] two-level scaling, blocks of 16 along N, tensor
+    amax given) of every float32 result that lies within tol of the exact
+    D_ref [M, N].  With (lo, hi) = f32_interval(D_ref, tol):
+      * s_global = fl(amax / 2688) (1 when amax is 0) is fixed;
+      * a block's amax lies between the largest of its elements' smallest
+        possible magnitudes (0 when lo <= 0 <= hi) and the largest of their
+        largest; the scale byte never decreases with the block amax, so it
+        lies in [byte_lo, byte_hi] (the bytes of those two amaxes);
+      * at scale byte c, with r = fl(1 / fl(s_global * E4M3(c))) >= 0, an
+        element's E2M1 value E2M1(fl(x * r)) never decreases with x, so it lies
+        in [E2M1(fl(lo * r)), E2M1(fl(hi * r))].
+    Returns (s_global, byte_lo [M, nb], byte_hi [M, nb], (v_lo, v_hi) at byte_lo,
+    (v_lo, v_hi) at byte_hi), element values float64 [M, N]."""
+    lo, hi = f32_interval(D_ref, tol)
+    M, N = lo.shape
+    s_global = nv_global_scale(F32(amax))
+    straddle = (lo <= 0) & (hi >= 0)
+    a_small = np.where(straddle, F32(0.0), np.minimum(np.abs(lo), np.abs(hi))).astype(F32)
+    a_large = np.maximum(np.abs(lo), np.abs(hi)).astype(F32)
+    byte_lo = _nv_scale_byte(np.max(_blocks(a_small, NV_BLOCK), axis=-1), s_global)
+    byte_hi = _nv_scale_byte(np.max(_blocks(a_large, NV_BLOCK), axis=-1), s_global)
+
+    def values_at(sbyte):
+        s_b = (s_global * e4m3_decode(sbyte).astype(F32)).astype(F32)
+        nz = s_b != 0
+        r = np.where(nz, F32(1.0) / np.where(nz, s_b, F32(1.0)), F32(0.0)).astype(F32)
+        r = np.repeat(r, NV_BLOCK, axis=1)[:, :N]
+        return (e2m1_decode(e2m1_encode_rne((lo * r).astype(F32))),
+                e2m1_decode(e2m1_encode_rne((hi * r).astype(F32))))
+
+    return s_global, byte_lo, byte_hi, values_at(byte_lo), values_at(byte_hi)
+
+
 def gemm_within_tolerance(D, D_ref, mag, out_bf16: bool = False):
     """Acceptance rule for GEMM/GEMV outputs: fp32 outputs within 1e-5 of the
     magnitude sum; bf16 outputs additionally allowed one bf16 rounding of D_ref."""

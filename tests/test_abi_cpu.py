@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "fp4.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(m.LIB_PATH), reason="libfp4.so not built")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, ARCH, WORKSPACE, HIP = range(8)
+OK, NULL, SHAPE, DTYPE, ALIGN, ARCH, WORKSPACE, HIP, ALIAS = range(9)
 
 
 def declared_functions():
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = m.load_library()
-    for s in range(8):
+    for s in range(9):
         assert lib.fp4_status_string(s)
     assert b"gfx950" in lib.fp4_status_string(ARCH)
 
@@ -116,16 +116,20 @@ def test_e4m3_dtype_is_a_gemm_output_only():
 def test_gemm_nvfp4_out_argument_errors():
     lib = m.load_library()
     g = lib.fp4_scaled_gemm_nvfp4_out
-    assert g(2, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == DTYPE
-    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 48, P, P, P, P, None) == SHAPE      # K % 32
-    assert g(0, P, P, P, P, P, P, 1.0, -1, 8, 64, P, P, P, P, None) == SHAPE
-    assert g(1, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == DTYPE      # MX: no g_a/g_b
-    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, None, P, None) == NULL    # d_amax
-    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, None, P, P, None) == NULL    # d_scales
+    S = ctypes.c_void_p(8192)    # d_global_scale, distinct from d_amax (P)
+    assert g(2, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, S, None) == DTYPE
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 48, P, P, P, S, None) == SHAPE      # K % 32
+    assert g(0, P, P, P, P, P, P, 1.0, -1, 8, 64, P, P, P, S, None) == SHAPE
+    assert g(1, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, S, None) == DTYPE      # MX: no g_a/g_b
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, None, S, None) == NULL    # d_amax
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, None, P, S, None) == NULL    # d_scales
     assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, None, None) == NULL    # d_global_scale
-    assert g(0, P, P, None, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == NULL    # g_a
-    assert g(0, ctypes.c_void_p(4104), P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == ALIGN
-    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, ctypes.c_void_p(4098), P, None) == ALIGN
+    assert g(0, P, P, None, P, P, P, 1.0, 8, 8, 64, P, P, P, S, None) == NULL    # g_a
+    assert g(0, ctypes.c_void_p(4104), P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, S, None) == ALIGN
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, ctypes.c_void_p(4098), S, None) == ALIGN
+    # d_amax aliasing d_global_scale: workgroup 0 would overwrite the amax others read
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 64, P, P, P, P, None) == ALIAS
+    assert g(0, P, P, P, P, P, P, 1.0, 8, 8, 0, P, P, S, S, None) == ALIAS       # K = 0 too
     assert g(0, None, None, None, None, None, None, 1.0, 0, 8, 64, None, None, None, None, None) == OK
 
 

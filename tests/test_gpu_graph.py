@@ -8,6 +8,7 @@
 - Calls issued at the same time from two host threads, each on its own
   stream, give exactly the bytes of the same calls made one after another.
 """
+import os
 import threading
 
 import numpy as np
@@ -130,3 +131,69 @@ def test_concurrent_calls_from_two_threads_on_two_streams():
     for i in range(2):
         for j, (a, b) in enumerate(zip(results[i], serial[i])):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (i, j)
+
+
+_FIRST_CALLS = r'''
+import sys, threading
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import micro_scaled_fp4_amd as fp4
+import workloads
+dev = "cuda:0"
+torch.cuda.init()
+M, N, K = 300, 520, 1024
+qa = torch.from_numpy(workloads.random_codes((M, K // 2), 1))
+qw = torch.from_numpy(workloads.random_codes((N, K // 2), 2))
+sa = torch.from_numpy(workloads.random_bytes((M, K // 16), 0x20, 0x50, 3))
+sw = torch.from_numpy(workloads.random_bytes((N, K // 16), 0x20, 0x50, 4))
+sam = torch.from_numpy(workloads.random_bytes((M, K // 32), 120, 134, 5))
+swm = torch.from_numpy(workloads.random_bytes((N, K // 32), 120, 134, 6))
+qa, qw, sa, sw, sam, swm = (t.to(dev) for t in (qa, qw, sa, sw, sam, swm))
+g = torch.ones(1, dtype=torch.float32, device=dev)
+x = torch.from_numpy(workloads.normal((4, K), 7)).to(dev).to(torch.bfloat16)
+torch.cuda.synchronize()
+
+def work():
+    return [fp4.fp4_scaled_gemm(fp4.FP4_NVFP4, qa, sa, g, qw, sw, g, K, 1.0, torch.bfloat16),
+            fp4.fp4_scaled_gemm(fp4.FP4_MXFP4, qa, sam, None, qw, swm, None, K, 1.0, torch.float32),
+            fp4.fp4_gemv_batched(x, qw, sw, g, K, 1.0, torch.float32)]
+
+streams = [torch.cuda.Stream() for _ in range(2)]
+results, errors = [None, None], []
+barrier = threading.Barrier(2, timeout=60)
+
+def run(i):
+    try:
+        torch.cuda.set_device(0)
+        with torch.cuda.stream(streams[i]):
+            barrier.wait()             # both threads make the library's first calls together
+            results[i] = work()
+        streams[i].synchronize()
+    except Exception as e:
+        errors.append(repr(e))
+
+threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+for t in threads: t.start()
+for t in threads: t.join(timeout=90)
+assert not errors, errors
+assert all(not t.is_alive() for t in threads)
+serial = work()
+torch.cuda.synchronize()
+for i in range(2):
+    for a, b in zip(results[i], serial):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+print("first-calls-ok", flush=True)
+'''
+
+
+def test_first_calls_of_a_fresh_process_from_two_threads():
+    """The library's very first GEMM (NVFP4 and MXFP4) and GEMV calls in a
+    fresh process, made at the same time from two host threads on two streams
+    (each kernel's one-time per-device setup races), give the serial results."""
+    import subprocess
+    import sys
+    announce("fresh process: first calls from two threads")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALLS, root], capture_output=True, text=True,
+                       timeout=110)
+    assert r.returncode == 0 and "first-calls-ok" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]

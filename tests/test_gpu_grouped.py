@@ -2,8 +2,9 @@
 layer) against the float64 oracle.
 
 Pass rule as for fp4_scaled_gemm: |D - D_ref| <= 1e-5 * |g_d| * sum_k |a * w|
-(float32 output), plus one bf16 rounding (bf16 output); E4M3 output bit-exact
-against the oracle's encoding of the kernel's float32 output.  Each group's
+(float32 output), plus one bf16 rounding (bf16 output); E4M3 output: every byte
+admissible under that rule around the float64 reference (requant_checks), and
+bit-exact against the oracle's encoding of the kernel's float32 output.  Each group's
 rows must also equal fp4_scaled_gemm of those rows bit for bit.
 """
 import numpy as np
@@ -14,6 +15,7 @@ import micro_scaled_fp4_amd as fp4
 import workloads
 from oracle import fp4_oracle as o
 from gpu_util import announce, to_gpu_u8
+from requant_checks import check_e4m3_against_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -80,7 +82,12 @@ def test_grouped_gemm_matches_oracle(fmt, case):
         assert ok, f"max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
     D32 = _gpu_grouped(fmt, ops, K, 0.25, torch.float32)
     D8 = _gpu_grouped(fmt, ops, K, 0.25, torch.float8_e4m3fn)
-    assert np.array_equal(D8.view(torch.uint8).cpu().numpy(), o.gemm_e4m3_output(D32.cpu().numpy()))
+    codes = D8.view(torch.uint8).cpu().numpy()
+    ref, mag = o.grouped_gemm_ref(A, W, ops[6], 0.25)
+    rows = ~np.isnan(ref[:, 0])     # rows inside some group
+    assert o.gemm_within_tolerance(D32.cpu().numpy()[rows], ref[rows], mag[rows])[0]
+    check_e4m3_against_reference(codes[rows], ref[rows], mag[rows], f"grouped {fmt} case {case}")
+    assert np.array_equal(codes, o.gemm_e4m3_output(D32.cpu().numpy()))
 
 
 @pytest.mark.parametrize("fmt", ["nv", "mx"])

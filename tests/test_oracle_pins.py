@@ -570,6 +570,26 @@ def test_tolerance_rule_and_gemv_reference():
     assert np.array_equal(y, Dy) and y.shape == (4, 64)
 
 
+def test_gemv_reference_one_tensor_scale_hand_worked(golden):
+    """gemv_ref quantizes all rows of x with one tensor scale: two rows of very
+    different magnitude (2688 and 1.0) give the hand-worked outputs of
+    tests/golden/gemv_tensor_scale.txt, which differ from per-row scaling."""
+    (row,) = golden("gemv_tensor_scale.txt")
+    x0, x1 = float(row[0]), float(row[1])
+    w0c, w0s = int(row[2]), int(row[3], 16)
+    w1c = [int(c) for c in row[4].split(",")]
+    w1s, g_w, g_d = int(row[5], 16), float(row[6]), float(row[7])
+    want = np.array([[float(row[8]), float(row[9])], [float(row[10]), float(row[11])]])
+    K = 16
+    x = np.array([[x0] * K, [x1] * K], F32)
+    codes = np.array([[w0c] * K, [w1c[i % 2] for i in range(K)]], np.uint8)
+    Wq = o.pack_nibbles(codes)
+    Ws = np.array([[w0s], [w1s]], np.uint8)
+    y, mag = o.gemv_ref(x, Wq, Ws, F32(g_w), g_d, K)
+    assert np.array_equal(y, want), y
+    assert np.array_equal(mag, np.abs(want))
+
+
 # ------------------------------------------------ NVFP4 scale variants ------
 def test_nvfp4_ex_defaults_are_nvfp4_quantize():
     x = np.random.default_rng(11).standard_normal((33, 200)).astype(F32)
