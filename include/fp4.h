@@ -99,6 +99,27 @@ fp4_status nvfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t col
                           float* global_scale, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/*
+ * nvfp4_quantize_no_workspace -- nvfp4_quantize without the workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The caller still owns
+ * x, q, scales, global_amax and global_scale; with amax_given == 0 the first
+ * pass writes its partial maxima into an array the library keeps on each device
+ * it runs on (FP4_AMAX_WORKSPACE_BYTES, held until the process ends) instead of
+ * a workspace.  The call allocates nothing and calls no allocating routine.
+ * That array is shared by every call on a device and keeps the last call's
+ * contents: calls that overlap on one device (concurrent streams, or host
+ * threads enqueuing on different streams) race and must be serialized by the
+ * caller.  Every size fits (the first pass uses at most 1024 workgroups, one
+ * partial each, and writes every partial the second pass reads, so nothing has
+ * to start at zero).  Arguments, outputs and errors as nvfp4_quantize, with a
+ * failed lookup of the array returning FP4_ERR_HIP; the outputs are
+ * bit-identical to nvfp4_quantize's.
+ */
+fp4_status nvfp4_quantize_no_workspace(const void* x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                       uint8_t* q, uint8_t* scales, float* global_amax,
+                                       int amax_given, float* global_scale, hipStream_t stream);
+
 /* Widest scale search of nvfp4_quantize_ex: +-126 codes covers every finite E4M3 byte. */
 #define FP4_MAX_SCALE_SEARCH 126
 

@@ -34,6 +34,8 @@ _c_p = ctypes.c_void_p
 SIGNATURES = {
     "nvfp4_quantize": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p,
                                       ctypes.c_int, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "nvfp4_quantize_no_workspace": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p,
+                                                   _c_p, ctypes.c_int, _c_p, _c_p]),
     "nvfp4_quantize_ex": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_i64, ctypes.c_int,
                                          ctypes.c_int, _c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_p,
                                          ctypes.c_size_t, _c_p]),
@@ -157,6 +159,32 @@ def nvfp4_quantize(x: torch.Tensor, amax=None, workspace: Optional[torch.Tensor]
                             0 if workspace is None else workspace.numel() * workspace.element_size(),
                             _stream(dev))
     _check(st, "nvfp4_quantize")
+    return q, sc, a, g_scale
+
+
+def nvfp4_quantize_no_workspace(x: torch.Tensor, amax=None, out=None):
+    """nvfp4_quantize through the allocation-free entry point: the dynamic amax
+    pass uses the library's own device array, so the C call allocates nothing.
+    out: optional (codes, scales, amax f32[1], s_global f32[1]) tensors to write
+    into (then this function allocates nothing either; with amax given, out[2]
+    is read as the static amax).  Returns the four tensors."""
+    x = _gpu_2d(x, "x")
+    dev = x.device
+    rows, cols = x.shape
+    if out is None:
+        q = torch.empty((rows, (cols + 1) // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((rows, (cols + NV_BLOCK - 1) // NV_BLOCK), dtype=torch.uint8, device=dev)
+        a = _amax_arg(amax, dev)
+        if a is None:
+            a = torch.empty(1, dtype=torch.float32, device=dev)
+        g_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        q, sc, a, g_scale = out
+    given = amax is not None
+    st = load_library().nvfp4_quantize_no_workspace(
+        _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(q), _ptr(sc), _ptr(a), int(given),
+        _ptr(g_scale), _stream(dev))
+    _check(st, "nvfp4_quantize_no_workspace")
     return q, sc, a, g_scale
 
 

@@ -148,6 +148,39 @@ fp4_status nvfp4_quantize_ex(const void* x, fp4_dtype xt, int64_t rows, int64_t 
   return FP4_OK;
 }
 
+fp4_status nvfp4_quantize_no_workspace(const void* x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                       uint8_t* q, uint8_t* scales, float* global_amax,
+                                       int amax_given, float* global_scale, hipStream_t stream) {
+  // the same checks as nvfp4_quantize, with a stand-in for the workspace it
+  // does not take (never dereferenced: the library's scratch replaces it)
+  fp4_status st = check_quant_args(x, xt, rows, cols, q, scales, global_amax, amax_given,
+                                   global_scale, reinterpret_cast<const void*>(FP4_AMAX_WORKSPACE_BYTES),
+                                   FP4_AMAX_WORKSPACE_BYTES);
+  if (st != FP4_OK) return st;
+  if ((st = check_arch()) != FP4_OK) return st;
+  const bool bf16 = xt == FP4_BF16;
+  if (rows == 0 || cols == 0) {
+    FP4_TRY_LAUNCH(fp4impl::launch_empty_scales(amax_given ? nullptr : global_amax, global_scale,
+                                                stream),
+                   "nvfp4_quantize_no_workspace");
+    return FP4_OK;
+  }
+  uint32_t* partials = nullptr;
+  int npart = 0;
+  if (!amax_given) {
+    FP4_TRY_LAUNCH(fp4impl::amax_scratch(&partials), "nvfp4_quantize_no_workspace/scratch");
+    // the amax pass never uses more than kAmaxPartials workgroups, so every
+    // size fits the scratch; the first pass writes every partial the second reads
+    FP4_TRY_LAUNCH(fp4impl::launch_amax(x, bf16, rows * cols, partials, &npart, stream),
+                   "nvfp4_quantize_no_workspace/amax");
+  }
+  FP4_TRY_LAUNCH(fp4impl::launch_nv_quant(x, bf16, rows, cols, q, scales,
+                                          amax_given ? global_amax : nullptr, partials, npart,
+                                          amax_given ? nullptr : global_amax, global_scale, stream),
+                 "nvfp4_quantize_no_workspace/encode");
+  return FP4_OK;
+}
+
 fp4_status mxfp4_quantize(const void* x, fp4_dtype xt, int64_t rows, int64_t cols, uint8_t* q,
                           uint8_t* scales, hipStream_t stream) {
   if (!valid_dtype(xt)) return FP4_ERR_DTYPE;

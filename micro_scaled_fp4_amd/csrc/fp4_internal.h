@@ -36,6 +36,10 @@ constexpr int kAmaxPartials = 1024;  // FP4_AMAX_WORKSPACE_BYTES / 4
 hipError_t launch_amax(const void* x, bool bf16, int64_t n, uint32_t* partials, int* npart,
                        hipStream_t stream);
 
+// Device address, on the current device, of the library's own array of
+// kAmaxPartials partial maxima (looked up once per device, then cached).
+hipError_t amax_scratch(uint32_t** out);
+
 // NVFP4 quantize.  Exactly one of (amax_in) or (partials, npart) gives G.
 // block: 8, 16 or 32 values per E4M3 scale; window > 0: the scale byte is
 // searched over +-window codes around the amax rule's (least squared error).

@@ -14,6 +14,8 @@
 // cols to be a multiple of the block and 16-byte aligned pointers.  The
 // "generic" kernels take any shape and alignment (partial last blocks, odd
 // rows) with scalar accesses.
+#include <atomic>
+
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
@@ -586,9 +588,38 @@ hipError_t nv_quant_dispatch(const void* x, int64_t rows, int64_t cols, int bloc
   return hipGetLastError();
 }
 
+// Partial maxima of the amax pass for nvfp4_quantize_no_workspace: one copy per
+// device, kept until the process ends.  Host code never names it directly (on
+// the host the name is only a stand-in); it uses the device address from
+// hipGetSymbolAddress, kept per device below.
+static __device__ __align__(256) uint32_t scratch[fp4impl::kAmaxPartials];
+
+constexpr int kScratchDevices = 64;
+std::atomic<uintptr_t> g_scratch_addr[kScratchDevices];
+
 }  // namespace
 
 namespace fp4impl {
+
+hipError_t amax_scratch(uint32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  uintptr_t p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    // once per device, with that device current (two racing first calls both
+    // look the address up; they get the same one)
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    p = reinterpret_cast<uintptr_t>(a);
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = reinterpret_cast<uint32_t*>(p);
+  return hipSuccess;
+}
 
 hipError_t launch_amax(const void* x, bool bf16, int64_t n, uint32_t* partials, int* npart,
                        hipStream_t stream) {

@@ -133,6 +133,20 @@ def test_gemm_nvfp4_out_argument_errors():
     assert g(0, None, None, None, None, None, None, 1.0, 0, 8, 64, None, None, None, None, None) == OK
 
 
+def test_no_workspace_quantize_argument_errors():
+    """nvfp4_quantize_no_workspace takes nvfp4_quantize's arguments minus the
+    workspace and rejects the same bad ones on the host."""
+    lib = m.load_library()
+    q = lib.nvfp4_quantize_no_workspace
+    assert q(P, 9, 4, 16, P, P, P, 0, P, None) == DTYPE
+    assert q(P, 1, -1, 16, P, P, P, 0, P, None) == SHAPE
+    assert q(P, 1, 4, 16, P, P, P, 0, None, None) == NULL
+    assert q(None, 1, 4, 16, P, P, P, 0, P, None) == NULL
+    assert q(P, 1, 4, 16, P, P, None, 1, P, None) == NULL      # static amax missing
+    assert q(ctypes.c_void_p(4097), 1, 4, 16, P, P, P, 0, P, None) == ALIGN
+    assert q(P, 1, 4, 16, P, P, P, 0, ctypes.c_void_p(4098), None) == ALIGN
+
+
 def test_variant_grouped_and_rotation_argument_errors():
     """nvfp4_quantize_ex / nvfp4_dequantize_ex, fp4_grouped_gemm,
     hadamard_quantize_mx and hadamard_rotate reject bad arguments on the host.
