@@ -10,10 +10,16 @@
 // significant bits, magnitudes in [2^-10, 2688]), so their products are exact
 // and only the float32 accumulation rounds.
 //
-// Launch 1 (k_gemv_xprep): x -> NVFP4 exactly as nvfp4_quantize does (every
-//   workgroup reduces the small x for the global amax itself), stored in the
-//   workspace as x' in fp16, [B][Kp] with K padded to a multiple of 128.
-// Launch 2 (k_gemv_mfma): W streaming on v_mfma_f32_16x16x32_f16.  The batch
+// Launch 1 (k_gemv_xquant): x -> NVFP4 once, exactly as nvfp4_quantize does,
+//   into the workspace: as exact fp16 x' rows (when the streaming kernel keeps
+//   x' in LDS, or for the long-K kernel) or as codes + scale bytes (wider
+//   batches), zero past K.  Small x: every prep workgroup reduces all of x for
+//   the global amax itself; larger x: a first launch writes per-workgroup
+//   partial maxima (the quantizer's amax pass) and the prep reduces those.
+// Launch 2, the streaming kernel (k_gemv_stream; below): one workgroup per CU
+//   copies x from the workspace into LDS and streams W past it.
+// Long K (x not fitting LDS): k_gemv_mfma, W streaming on
+//   v_mfma_f32_16x16x32_f16.  The batch
 //   rows are the MFMA's M side (rows >= B are zero), 16 W rows its N side, so
 //   one MFMA applies a W fragment to every batch row at once.  A workgroup is
 //   persistent over 16-row strips of W; its waves split K (a wave keeps the
@@ -37,95 +43,121 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-constexpr int kPrepThreads = 256;
-constexpr size_t kHeader = 256;        // workspace header: [0] s_global of x
+constexpr int kPrepThreads = 1024;
+// Workspace: [0, 4 KiB) partial maxima of x (larger x) | [4 KiB, +256) header,
+// s_global of x | from kWsData: x quantized by the prep launch.
+constexpr size_t kWsPartials = 0;
+constexpr size_t kWsHeader = 4096;
+constexpr size_t kWsData = 4096 + 256;
+// x of at most this many values: each prep workgroup reduces all of it for the
+// amax (at most 8 workgroups, each reading at most 512 KB)
+constexpr int64_t kSmallX = (int64_t)1 << 17;
 constexpr int kMaxWaves = 16;
 constexpr int kMaxSteps = 3;           // 128-value steps per wave kept in registers
 
 inline int64_t kpad(int64_t K) { return (K + 127) / 128 * 128; }
 
-// -------------------------------------------------------------- x prologue --
-template <bool BF16>
+// -------------------------------------------------------------- x prep --
+// x [B, K] -> NVFP4 with one tensor scale over all of x, each step as
+// nvfp4_quantize takes it: G = max|x| (from `partials` when given, else reduced
+// here over all of x), s_global, then per 16-value block the E4M3 scale and
+// the E2M1 codes.  F16OUT: x' = E4M3 * E2M1 (exact in fp16) as rows [B][Kpad];
+// else codes [B][Kpad/2] followed by scale bytes [B][Kpad/16].  Blocks past K
+// (up to Kpad) are zeros.  One thread per 16-value block of [B, Kpad].
+template <bool BF16, bool F16OUT>
 __global__ void __launch_bounds__(kPrepThreads)
-    k_gemv_xprep(const void* __restrict__ x, int64_t B, int64_t K, int64_t Kp,
-                 uint8_t* __restrict__ ws) {
+    k_gemv_xquant(const void* __restrict__ x, int64_t B, int64_t K, int64_t Kpad,
+                  const uint32_t* __restrict__ partials, int npart, uint8_t* __restrict__ ws) {
   __shared__ uint32_t red[kPrepThreads / 64];
-  const int64_t n = B * K;
-  // global amax of x (small: every workgroup reduces all of it)
-  uint32_t m = 0;
-  if (BF16) {
-    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-    for (int64_t i = threadIdx.x; i < n / 8; i += kPrepThreads) {
-      const u32x4 v = xv[i];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  constexpr int kUnroll = 12;   // 16-byte vectors in flight per thread in the amax loop
+  const int64_t bpr = Kpad / 16;
+  const int64_t blk = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
+  const int64_t row = blk / bpr, c0 = (blk - row * bpr) * 16;
+  const bool live = blk < B * bpr && c0 < K;
+  // this thread's block first, so its loads overlap the amax loads
+  float v[16];
+  {
+    const int64_t base = live ? row * K + c0 : 0;
+    if (BF16) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + base);
+      const u32x4 a = p[0], b = p[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[2 * j] = bf16_lo(w[j]);
+        v[2 * j + 1] = bf16_hi(w[j]);
+      }
+    } else {
+      const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + base);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t a = w[j] & 0x7fff7fffu;
-        m = umax(m, umax(a << 16, a & 0xffff0000u));
+        const f32x4 a = p[j];
+        v[4 * j] = a.x;
+        v[4 * j + 1] = a.y;
+        v[4 * j + 2] = a.z;
+        v[4 * j + 3] = a.w;
       }
     }
+  }
+  uint32_t m = 0;
+  if (partials != nullptr) {
+    for (int i = threadIdx.x; i < npart; i += kPrepThreads) m = umax(m, partials[i]);
   } else {
+    const int64_t nvec = B * K / (BF16 ? 8 : 4);   // K % 32 == 0: whole 16-byte vectors
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-    for (int64_t i = threadIdx.x; i < n / 4; i += kPrepThreads) {
-      const u32x4 v = xv[i];
-      m = umax(umax(m, v.x & 0x7fffffffu), umax(v.y & 0x7fffffffu, umax(v.z & 0x7fffffffu, v.w & 0x7fffffffu)));
+    for (int64_t i0 = threadIdx.x; i0 < nvec; i0 += kUnroll * kPrepThreads) {
+      u32x4 t[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + u * kPrepThreads;
+        t[u] = i < nvec ? xv[i] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t w[4] = {t[u].x, t[u].y, t[u].z, t[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (BF16) {
+            const uint32_t a = w[j] & 0x7fff7fffu;
+            m = umax(m, umax(a << 16, a & 0xffff0000u));
+          } else {
+            m = umax(m, w[j] & 0x7fffffffu);
+          }
+        }
+      }
     }
   }
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+#pragma unroll
+  for (int i = 0; i < kPrepThreads / 64; ++i) m = umax(m, red[i]);
   const float s_global = nv_global_scale(__uint_as_float(m));
-  if (blockIdx.x == 0 && threadIdx.x == 0) reinterpret_cast<float*>(ws)[0] = s_global;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<float*>(ws + kWsHeader) = s_global;
 
-  // one thread per 16-value block of the padded [B, Kp] x'
-  const int64_t bpr = Kp / 16;
-  const int64_t blk = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
   if (blk >= B * bpr) return;
-  const int64_t row = blk / bpr, c0 = (blk - row * bpr) * 16;
-  _Float16* out = reinterpret_cast<_Float16*>(ws + kHeader) + row * Kp + c0;
-  if (c0 >= K) {
+  uint8_t* data = ws + kWsData;
+  uint32_t c[2] = {0u, 0u}, sc = 0u;
+  if (live) {   // blocks past K (up to Kpad) stay zero
+    uint32_t am = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) out[j] = (_Float16)0.0f;
-    return;
+    for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
+    float r;
+    nv_block_scale(__uint_as_float(am), s_global, sc, r);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
+    c[0] = e2m1_pack8(v);
+    c[1] = e2m1_pack8(v + 8);
   }
-  float v[16];
-  const int64_t base = row * K + c0;
-  if (BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + base);
-    const u32x4 a = p[0], c = p[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[2 * j] = bf16_lo(w[j]);
-      v[2 * j + 1] = bf16_hi(w[j]);
-    }
+  if (F16OUT) {
+    const f16x2 h = e4m3_h2(sc);
+    f16x8* out = reinterpret_cast<f16x8*>(data + 2 * (row * Kpad + c0));
+    out[0] = dq8(c[0], h);     // exact: E2M1 * E4M3
+    out[1] = dq8(c[1], h);
   } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + base);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 a = p[j];
-      v[4 * j] = a.x;
-      v[4 * j + 1] = a.y;
-      v[4 * j + 2] = a.z;
-      v[4 * j + 3] = a.w;
-    }
+    *reinterpret_cast<u32x2*>(data + row * (Kpad / 2) + c0 / 2) = u32x2{c[0], c[1]};
+    data[B * (Kpad / 2) + blk] = (uint8_t)sc;
   }
-  uint32_t am = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
-  uint32_t sc;
-  float r;
-  nv_block_scale(__uint_as_float(am), s_global, sc, r);
-  const float sv = e4m3_value(sc);
-  _Float16 h[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) h[j] = (_Float16)(e2m1_value(e2m1_code(v[j] * r)) * sv);   // exact
-  u32x4* o4 = reinterpret_cast<u32x4*>(out);
-  uint32_t wd[8];
-  __builtin_memcpy(wd, h, 32);
-  o4[0] = u32x4{wd[0], wd[1], wd[2], wd[3]};
-  o4[1] = u32x4{wd[4], wd[5], wd[6], wd[7]};
 }
 
 // --------------------------------------------------------- W streaming --
@@ -211,9 +243,9 @@ __global__ void __launch_bounds__(kMaxWaves * 64)
   const int b = lane & 15, g = lane >> 4;
   const int T = Kp / 128;
   const int t0 = wave * spw;
-  const _Float16* xp = reinterpret_cast<const _Float16*>(ws + kHeader);
+  const _Float16* xp = reinterpret_cast<const _Float16*>(ws + kWsData);
   const int64_t wrow_bytes = K / 2, srow_bytes = K / 16;
-  const float gscale = reinterpret_cast<const float*>(ws)[0] * (*g_w);
+  const float gscale = *reinterpret_cast<const float*>(ws + kWsHeader) * (*g_w);
   const int nstrips = (N + 15) / 16;
   const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
@@ -287,12 +319,14 @@ __global__ void __launch_bounds__(kMaxWaves * 64)
   }
 }
 
-// ------------------------------------------------------ fused streaming GEMV --
+// ------------------------------------------------------ streaming GEMV --
 // One workgroup of 16 waves per CU, persistent over rounds of strips.
-// Prologue: every workgroup quantizes all of x itself (global amax, then
-// per-block NVFP4 exactly as nvfp4_quantize) into LDS -- as exact fp16 x' when
-// it fits (XF16), else as codes + scale bytes dequantized per use.  Its first x
-// loads are issued before the first W loads so they do not queue behind them.
+// Prologue: narrow batches (fp16 x' fits LDS, XF16): every workgroup quantizes
+// all of the small x itself (global amax, then per-block NVFP4 exactly as
+// nvfp4_quantize) into LDS as exact fp16 x'.  Wider batches: x, quantized once
+// by the prep launch, is copied from the workspace into LDS as codes + scale
+// bytes, dequantized per use.  The first x loads are issued before the first W
+// loads.
 // Streaming: a round gives each of the kSlots wave pairs one 16-row strip; the
 // two waves of a pair stream the two halves of K, kPairs pairs of 128-value
 // steps in flight per wave.  At the round's end the upper half's partial tile
@@ -305,7 +339,7 @@ constexpr int kSlots = kStreamWaves / kSplit;   // strips per workgroup and roun
 constexpr int kPairs = 4;                       // pairs of steps in flight per wave
 constexpr int kXRegVecs = 4;                    // 16-byte x vectors per thread held in registers
 constexpr int kRedBytes = 2 * kSlots * 64 * 16; // double-buffered partial tiles
-constexpr int kStreamLdsMax = 160 * 1024 - 256;  // dynamic LDS (the kernel's static LDS is 64 bytes)
+constexpr int kStreamLdsMax = 160 * 1024 - 256;  // dynamic LDS (the kernel has no static LDS)
 
 __host__ __device__ inline int xf16_row_bytes(int Kq) {
   const int base = Kq * 2 + Kq / 4;
@@ -339,13 +373,19 @@ constexpr int kScaleHalf = 0, kScaleDword = 1, kScaleGroup = 2;
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
 constexpr int kLoadNT = 2;                      // buffer load cache policy: nontemporal
 
-template <bool XBF16, bool XF16, int SCM>
+// XSRC: where x comes from -- kXFromWs: the prep launch's quantized x in the
+// workspace; kXBf16 / kXF32: x itself, quantized here by every workgroup.
+constexpr int kXFromWs = 0, kXBf16 = 1, kXF32 = 2;
+
+template <int XSRC, bool XF16, int SCM>
 __global__ void __launch_bounds__(kStreamThreads, 1)
-    k_gemv_stream(const void* __restrict__ x, int B, const uint8_t* __restrict__ W,
-                  const uint8_t* __restrict__ w_scales, const float* __restrict__ g_w, int N,
-                  int K, int Kq, int lds_x_bytes, float g_d, void* __restrict__ y, bool YBF16) {
+    k_gemv_stream(const void* __restrict__ x, const uint8_t* __restrict__ ws, int B,
+                  const uint8_t* __restrict__ W, const uint8_t* __restrict__ w_scales,
+                  const float* __restrict__ g_w, int N, int K, int Kq, int lds_x_bytes, float g_d,
+                  void* __restrict__ y, bool YBF16) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ uint32_t red_max[kStreamWaves];
+  constexpr bool XBF16 = XSRC == kXBf16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = lane & 15, g = lane >> 4;
@@ -363,6 +403,33 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   uint8_t* tb = lds + lds_x_bytes + wave * 2048;
   v4f* red = reinterpret_cast<v4f*>(lds + lds_x_bytes + kStreamWaves * 2048);
 
+  // ---- x.  kXFromWs: the prep launch's x from the workspace (fp16 x' rows
+  // [B][Kq] when XF16, else codes [B][Kq/2] followed by scale bytes
+  // [B][Kq/16]), copied to LDS in 16-byte chunks.  Otherwise x itself, which
+  // this workgroup quantizes (below).  Either way the first x loads are issued
+  // before the first W loads, so they do not queue behind them in the
+  // in-order load queue.
+  const int row_chunks = XF16 ? Kq / 8 : Kq / 32;          // 16-byte chunks per x row
+  const int nchunk = B * row_chunks + (XF16 ? 0 : B * bpr / 16);
+  const u32x4* xsrc = reinterpret_cast<const u32x4*>(ws + kWsData);
+  auto x_dst = [&](int c) {
+    if (XF16 || c < B * row_chunks) {
+      const int row = c / row_chunks, k = c - row * row_chunks;
+      // XF16: chunk k holds values 8k .. 8k + 7, at byte 2 (8k) + 16 (8k / 64)
+      return reinterpret_cast<u32x4*>(XF16 ? lds + row * xf_row + 16 * k + 16 * (k / 8)
+                                           : lds + row * xc_row + 16 * k);
+    }
+    return reinterpret_cast<u32x4*>(xs_base + 16 * (c - B * row_chunks));
+  };
+  u32x4 xr[kXRegVecs];  // workspace chunks (XSRC == kXFromWs)
+  if constexpr (XSRC == kXFromWs) {
+#pragma unroll
+    for (int i = 0; i < kXRegVecs; ++i) {
+      const int c = threadIdx.x + i * kStreamThreads;
+      xr[i] = xsrc[c < nchunk ? c : 0];
+    }
+  }
+
   // ---- x: first blocks into registers (thread t owns blocks t + i * 1024)
   constexpr int VPB = XBF16 ? 2 : 4;             // 16-byte vectors per 16-value block
   constexpr int kXB = kXRegVecs / VPB;
@@ -373,13 +440,15 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     ok = blk < nblk && c0 < K;
     return xv + (ok ? ((int64_t)row * K + c0) / (16 / VPB) : 0);
   };
-  u32x4 xr[kXB][VPB];
+  u32x4 xrb[kXB][VPB];  // x blocks (XSRC != kXFromWs)
+  if constexpr (XSRC != kXFromWs) {
 #pragma unroll
-  for (int i = 0; i < kXB; ++i) {
-    bool ok;
-    const u32x4* src = block_src(threadIdx.x + i * kStreamThreads, ok);
+    for (int i = 0; i < kXB; ++i) {
+      bool ok;
+      const u32x4* src = block_src(threadIdx.x + i * kStreamThreads, ok);
 #pragma unroll
-    for (int v = 0; v < VPB; ++v) xr[i][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+      for (int v = 0; v < VPB; ++v) xrb[i][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   // ---- W ring: a wave's elements are (round r, pair pbeg + e), e < Ep
@@ -445,97 +514,112 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
 #pragma unroll
   for (int i = 0; i < kPairs; ++i) load_elem(ra[i], rb[i], rs[i], i == 0);
 
-  // ---- x -> NVFP4 (global amax over all of [B, K], then per 16-value block)
-  auto vec_absmax = [&](const u32x4& v) {
-    if (XBF16) {
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      uint32_t m = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t t = w4[j] & 0x7fff7fffu;
-        m = umax(m, umax(t << 16, t & 0xffff0000u));
+  float s_gx;
+  if constexpr (XSRC == kXFromWs) {
+    // ---- x into LDS
+  #pragma unroll
+    for (int i = 0; i < kXRegVecs; ++i) {
+      const int c = threadIdx.x + i * kStreamThreads;
+      if (c < nchunk) *x_dst(c) = xr[i];
+    }
+    for (int c = threadIdx.x + kXRegVecs * kStreamThreads; c < nchunk; c += kStreamThreads)
+      *x_dst(c) = xsrc[c];
+    __syncthreads();
+    s_gx = *reinterpret_cast<const float*>(ws + kWsHeader);
+  } else {
+    // ---- x -> NVFP4 (global amax over all of [B, K], then per 16-value block)
+    auto vec_absmax = [&](const u32x4& v) {
+      if (XBF16) {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        uint32_t m = 0;
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t t = w4[j] & 0x7fff7fffu;
+          m = umax(m, umax(t << 16, t & 0xffff0000u));
+        }
+        return m;
       }
-      return m;
+      return umax(umax(v.x & 0x7fffffffu, v.y & 0x7fffffffu),
+                  umax(v.z & 0x7fffffffu, v.w & 0x7fffffffu));
+    };
+    uint32_t m = 0;
+  #pragma unroll
+    for (int i = 0; i < kXB; ++i)
+  #pragma unroll
+      for (int v = 0; v < VPB; ++v) m = umax(m, vec_absmax(xrb[i][v]));
+    for (int blk0 = threadIdx.x + kXB * kStreamThreads; blk0 < nblk; blk0 += 2 * kStreamThreads) {
+      u32x4 t[2][VPB];
+  #pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bool ok;
+        const u32x4* src = block_src(blk0 + h * kStreamThreads, ok);
+  #pragma unroll
+        for (int v = 0; v < VPB; ++v) t[h][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+      }
+  #pragma unroll
+      for (int h = 0; h < 2; ++h)
+  #pragma unroll
+        for (int v = 0; v < VPB; ++v) m = umax(m, vec_absmax(t[h][v]));
     }
-    return umax(umax(v.x & 0x7fffffffu, v.y & 0x7fffffffu),
-                umax(v.z & 0x7fffffffu, v.w & 0x7fffffffu));
-  };
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < kXB; ++i)
-#pragma unroll
-    for (int v = 0; v < VPB; ++v) m = umax(m, vec_absmax(xr[i][v]));
-  for (int blk0 = threadIdx.x + kXB * kStreamThreads; blk0 < nblk; blk0 += 2 * kStreamThreads) {
-    u32x4 t[2][VPB];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bool ok;
-      const u32x4* src = block_src(blk0 + h * kStreamThreads, ok);
-#pragma unroll
-      for (int v = 0; v < VPB; ++v) t[h][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int v = 0; v < VPB; ++v) m = umax(m, vec_absmax(t[h][v]));
-  }
-  const float s_gx = nv_global_scale(__uint_as_float(block_max_1024(m, red_max)));
-  auto quant_block = [&](int blk, const u32x4 (&vv)[VPB]) {
-    const int row = blk / bpr, c0 = (blk - row * bpr) * 16;
-    float v[16];
-    if (XBF16) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t w4[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[8 * j + 2 * q] = bf16_lo(w4[q]);
-          v[8 * j + 2 * q + 1] = bf16_hi(w4[q]);
+    const float s_gx_here = nv_global_scale(__uint_as_float(block_max_1024(m, red_max)));
+    auto quant_block = [&](int blk, const u32x4 (&vv)[VPB]) {
+      const int row = blk / bpr, c0 = (blk - row * bpr) * 16;
+      float v[16];
+      if (XBF16) {
+  #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t w4[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[8 * j + 2 * q] = bf16_lo(w4[q]);
+            v[8 * j + 2 * q + 1] = bf16_hi(w4[q]);
+          }
+        }
+      } else {
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[4 * j] = __uint_as_float(vv[j].x);
+          v[4 * j + 1] = __uint_as_float(vv[j].y);
+          v[4 * j + 2] = __uint_as_float(vv[j].z);
+          v[4 * j + 3] = __uint_as_float(vv[j].w);
         }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[4 * j] = __uint_as_float(vv[j].x);
-        v[4 * j + 1] = __uint_as_float(vv[j].y);
-        v[4 * j + 2] = __uint_as_float(vv[j].z);
-        v[4 * j + 3] = __uint_as_float(vv[j].w);
+      uint32_t am = 0;
+  #pragma unroll
+      for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
+      uint32_t sc;
+      float r;
+      nv_block_scale(__uint_as_float(am), s_gx_here, sc, r);
+  #pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
+      uint32_t c[2] = {e2m1_pack8(v), e2m1_pack8(v + 8)};
+      if (c0 >= K) c[0] = c[1] = sc = 0u;        // padding past K: x' = 0
+      if (XF16) {
+        const v2h h = e4m3_h2(sc);
+        v8h* dst = reinterpret_cast<v8h*>(lds + row * xf_row + c0 * 2 + 16 * (c0 / 64));
+        dst[0] = dq8(c[0], h);
+        dst[1] = dq8(c[1], h);
+      } else {
+        *reinterpret_cast<u32x2*>(lds + row * xc_row + c0 / 2) = u32x2{c[0], c[1]};
+        xs_base[row * bpr + c0 / 16] = (uint8_t)sc;
       }
+    };
+  #pragma unroll
+    for (int i = 0; i < kXB; ++i) {
+      const int blk = threadIdx.x + i * kStreamThreads;
+      if (blk < nblk) quant_block(blk, xrb[i]);
     }
-    uint32_t am = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
-    uint32_t sc;
-    float r;
-    nv_block_scale(__uint_as_float(am), s_gx, sc, r);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
-    uint32_t c[2] = {e2m1_pack8(v), e2m1_pack8(v + 8)};
-    if (c0 >= K) c[0] = c[1] = sc = 0u;        // padding past K: x' = 0
-    if (XF16) {
-      const v2h h = e4m3_h2(sc);
-      v8h* dst = reinterpret_cast<v8h*>(lds + row * xf_row + c0 * 2 + 16 * (c0 / 64));
-      dst[0] = dq8(c[0], h);
-      dst[1] = dq8(c[1], h);
-    } else {
-      *reinterpret_cast<u32x2*>(lds + row * xc_row + c0 / 2) = u32x2{c[0], c[1]};
-      xs_base[row * bpr + c0 / 16] = (uint8_t)sc;
+    for (int blk = threadIdx.x + kXB * kStreamThreads; blk < nblk; blk += kStreamThreads) {
+      bool ok;
+      const u32x4* src = block_src(blk, ok);
+      u32x4 t[VPB];
+  #pragma unroll
+      for (int v = 0; v < VPB; ++v) t[v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+      quant_block(blk, t);
     }
-  };
-#pragma unroll
-  for (int i = 0; i < kXB; ++i) {
-    const int blk = threadIdx.x + i * kStreamThreads;
-    if (blk < nblk) quant_block(blk, xr[i]);
+    __syncthreads();
+    s_gx = s_gx_here;
   }
-  for (int blk = threadIdx.x + kXB * kStreamThreads; blk < nblk; blk += kStreamThreads) {
-    bool ok;
-    const u32x4* src = block_src(blk, ok);
-    u32x4 t[VPB];
-#pragma unroll
-    for (int v = 0; v < VPB; ++v) t[v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
-    quant_block(blk, t);
-  }
-  __syncthreads();
   const float gscale = s_gx * (*g_w);
 
   // ---- stream W
@@ -659,6 +743,7 @@ int num_cus() {
 
 struct StreamArgs {
   const void* x;
+  const uint8_t* ws;
   int B;
   const uint8_t* W;
   const uint8_t* w_scales;
@@ -669,16 +754,43 @@ struct StreamArgs {
   bool y_bf16;
 };
 
-template <bool XB, bool XF, int SCM>
+template <int XS, bool XF, int SCM>
 hipError_t launch_stream(const StreamArgs& a, int grid, int lds, hipStream_t stream) {
   // the limit is set once per device to the most any call of this kernel uses
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e = fp4impl::set_lds_limit_once(
-      lds_set, reinterpret_cast<const void*>(&k_gemv_stream<XB, XF, SCM>), kStreamLdsMax);
+      lds_set, reinterpret_cast<const void*>(&k_gemv_stream<XS, XF, SCM>), kStreamLdsMax);
   if (e != hipSuccess) return e;
   if (lds > kStreamLdsMax) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemv_stream<XB, XF, SCM>), dim3(grid), dim3(kStreamThreads), lds, stream,
-                     a.x, a.B, a.W, a.w_scales, a.g_w, a.N, a.K, a.Kq, a.lds_x, a.g_d, a.y, a.y_bf16);
+  hipLaunchKernelGGL((k_gemv_stream<XS, XF, SCM>), dim3(grid), dim3(kStreamThreads), lds, stream,
+                     a.x, a.ws, a.B, a.W, a.w_scales, a.g_w, a.N, a.K, a.Kq, a.lds_x, a.g_d, a.y,
+                     a.y_bf16);
+  return hipGetLastError();
+}
+
+// x [B, K] -> the workspace (k_gemv_xquant), with the amax of a larger x from
+// per-workgroup partial maxima first.
+hipError_t launch_xquant(const void* x, bool x_bf16, int64_t B, int64_t K, int64_t Kpad,
+                         bool f16_out, uint8_t* ws, hipStream_t stream) {
+  const uint32_t* partials = nullptr;
+  int npart = 0;
+  if (B * K > kSmallX) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(ws + kWsPartials);
+    hipError_t e = fp4impl::launch_amax(x, x_bf16, B * K, p, &npart, stream);
+    if (e != hipSuccess) return e;
+    partials = p;
+  }
+  const int64_t nblk = B * (Kpad / 16);
+  const dim3 grid((unsigned)((nblk + kPrepThreads - 1) / kPrepThreads));
+#define FP4_XQ(XB, F16)                                                                    \
+  hipLaunchKernelGGL((k_gemv_xquant<XB, F16>), grid, dim3(kPrepThreads), 0, stream, x, B, K, \
+                     Kpad, partials, npart, ws)
+  if (x_bf16) {
+    if (f16_out) FP4_XQ(true, true); else FP4_XQ(true, false);
+  } else {
+    if (f16_out) FP4_XQ(false, true); else FP4_XQ(false, false);
+  }
+#undef FP4_XQ
   return hipGetLastError();
 }
 
@@ -702,7 +814,10 @@ hipError_t launch_zero_fill(void* y, int64_t n, int elem_bytes, hipStream_t stre
 }
 
 size_t gemv_workspace_bytes(int64_t B, int64_t K) {
-  return kHeader + (size_t)(B * kpad(K) * 2);
+  // the larger of the streaming kernel's x (fp16 rows of K rounded up to 256)
+  // and the long-K kernel's (fp16 rows of K rounded up to 128)
+  const int64_t Kq = (K + 255) / 256 * 256;
+  return kWsData + (size_t)(B * Kq * 2);
 }
 
 hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
@@ -711,8 +826,9 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   if (N > (1 << 30) || K > (1 << 30)) return hipErrorInvalidValue;
   const int ncu = num_cus();
   if (K == 0) return launch_zero_fill(y, B * N, y_bf16 ? 2 : 4, stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int nstrips = (int)((N + 15) / 16);
-  // fused streaming kernel when the quantized x fits in LDS
+  // streaming kernel when the quantized x fits in LDS
   const int64_t Kq = (K + 255) / 256 * 256;
   const int64_t lds_f16 = B * xf16_row_bytes((int)Kq);
   const int64_t lds_fp4 = B * (Kq / 2 + 16) + B * (Kq / 16);
@@ -725,37 +841,35 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   // (the strip-relative buffer offsets need 16 rows of W to span < 2^31 bytes;
   // the x' sizes above already keep K far below that)
   if ((xf16 || lds_fp4 + lds_fixed <= lds_max) && K < (1 << 27)) {
+    // x' fits LDS as fp16 (narrow batches): every workgroup quantizes the
+    // small x itself, one launch in all; wider batches: the prep launch
+    // quantizes x once into the workspace (in every workgroup that work would
+    // cost more than the extra launch)
+    const int xs = xf16 ? (x_bf16 ? kXBf16 : kXF32) : kXFromWs;
+    if (xs == kXFromWs) {
+      hipError_t e = launch_xquant(x, x_bf16, B, K, Kq, false, ws, stream);
+      if (e != hipSuccess) return e;
+    }
     const int lds_x = (int)(((xf16 ? lds_f16 : lds_fp4) + 15) / 16 * 16);
     const int lds = lds_x + (int)lds_fixed;
     const int grid = nstrips < ncu ? nstrips : ncu;
-    const StreamArgs sa{x, (int)B, W, w_scales, g_w, (int)N, (int)K, (int)Kq, lds_x, g_d, y, y_bf16};
-    const int sel = (x_bf16 ? 4 : 0) | (xf16 ? 2 : 0);
-    switch (sel * 3 + scm) {
-      case 0: return launch_stream<false, false, kScaleHalf>(sa, grid, lds, stream);
-      case 1: return launch_stream<false, false, kScaleDword>(sa, grid, lds, stream);
-      case 2: return launch_stream<false, false, kScaleGroup>(sa, grid, lds, stream);
-      case 6: return launch_stream<false, true, kScaleHalf>(sa, grid, lds, stream);
-      case 7: return launch_stream<false, true, kScaleDword>(sa, grid, lds, stream);
-      case 8: return launch_stream<false, true, kScaleGroup>(sa, grid, lds, stream);
-      case 12: return launch_stream<true, false, kScaleHalf>(sa, grid, lds, stream);
-      case 13: return launch_stream<true, false, kScaleDword>(sa, grid, lds, stream);
-      case 14: return launch_stream<true, false, kScaleGroup>(sa, grid, lds, stream);
-      case 18: return launch_stream<true, true, kScaleHalf>(sa, grid, lds, stream);
-      case 19: return launch_stream<true, true, kScaleDword>(sa, grid, lds, stream);
-      default: return launch_stream<true, true, kScaleGroup>(sa, grid, lds, stream);
+    const StreamArgs sa{x, ws, (int)B, W, w_scales, g_w, (int)N, (int)K, (int)Kq, lds_x, g_d, y, y_bf16};
+    switch (xs * 3 + scm) {
+      case 0: return launch_stream<kXFromWs, false, kScaleHalf>(sa, grid, lds, stream);
+      case 1: return launch_stream<kXFromWs, false, kScaleDword>(sa, grid, lds, stream);
+      case 2: return launch_stream<kXFromWs, false, kScaleGroup>(sa, grid, lds, stream);
+      case 3: return launch_stream<kXBf16, true, kScaleHalf>(sa, grid, lds, stream);
+      case 4: return launch_stream<kXBf16, true, kScaleDword>(sa, grid, lds, stream);
+      case 5: return launch_stream<kXBf16, true, kScaleGroup>(sa, grid, lds, stream);
+      case 6: return launch_stream<kXF32, true, kScaleHalf>(sa, grid, lds, stream);
+      case 7: return launch_stream<kXF32, true, kScaleDword>(sa, grid, lds, stream);
+      default: return launch_stream<kXF32, true, kScaleGroup>(sa, grid, lds, stream);
     }
   }
 
   // very long K: x' through the workspace, waves split K
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int64_t Kp = kpad(K);
-  const int64_t nblk = B * (Kp / 16);
-  const dim3 g1((unsigned)((nblk + kPrepThreads - 1) / kPrepThreads));
-  if (x_bf16)
-    hipLaunchKernelGGL(k_gemv_xprep<true>, g1, dim3(kPrepThreads), 0, stream, x, B, K, Kp, ws);
-  else
-    hipLaunchKernelGGL(k_gemv_xprep<false>, g1, dim3(kPrepThreads), 0, stream, x, B, K, Kp, ws);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_xquant(x, x_bf16, B, K, Kp, true, ws, stream);
   if (e != hipSuccess) return e;
   const int T = (int)(Kp / 128);
   int spw = (T + kMaxWaves - 1) / kMaxWaves;
