@@ -39,6 +39,7 @@ using namespace fp4dev;
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -716,6 +717,290 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   for (int r = Ep > 0 ? nmine : 0; r < R; ++r) finish(r, acc0, r < nmine);
 }
 
+// ------------------------------------------------- FP4-MFMA GEMV (B <= 4) --
+// Narrow batches: W's codes go into the FP4 MFMA as they are
+// (v_mfma_scale_f32_16x16x128_f8f6f4, both operands E2M1, unit scales), with no
+// dequantization.  W is loaded 8 rows x 128 contiguous bytes per instruction
+// (16 rows x 64 bytes, the MFMA's operand shape, reads HBM ~35% slower) and
+// reaches the MFMA layout through a wave-private XOR-swizzled LDS tile.  x is the other operand, laid out
+// block-diagonally: for MFMA t of a 128-value step, row m of the x operand is
+// batch row 2t + m / 8 restricted to the step's 16-value block m % 8 (zero
+// elsewhere), so D[m][n] = sum over that block of E2M1(x) E2M1(w), one exact
+// block dot product per output.  Lane (g, n) of the MFMA output holds
+// D[4g + j][n], j = 0..3: W row n against x blocks 4 (g % 2) + j of batch row
+// 2t + g / 2; it applies the two E4M3 block scales, acc += (s_x s_w) D, the
+// product exact (at most 8 + 12 significant bits), one rounding per block; W's
+// four scale bytes for those blocks are contiguous.  Rounds, strips, the split
+// of K between two waves and the exchange of partial sums are those of
+// k_gemv_stream; every workgroup quantizes the small x itself.
+// Pairs of 128-value steps in flight per wave, which is also the group of pairs
+// whose W scale bytes (16 rows x 4 pairs x 16 bytes) arrive with one 16-byte
+// load per lane, passed on through a 1 KB LDS area per wave (per-pair scale
+// loads of a few bytes from 16 rows each would double the memory requests).
+constexpr int kFp4Pairs = 4;
+
+template <bool XBF16, int NMF>
+__global__ void __launch_bounds__(kStreamThreads, 1)
+    k_gemv_fp4(const void* __restrict__ x, int B, const uint8_t* __restrict__ W,
+               const uint8_t* __restrict__ w_scales, const float* __restrict__ g_w, int N, int K,
+               int Kq, float g_d, void* __restrict__ y, bool YBF16) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ uint32_t red_max[kStreamWaves];
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+  const int nstrips = (N + 15) / 16;
+  const int wrow = K / 2, srow = K / 16;
+  const int S = Kq / 128;                        // 128-value steps
+  const int bpr = Kq / 16;                       // x blocks per padded row
+  // LDS: W transpose tiles [16 waves] x 2 KB | W scale groups [16 waves] x 1 KB |
+  // x operand tiles [NMF][S][64 lanes] x 16 bytes | x block scales (E4M3
+  // values) [2 NMF][bpr] floats | partial sums [2][kSlots][64][NMF] floats
+  uint8_t* tb = lds + wave * 2048;
+  uint8_t* sgw = lds + kStreamWaves * 2048 + wave * 1024;
+  u32x4* xt = reinterpret_cast<u32x4*>(lds + kStreamWaves * 3072);
+  float* sxs = reinterpret_cast<float*>(lds + kStreamWaves * 3072 + NMF * S * 1024);
+  float* red = sxs + 2 * NMF * bpr;
+
+  // ---- x: first blocks into registers (thread t owns blocks t + i * 1024)
+  constexpr int VPB = XBF16 ? 2 : 4;             // 16-byte vectors per 16-value block
+  constexpr int kXB = kXRegVecs / VPB;
+  const int nblk = B * bpr;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  auto block_src = [&](int blk, bool& ok) {
+    const int row = blk / bpr, c0 = (blk - row * bpr) * 16;
+    ok = blk < nblk && c0 < K;
+    return xv + (ok ? ((int64_t)row * K + c0) / (16 / VPB) : 0);
+  };
+  u32x4 xr[kXB][VPB];
+#pragma unroll
+  for (int i = 0; i < kXB; ++i) {
+    bool ok;
+    const u32x4* src = block_src(threadIdx.x + i * kStreamThreads, ok);
+#pragma unroll
+    for (int v = 0; v < VPB; ++v) xr[i][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- W ring: a wave's elements are (round r, pair pbeg + e), e < Ep (as in
+  // k_gemv_stream).  A pair is 16 strip rows x 128 bytes: lane l loads the
+  // 16-byte chunk l % 8 of rows l / 8 and 8 + l / 8.  Chunk c holds values
+  // 256 p + 32 c .. +32, which the MFMA of step c / 4 takes as K group c % 4 (x's
+  // operand tiles follow the same order).  With a group's first pair p, lane
+  // (g, n) loads row n's 16 scale bytes of pair p + g.
+  const int part = wave / kSlots, slot = wave - part * kSlots;
+  const int Pq = Kq / 256;
+  const int Ph = (Pq + kSplit - 1) / kSplit;
+  const int pbeg = min(part * Ph, Pq), pend = min(pbeg + Ph, Pq);
+  const int E = pend - pbeg;
+  const int Ep = (E + kFp4Pairs - 1) / kFp4Pairs * kFp4Pairs;
+  const int G = gridDim.x * kSlots;
+  const int s_first = slot * gridDim.x + blockIdx.x;
+  const int R = (nstrips + G - 1) / G;
+  const int nmine = s_first < nstrips ? (nstrips - s_first + G - 1) / G : 0;
+  const int J = nmine * Ep;
+  u32x4 ra[kFp4Pairs], rb[kFp4Pairs];
+  u32x4 sg;                                      // scale group in flight
+  const int r8 = lane >> 3, c8 = lane & 7;
+  const int w_lane = r8 * wrow + 16 * c8;
+  const int g_lane = n16 * srow + 16 * g;
+  int lr = 0, le = 0;                            // next element to load
+  auto load_elem = [&](int i) {
+    const bool live = lr < nmine && le < E;
+    const int r0 = lr < nmine ? (s_first + lr * G) * 16 : 0;
+    const int rows = live ? min(16, N - r0) : 0;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W) + (int64_t)r0 * wrow, 0, rows * wrow, kBufferWord3);
+    const int pp = pbeg + le;
+    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, 128 * pp, kLoadNT);
+    rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + 8 * wrow, 128 * pp, kLoadNT);
+    if (i == 0) {   // the group's first pair (le % kFp4Pairs == 0): its kFp4Pairs pairs' scales
+      const int grows = lr < nmine ? min(16, N - r0) : 0;
+      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, grows * srow, kBufferWord3);
+      sg = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane, 16 * pp, 0);
+    }
+    if (++le >= Ep) { le = 0; ++lr; }
+  };
+#pragma unroll
+  for (int i = 0; i < kFp4Pairs; ++i) load_elem(i);
+
+  // ---- x operand tiles and block scales start at zero (padding blocks, the
+  // other batch row of a tile, batch rows past B); the barriers of the amax
+  // reduction order these stores before the quantized blocks' stores
+  for (int i = threadIdx.x; i < NMF * S * 64; i += kStreamThreads) xt[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = threadIdx.x; i < 2 * NMF * bpr; i += kStreamThreads) sxs[i] = 0.0f;
+
+  // ---- x -> NVFP4 (global amax over all of [B, K], then per 16-value block)
+  auto vec_absmax = [&](const u32x4& v) {
+    if (XBF16) {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t t = w4[j] & 0x7fff7fffu;
+        m = umax(m, umax(t << 16, t & 0xffff0000u));
+      }
+      return m;
+    }
+    return umax(umax(v.x & 0x7fffffffu, v.y & 0x7fffffffu),
+                umax(v.z & 0x7fffffffu, v.w & 0x7fffffffu));
+  };
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kXB; ++i)
+#pragma unroll
+    for (int v = 0; v < VPB; ++v) m = umax(m, vec_absmax(xr[i][v]));
+  for (int blk0 = threadIdx.x + kXB * kStreamThreads; blk0 < nblk; blk0 += kStreamThreads) {
+    bool ok;
+    const u32x4* src = block_src(blk0, ok);
+#pragma unroll
+    for (int v = 0; v < VPB; ++v) m = umax(m, vec_absmax(ok ? src[v] : u32x4{0u, 0u, 0u, 0u}));
+  }
+  const float s_gx = nv_global_scale(__uint_as_float(block_max_1024(m, red_max)));
+  auto quant_block = [&](int blk, const u32x4 (&vv)[VPB]) {
+    const int row = blk / bpr, kb = blk - row * bpr;
+    if (kb * 16 >= K) return;                    // padding past K stays zero
+    float v[16];
+    if (XBF16) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w4[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[8 * j + 2 * q] = bf16_lo(w4[q]);
+          v[8 * j + 2 * q + 1] = bf16_hi(w4[q]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[4 * j] = __uint_as_float(vv[j].x);
+        v[4 * j + 1] = __uint_as_float(vv[j].y);
+        v[4 * j + 2] = __uint_as_float(vv[j].z);
+        v[4 * j + 3] = __uint_as_float(vv[j].w);
+      }
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) am = umax(am, __float_as_uint(v[j]) & 0x7fffffffu);
+    uint32_t sc;
+    float r;
+    nv_block_scale(__uint_as_float(am), s_gx, sc, r);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = v[j] * r;
+    sxs[row * bpr + kb] = e4m3_value(sc);
+    // tile t = row / 2, x row m = 8 (row % 2) + i of step kb / 8, block i = kb % 8
+    // in K group i / 2 (lane m + 16 (i / 2)), half i % 2 of that lane's 16 bytes
+    const int i = kb & 7, mrow = ((row & 1) << 3) | i;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(xt) +
+                   (((row >> 1) * S + (kb >> 3)) * 64 + mrow + 16 * (i >> 1)) * 16 + 8 * (i & 1);
+    *reinterpret_cast<u32x2*>(dst) = u32x2{e2m1_pack8(v), e2m1_pack8(v + 8)};
+  };
+#pragma unroll
+  for (int i = 0; i < kXB; ++i) {
+    const int blk = threadIdx.x + i * kStreamThreads;
+    if (blk < nblk) quant_block(blk, xr[i]);
+  }
+  for (int blk = threadIdx.x + kXB * kStreamThreads; blk < nblk; blk += kStreamThreads) {
+    bool ok;
+    const u32x4* src = block_src(blk, ok);
+    u32x4 t[VPB];
+#pragma unroll
+    for (int v = 0; v < VPB; ++v) t[v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+    quant_block(blk, t);
+  }
+  __syncthreads();
+  const float gscale = s_gx * (*g_w);
+
+  // ---- stream W
+  float acc[NMF];
+#pragma unroll
+  for (int t = 0; t < NMF; ++t) acc[t] = 0.0f;
+  // Sum over the lane pair holding one (batch row, W row) -- g and g ^ 1 -- then
+  // over the two K parts (the upper part's sums go through LDS, double-buffered
+  // by round parity, one barrier per round), in a fixed order; write y.
+  auto finish = [&](int r, bool valid) {
+    float a[NMF];
+#pragma unroll
+    for (int t = 0; t < NMF; ++t) a[t] = acc[t] + __shfl_xor(acc[t], 16, 64);
+    float* rp = red + (((r & 1) * kSlots + slot) * 64 + lane) * NMF;
+    if (part != 0) {
+#pragma unroll
+      for (int t = 0; t < NMF; ++t) rp[t] = a[t];
+    }
+    __syncthreads();
+    if (part != 0 || !valid) return;
+#pragma unroll
+    for (int t = 0; t < NMF; ++t) a[t] = a[t] + rp[t];
+    const int nn = (s_first + r * G) * 16 + n16;
+    if ((g & 1) == 0 && nn < N) {
+#pragma unroll
+      for (int t = 0; t < NMF; ++t) {
+        const int ob = 2 * t + (g >> 1);
+        if (ob < B) {
+          const float v = (a[t] * gscale) * g_d;
+          if (YBF16)
+            reinterpret_cast<uint16_t*>(y)[(int64_t)ob * N + nn] = (uint16_t)f32_to_bf16(v);
+          else
+            reinterpret_cast<float*>(y)[(int64_t)ob * N + nn] = v;
+        }
+      }
+    }
+  };
+  int cr = 0, ce = 0;                            // element being computed
+  const float* sx_lane = sxs + (g >> 1) * bpr + 4 * (g & 1);
+  // transpose tile: 16-byte chunk c of row r at chunk position c ^ (r % 8) ^ 4 (r / 8)
+  const int wsw = (r8 ^ c8) << 4;
+  auto elem = [&](int i) {
+    if (i == 0) *reinterpret_cast<u32x4*>(sgw + lane * 16) = sg;   // [pair q][row n] x 16 bytes
+    *reinterpret_cast<u32x4*>(tb + r8 * 128 + wsw) = ra[i];
+    *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + (wsw ^ 64)) = rb[i];
+    load_elem(i);
+    if (ce < E) {
+      const int step = 2 * (pbeg + ce);
+      // row n's scale bytes of this pair, blocks 8 st + 4 (g % 2) .. +3
+      const u32x2 sw2 = u32x2{*reinterpret_cast<const uint32_t*>(sgw + (16 * i + n16) * 16 + 4 * (g & 1)),
+                              *reinterpret_cast<const uint32_t*>(sgw + (16 * i + n16) * 16 + 8 + 4 * (g & 1))};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int c = 4 * st + g;                  // the chunk that is this lane's K group
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(
+            tb + n16 * 128 + ((c ^ (n16 & 7) ^ ((n16 >> 3) << 2)) << 4));
+        const uint32_t sw = st ? sw2.y : sw2.x;
+        const v8i wo = {(int)wv.x, (int)wv.y, (int)wv.z, (int)wv.w, 0, 0, 0, 0};
+        // the four E4M3 scale bytes of W row n, blocks 4 (g % 2) .. +3 of the step
+        const f32x2 w01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sw, false);
+        const f32x2 w23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sw, true);
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+          const u32x4 xo4 = xt[(t * S + step + st) * 64 + lane];
+          const v8i xo = {(int)xo4.x, (int)xo4.y, (int)xo4.z, (int)xo4.w, 0, 0, 0, 0};
+          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              xo, wo, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, 127, 0, 127);
+          const f32x4 sx = *reinterpret_cast<const f32x4*>(sx_lane + 2 * t * bpr + 8 * (step + st));
+          acc[t] = acc[t] + (sx.x * w01.x) * d.x;
+          acc[t] = acc[t] + (sx.y * w01.y) * d.y;
+          acc[t] = acc[t] + (sx.z * w23.x) * d.z;
+          acc[t] = acc[t] + (sx.w * w23.y) * d.w;
+        }
+      }
+    }
+    if (ce == Ep - 1) {
+      finish(cr, true);
+#pragma unroll
+      for (int t = 0; t < NMF; ++t) acc[t] = 0.0f;
+    }
+    if (++ce == Ep) { ce = 0; ++cr; }
+  };
+  for (int j0 = 0; j0 < J; j0 += kFp4Pairs) {
+#pragma unroll
+    for (int i = 0; i < kFp4Pairs; ++i) elem(i);
+  }
+  // every wave takes part in all R rounds' exchanges (see k_gemv_stream)
+  for (int r = Ep > 0 ? nmine : 0; r < R; ++r) finish(r, r < nmine);
+}
+
 // K = 0: every output is an empty sum.
 template <typename T>
 __global__ void __launch_bounds__(256) k_zero_fill(int64_t n, T* __restrict__ y) {
@@ -753,6 +1038,18 @@ struct StreamArgs {
   void* y;
   bool y_bf16;
 };
+
+template <bool XB, int NMF>
+hipError_t launch_fp4(const StreamArgs& a, int grid, int lds, hipStream_t stream) {
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = fp4impl::set_lds_limit_once(
+      lds_set, reinterpret_cast<const void*>(&k_gemv_fp4<XB, NMF>), kStreamLdsMax);
+  if (e != hipSuccess) return e;
+  if (lds > kStreamLdsMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemv_fp4<XB, NMF>), dim3(grid), dim3(kStreamThreads), lds, stream, a.x, a.B,
+                     a.W, a.w_scales, a.g_w, a.N, a.K, a.Kq, a.g_d, a.y, a.y_bf16);
+  return hipGetLastError();
+}
 
 template <int XS, bool XF, int SCM>
 hipError_t launch_stream(const StreamArgs& a, int grid, int lds, hipStream_t stream) {
@@ -840,6 +1137,21 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   const bool xf16 = lds_f16 + lds_fixed <= lds_max;
   // (the strip-relative buffer offsets need 16 rows of W to span < 2^31 bytes;
   // the x' sizes above already keep K far below that)
+  // narrow batches (K a multiple of 64, 4-aligned scale rows): the FP4-MFMA kernel
+  if (B <= 4 && K % 64 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 4 == 0 && K < (1 << 27)) {
+    const int nmf = (int)((B + 1) / 2);
+    const int64_t lds_k = kStreamWaves * 3072 + nmf * (Kq / 128) * 1024 + 2 * nmf * (Kq / 16) * 4 +
+                          2 * kSlots * 64 * nmf * 4;
+    if (lds_k <= lds_max) {
+      const int grid = nstrips < ncu ? nstrips : ncu;
+      const StreamArgs sa{x, ws, (int)B, W, w_scales, g_w, (int)N, (int)K, (int)Kq, 0, g_d, y, y_bf16};
+      if (x_bf16)
+        return nmf == 1 ? launch_fp4<true, 1>(sa, grid, (int)lds_k, stream)
+                        : launch_fp4<true, 2>(sa, grid, (int)lds_k, stream);
+      return nmf == 1 ? launch_fp4<false, 1>(sa, grid, (int)lds_k, stream)
+                      : launch_fp4<false, 2>(sa, grid, (int)lds_k, stream);
+    }
+  }
   if ((xf16 || lds_fp4 + lds_fixed <= lds_max) && K < (1 << 27)) {
     // x' fits LDS as fp16 (narrow batches): every workgroup quantizes the
     // small x itself, one launch in all; wider batches: the prep launch
