@@ -497,7 +497,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
         const int grows = lr < nmine ? min(16, N - r0) : 0;
         const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, grows * srow, kBufferWord3);
-        sg = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane, 16 * pp, 0);
+        // (the whole offset in the VGPR operand, so that the range check covers
+        // it: a group can reach past the scale row, and past the last row's end)
+        sg = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 16 * pp, 0, 0);
       }
     } else {
       const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
@@ -733,11 +735,15 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
 // four scale bytes for those blocks are contiguous.  Rounds, strips, the split
 // of K between two waves and the exchange of partial sums are those of
 // k_gemv_stream; every workgroup quantizes the small x itself.
-// Pairs of 128-value steps in flight per wave, which is also the group of pairs
-// whose W scale bytes (16 rows x 4 pairs x 16 bytes) arrive with one 16-byte
-// load per lane, passed on through a 1 KB LDS area per wave (per-pair scale
-// loads of a few bytes from 16 rows each would double the memory requests).
-constexpr int kFp4Pairs = 4;
+// Pairs of 128-value steps in flight per wave (deeper rings measured slower).
+// W's scale bytes come in groups of kFp4Group pairs: 16 rows x 128 bytes, two
+// loads of 8 rows x 128 bytes issued with the group's first pair and passed on
+// through a 2 KB LDS area per wave (16-byte loads from 16 rows x 64 bytes cost
+// ~2 us more per call at the decode shape; per-pair loads of a few bytes from
+// 16 rows each would double the memory requests).
+constexpr int kFp4Pairs = 2;
+constexpr int kFp4Group = 8;
+constexpr int kFp4WaveLds = 2048 + 16 * kFp4Group * 16;   // transpose tile + scale group
 
 template <bool XBF16, int NMF>
 __global__ void __launch_bounds__(kStreamThreads, 1)
@@ -754,13 +760,14 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   const int wrow = K / 2, srow = K / 16;
   const int S = Kq / 128;                        // 128-value steps
   const int bpr = Kq / 16;                       // x blocks per padded row
-  // LDS: W transpose tiles [16 waves] x 2 KB | W scale groups [16 waves] x 1 KB |
-  // x operand tiles [NMF][S][64 lanes] x 16 bytes | x block scales (E4M3
-  // values) [2 NMF][bpr] floats | partial sums [2][kSlots][64][NMF] floats
+  // LDS: W transpose tiles [16 waves] x 2 KB | W scale groups [16 waves] x
+  // [kFp4Group pairs][16 rows] x 16 bytes | x operand tiles [NMF][S][64 lanes]
+  // x 16 bytes | x block scales (E4M3 values) [2 NMF][bpr] floats | partial
+  // sums [2][kSlots][64][NMF] floats
   uint8_t* tb = lds + wave * 2048;
-  uint8_t* sgw = lds + kStreamWaves * 2048 + wave * 1024;
-  u32x4* xt = reinterpret_cast<u32x4*>(lds + kStreamWaves * 3072);
-  float* sxs = reinterpret_cast<float*>(lds + kStreamWaves * 3072 + NMF * S * 1024);
+  uint8_t* sgw = lds + kStreamWaves * 2048 + wave * (kFp4WaveLds - 2048);
+  u32x4* xt = reinterpret_cast<u32x4*>(lds + kStreamWaves * kFp4WaveLds);
+  float* sxs = reinterpret_cast<float*>(lds + kStreamWaves * kFp4WaveLds + NMF * S * 1024);
   float* red = sxs + 2 * NMF * bpr;
 
   // ---- x: first blocks into registers (thread t owns blocks t + i * 1024)
@@ -786,8 +793,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   // k_gemv_stream).  A pair is 16 strip rows x 128 bytes: lane l loads the
   // 16-byte chunk l % 8 of rows l / 8 and 8 + l / 8.  Chunk c holds values
   // 256 p + 32 c .. +32, which the MFMA of step c / 4 takes as K group c % 4 (x's
-  // operand tiles follow the same order).  With a group's first pair p, lane
-  // (g, n) loads row n's 16 scale bytes of pair p + g.
+  // operand tiles follow the same order).  With a scale group's first pair p,
+  // lane l loads the 16 scale bytes of pair p + l % 8 of rows l / 8 and
+  // 8 + l / 8.
   const int part = wave / kSlots, slot = wave - part * kSlots;
   const int Pq = Kq / 256;
   const int Ph = (Pq + kSplit - 1) / kSplit;
@@ -800,10 +808,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   const int nmine = s_first < nstrips ? (nstrips - s_first + G - 1) / G : 0;
   const int J = nmine * Ep;
   u32x4 ra[kFp4Pairs], rb[kFp4Pairs];
-  u32x4 sg;                                      // scale group in flight
+  u32x4 sga, sgb;                                // scale group in flight
   const int r8 = lane >> 3, c8 = lane & 7;
   const int w_lane = r8 * wrow + 16 * c8;
-  const int g_lane = n16 * srow + 16 * g;
+  const int g_lane = r8 * srow + 16 * c8;
   int lr = 0, le = 0;                            // next element to load
   auto load_elem = [&](int i) {
     const bool live = lr < nmine && le < E;
@@ -814,11 +822,14 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     const int pp = pbeg + le;
     ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, 128 * pp, kLoadNT);
     rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + 8 * wrow, 128 * pp, kLoadNT);
-    if (i == 0) {   // the group's first pair (le % kFp4Pairs == 0): its kFp4Pairs pairs' scales
+    if (le % kFp4Group == 0) {   // a scale group's first pair: the group's scale bytes
       const int grows = lr < nmine ? min(16, N - r0) : 0;
       const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, grows * srow, kBufferWord3);
-      sg = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane, 16 * pp, 0);
+      // (the whole offset in the VGPR operand, so that the range check covers it:
+      // a group can reach past the scale row, and past the last row's end)
+      sga = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 16 * pp, 0, 0);
+      sgb = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 8 * srow + 16 * pp, 0, 0);
     }
     if (++le >= Ep) { le = 0; ++lr; }
   };
@@ -953,15 +964,19 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   // transpose tile: 16-byte chunk c of row r at chunk position c ^ (r % 8) ^ 4 (r / 8)
   const int wsw = (r8 ^ c8) << 4;
   auto elem = [&](int i) {
-    if (i == 0) *reinterpret_cast<u32x4*>(sgw + lane * 16) = sg;   // [pair q][row n] x 16 bytes
+    const int q = ce % kFp4Group;                // pair within its scale group
+    if (q == 0) {                                // [pair q][row n] x 16 bytes
+      *reinterpret_cast<u32x4*>(sgw + (16 * c8 + r8) * 16) = sga;
+      *reinterpret_cast<u32x4*>(sgw + (16 * c8 + 8 + r8) * 16) = sgb;
+    }
     *reinterpret_cast<u32x4*>(tb + r8 * 128 + wsw) = ra[i];
     *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + (wsw ^ 64)) = rb[i];
     load_elem(i);
     if (ce < E) {
       const int step = 2 * (pbeg + ce);
       // row n's scale bytes of this pair, blocks 8 st + 4 (g % 2) .. +3
-      const u32x2 sw2 = u32x2{*reinterpret_cast<const uint32_t*>(sgw + (16 * i + n16) * 16 + 4 * (g & 1)),
-                              *reinterpret_cast<const uint32_t*>(sgw + (16 * i + n16) * 16 + 8 + 4 * (g & 1))};
+      const u32x2 sw2 = u32x2{*reinterpret_cast<const uint32_t*>(sgw + (16 * q + n16) * 16 + 4 * (g & 1)),
+                              *reinterpret_cast<const uint32_t*>(sgw + (16 * q + n16) * 16 + 8 + 4 * (g & 1))};
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int c = 4 * st + g;                  // the chunk that is this lane's K group
@@ -1140,7 +1155,7 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   // narrow batches (K a multiple of 64, 4-aligned scale rows): the FP4-MFMA kernel
   if (B <= 4 && K % 64 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 4 == 0 && K < (1 << 27)) {
     const int nmf = (int)((B + 1) / 2);
-    const int64_t lds_k = kStreamWaves * 3072 + nmf * (Kq / 128) * 1024 + 2 * nmf * (Kq / 16) * 4 +
+    const int64_t lds_k = kStreamWaves * kFp4WaveLds + nmf * (Kq / 128) * 1024 + 2 * nmf * (Kq / 16) * 4 +
                           2 * kSlots * 64 * nmf * 4;
     if (lds_k <= lds_max) {
       const int grid = nstrips < ncu ? nstrips : ncu;
