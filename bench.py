@@ -198,6 +198,31 @@ def same_size_copy_gbs(torch, dev, traffic_bytes, steps):
     return 2 * half / (float(np.median(times)) * 1e-3) / 1e9
 
 
+def same_size_read_gbs(torch, dev, read_bytes, steps):
+    """GB/s of a plain read-only pass over read_bytes per call: a row-wise max
+    over an int32 [R, 4096] tensor (writing R values, 0.02% of the bytes read),
+    timed as the calls are (graph over >= 1 GiB of buffers, median per call)."""
+    cols = 4096
+    rows = max(1, read_bytes // (4 * cols))
+    nbytes = rows * cols * 4
+    n = max(2, -(-GiB // nbytes))
+    srcs = [torch.zeros((rows, cols), dtype=torch.int32, device=dev) for _ in range(n)]
+    outs = [torch.empty(rows, dtype=torch.int32, device=dev) for _ in range(n)]
+
+    def red(i):
+        torch.amax(srcs[i], dim=1, out=outs[i])
+
+    op = Op("read", red, n, "GB/s", nbytes, HBM_PEAK_GBS, "hbm", "amax", None)
+    op.capture(torch)
+    times = []
+    for _ in range(steps):
+        e0, e1 = op.replay_timed(torch)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / n)
+    del op, srcs, outs
+    return nbytes / (float(np.median(times)) * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -568,9 +593,10 @@ def main():
     # captured and replayed like the calls above: the rate a kernel of that size
     # reaches, launch ramp and tail included
     gemv_ops = [op for op in ops if op.name.startswith("gemv_b")]
-    copy_small_gbs = None
+    copy_small_gbs = read_small_gbs = None
     if gemv_ops:
         copy_small_gbs = same_size_copy_gbs(torch, dev, gemv_ops[0].per_call, max(args.steps, 3))
+        read_small_gbs = same_size_read_gbs(torch, dev, gemv_ops[0].per_call, max(args.steps, 3))
 
     traffic = load_traffic()
     comps = {}
@@ -602,6 +628,7 @@ def main():
             comps[op.name]["frac_of_copy"] = round(achieved / copy_gbs, 4)
         if op in gemv_ops:
             comps[op.name]["frac_of_same_size_copy"] = round(achieved / copy_small_gbs, 4)
+            comps[op.name]["frac_of_same_size_read"] = round(achieved / read_small_gbs, 4)
         if op.name in ("gemm_nvfp4", "gemm_nvfp4_e4m3_out", "gemm_nvfp4_nvfp4_out"):
             comps[op.name]["frac_of_fp4_peak"] = round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4)
 
@@ -651,7 +678,10 @@ def main():
                     "note": "torch copy_ of 512 MiB, for reference against the 8 TB/s peak",
                     "device_copy_gemv_size_GBs": None if copy_small_gbs is None else round(copy_small_gbs, 1),
                     "gemv_size_note": "torch copy_ moving the GEMV's bytes per call (half read, half "
-                                      "written), as a graph cycling over >= 1 GiB of buffers"},
+                                      "written), as a graph cycling over >= 1 GiB of buffers",
+                    "device_read_gemv_size_GBs": None if read_small_gbs is None else round(read_small_gbs, 1),
+                    "gemv_read_note": "torch amax over rows of an int32 tensor of the GEMV's bytes per "
+                                      "call (read only), as a graph cycling over >= 1 GiB of buffers"},
         "setup_s": round(setup_s, 1),
     }
 

@@ -337,7 +337,7 @@ constexpr int kStreamThreads = 1024;
 constexpr int kStreamWaves = kStreamThreads / 64;
 constexpr int kSplit = 2;                       // waves per strip (K parts)
 constexpr int kSlots = kStreamWaves / kSplit;   // strips per workgroup and round
-constexpr int kPairs = 4;                       // pairs of steps in flight per wave
+constexpr int kPairs = 2;                       // pairs of steps in flight per wave (4: ~2 us slower at B = 16)
 constexpr int kXRegVecs = 4;                    // 16-byte x vectors per thread held in registers
 constexpr int kRedBytes = 2 * kSlots * 64 * 16; // double-buffered partial tiles
 constexpr int kStreamLdsMax = 160 * 1024 - 256;  // dynamic LDS (the kernel has no static LDS)
@@ -364,13 +364,17 @@ __device__ __forceinline__ uint32_t block_max_1024(uint32_t v, uint32_t* red) {
 // products.  A lane's W scales for a pair are then 4 contiguous bytes.
 //
 // W scale bytes (SCM):
-//   kScaleGroup  K % 256 == 0 and 16-aligned scales: the group's scales, 16 rows x
-//                kPairs * 16 bytes, arrive with one 16-byte load per lane issued
-//                with the group before (ring slot 0), pass through a 1 KB LDS
-//                area per wave, and each pair reads its dword there.
+//   kScaleGroup  K % 256 == 0 and 16-aligned scales: the scales of kGroupPairs
+//                pairs, 16 rows x 128 bytes, arrive with two loads of 8 rows x
+//                128 bytes issued with the group's first pair, pass through a
+//                2 KB LDS area per wave, and each pair reads its dword there
+//                (loads of 16 rows x 64 bytes cost ~2 us more per call at the
+//                decode shape).
 //   kScaleDword  K % 64 == 0, 4-aligned: one dword load per pair.
 //   kScaleHalf   otherwise: two 16-bit loads per pair.
 constexpr int kScaleHalf = 0, kScaleDword = 1, kScaleGroup = 2;
+constexpr int kGroupPairs = 8;                   // pairs per W scale group
+constexpr int kGroupLds = 16 * kGroupPairs * 16; // a scale group in LDS: [pair][16 rows] x 16 bytes
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
 constexpr int kLoadNT = 2;                      // buffer load cache policy: nontemporal
 
@@ -477,13 +481,13 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   // offset inside the strip is fixed; the pair's offset is a scalar.
   u32x4 ra[kPairs], rb[kPairs];
   uint32_t rs[kPairs];
-  u32x4 sg;                                      // scale group in flight
+  u32x4 sga, sgb;                                 // scale group in flight
   const int w_lane = r8 * wrow + 16 * c8;
   const int s_lane = b * srow + 4 * g;
-  const int g_lane = b * srow + 16 * g;          // group load: row b, pair g of the group
-  uint8_t* sa = lds + lds_x_bytes + kStreamWaves * 2048 + kRedBytes + wave * 1024;
+  const int g_lane = r8 * srow + 16 * c8;        // group loads: rows r8, 8 + r8, pair c8 of the group
+  uint8_t* sa = lds + lds_x_bytes + kStreamWaves * 2048 + kRedBytes + wave * kGroupLds;
   int lr = 0, le = 0;                            // next element to load
-  auto load_elem = [&](u32x4& a, u32x4& bb, uint32_t& sc, bool group) {
+  auto load_elem = [&](u32x4& a, u32x4& bb, uint32_t& sc) {
     const bool live = lr < nmine && le < E;
     const int r0 = lr < nmine ? (s_first + lr * G) * 16 : 0;
     const int rows = live ? min(16, N - r0) : 0;
@@ -493,13 +497,14 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     a = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, 128 * pp, kLoadNT);
     bb = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + 8 * wrow, 128 * pp, kLoadNT);
     if (SCM == kScaleGroup) {
-      if (group) {   // the group's first element (le % kPairs == 0): its kPairs pairs
+      if (le % kGroupPairs == 0) {   // a scale group's first pair: the group's scale bytes
         const int grows = lr < nmine ? min(16, N - r0) : 0;
         const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, grows * srow, kBufferWord3);
         // (the whole offset in the VGPR operand, so that the range check covers
         // it: a group can reach past the scale row, and past the last row's end)
-        sg = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 16 * pp, 0, 0);
+        sga = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 16 * pp, 0, 0);
+        sgb = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 8 * srow + 16 * pp, 0, 0);
       }
     } else {
       const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
@@ -515,7 +520,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     if (++le >= Ep) { le = 0; ++lr; }
   };
 #pragma unroll
-  for (int i = 0; i < kPairs; ++i) load_elem(ra[i], rb[i], rs[i], i == 0);
+  for (int i = 0; i < kPairs; ++i) load_elem(ra[i], rb[i], rs[i]);
 
   float s_gx;
   if constexpr (XSRC == kXFromWs) {
@@ -661,14 +666,17 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   // dequantize and accumulate.
   auto elem = [&](u32x4& ra_i, u32x4& rb_i, uint32_t& rs_i, int i) {
     uint32_t sw = rs_i;
-    if (SCM == kScaleGroup && i == 0)
-      *reinterpret_cast<u32x4*>(sa + lane * 16) = sg;   // [pair q][row b] x 16 bytes
+    const int q = ce % kGroupPairs;              // pair within its scale group
+    if (SCM == kScaleGroup && q == 0) {          // [pair q][row b] x 16 bytes
+      *reinterpret_cast<u32x4*>(sa + (16 * c8 + r8) * 16) = sga;
+      *reinterpret_cast<u32x4*>(sa + (16 * c8 + 8 + r8) * 16) = sgb;
+    }
     *reinterpret_cast<u32x4*>(tb + r8 * 128 + wsw) = ra_i;
     *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + (wsw ^ 64)) = rb_i;
-    load_elem(ra_i, rb_i, rs_i, i == 0);
+    load_elem(ra_i, rb_i, rs_i);
     if (ce < E) {
       if (SCM == kScaleGroup)
-        sw = *reinterpret_cast<const uint32_t*>(sa + (16 * i + b) * 16 + 4 * g);
+        sw = *reinterpret_cast<const uint32_t*>(sa + (16 * q + b) * 16 + 4 * g);
       const int cpp = pbeg + ce;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -736,14 +744,13 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
 // of K between two waves and the exchange of partial sums are those of
 // k_gemv_stream; every workgroup quantizes the small x itself.
 // Pairs of 128-value steps in flight per wave (deeper rings measured slower).
-// W's scale bytes come in groups of kFp4Group pairs: 16 rows x 128 bytes, two
+// W's scale bytes come in groups of kGroupPairs pairs: 16 rows x 128 bytes, two
 // loads of 8 rows x 128 bytes issued with the group's first pair and passed on
 // through a 2 KB LDS area per wave (16-byte loads from 16 rows x 64 bytes cost
 // ~2 us more per call at the decode shape; per-pair loads of a few bytes from
 // 16 rows each would double the memory requests).
 constexpr int kFp4Pairs = 2;
-constexpr int kFp4Group = 8;
-constexpr int kFp4WaveLds = 2048 + 16 * kFp4Group * 16;   // transpose tile + scale group
+constexpr int kFp4WaveLds = 2048 + kGroupLds;   // transpose tile + scale group
 
 template <bool XBF16, int NMF>
 __global__ void __launch_bounds__(kStreamThreads, 1)
@@ -761,11 +768,11 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   const int S = Kq / 128;                        // 128-value steps
   const int bpr = Kq / 16;                       // x blocks per padded row
   // LDS: W transpose tiles [16 waves] x 2 KB | W scale groups [16 waves] x
-  // [kFp4Group pairs][16 rows] x 16 bytes | x operand tiles [NMF][S][64 lanes]
+  // [kGroupPairs pairs][16 rows] x 16 bytes | x operand tiles [NMF][S][64 lanes]
   // x 16 bytes | x block scales (E4M3 values) [2 NMF][bpr] floats | partial
   // sums [2][kSlots][64][NMF] floats
   uint8_t* tb = lds + wave * 2048;
-  uint8_t* sgw = lds + kStreamWaves * 2048 + wave * (kFp4WaveLds - 2048);
+  uint8_t* sgw = lds + kStreamWaves * 2048 + wave * kGroupLds;
   u32x4* xt = reinterpret_cast<u32x4*>(lds + kStreamWaves * kFp4WaveLds);
   float* sxs = reinterpret_cast<float*>(lds + kStreamWaves * kFp4WaveLds + NMF * S * 1024);
   float* red = sxs + 2 * NMF * bpr;
@@ -822,7 +829,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
     const int pp = pbeg + le;
     ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, 128 * pp, kLoadNT);
     rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + 8 * wrow, 128 * pp, kLoadNT);
-    if (le % kFp4Group == 0) {   // a scale group's first pair: the group's scale bytes
+    if (le % kGroupPairs == 0) {   // a scale group's first pair: the group's scale bytes
       const int grows = lr < nmine ? min(16, N - r0) : 0;
       const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, grows * srow, kBufferWord3);
@@ -964,7 +971,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   // transpose tile: 16-byte chunk c of row r at chunk position c ^ (r % 8) ^ 4 (r / 8)
   const int wsw = (r8 ^ c8) << 4;
   auto elem = [&](int i) {
-    const int q = ce % kFp4Group;                // pair within its scale group
+    const int q = ce % kGroupPairs;                // pair within its scale group
     if (q == 0) {                                // [pair q][row n] x 16 bytes
       *reinterpret_cast<u32x4*>(sgw + (16 * c8 + r8) * 16) = sga;
       *reinterpret_cast<u32x4*>(sgw + (16 * c8 + 8 + r8) * 16) = sgb;
@@ -1147,7 +1154,7 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   int scm = kScaleHalf;
   if (K % 64 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 4 == 0) scm = kScaleDword;
   if (K % 256 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 16 == 0) scm = kScaleGroup;
-  const int64_t lds_fixed = kStreamWaves * 2048 + kRedBytes + kStreamWaves * 1024;
+  const int64_t lds_fixed = kStreamWaves * 2048 + kRedBytes + kStreamWaves * kGroupLds;
   const int64_t lds_max = kStreamLdsMax;
   const bool xf16 = lds_f16 + lds_fixed <= lds_max;
   // (the strip-relative buffer offsets need 16 rows of W to span < 2^31 bytes;
