@@ -28,6 +28,26 @@ inline hipError_t set_lds_limit_once(std::atomic<uint64_t>& done, const void* fn
   return e;
 }
 
+// Compute units of the current device, looked up once per device (devices
+// >= 64: on every call), so calls on devices of different sizes (compute
+// partitions) each see their own count.
+inline int num_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int cus = 0;
+  const int n = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                        cus > 0
+                    ? cus
+                    : 256;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 constexpr int kAmaxPartials = 1024;  // FP4_AMAX_WORKSPACE_BYTES / 4
 
 // ---- quantize.hip ---------------------------------------------------------

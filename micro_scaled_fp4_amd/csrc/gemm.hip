@@ -331,13 +331,13 @@ __device__ __forceinline__ void store_scales(const StageScales<MX>& r, uint8_t* 
 // (before the multiply by alpha) in acc[i][j].  EDGE: the tile may cross M or
 // N, or rows may not take whole 4-output stores; otherwise every store is
 // whole and unconditional.
-template <int OUT, bool EDGE>
-__device__ __forceinline__ void store_outputs(v4f (&acc)[kTN][kTM], float alpha, float s_glob,
+template <int OUT, bool EDGE, int TN = kTN, int TM = kTM>
+__device__ __forceinline__ void store_outputs(v4f (&acc)[TN][TM], float alpha, float s_glob,
                                               int mb, int nb, int M, int N, void* __restrict__ D,
                                               uint8_t* __restrict__ d_scales, bool vec_out, int r16,
                                               int g) {
 #pragma unroll
-  for (int j = 0; j < kTM; ++j) {
+  for (int j = 0; j < TM; ++j) {
     const int m = mb + 16 * j;
     if (EDGE && m >= M) continue;
     if constexpr (OUT == 0) {
@@ -349,7 +349,7 @@ __device__ __forceinline__ void store_outputs(v4f (&acc)[kTN][kTM], float alpha,
       uint8_t* qrow = reinterpret_cast<uint8_t*>(D) + (int64_t)m * ((N + 1) / 2);
       uint8_t* srow = d_scales + (int64_t)m * ((N + 15) / 16);
 #pragma unroll
-      for (int i4 = 0; i4 < kTN; i4 += 4) {
+      for (int i4 = 0; i4 < TN; i4 += 4) {
         v4f x[4];
         float a[4];
 #pragma unroll
@@ -392,7 +392,7 @@ __device__ __forceinline__ void store_outputs(v4f (&acc)[kTN][kTM], float alpha,
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kTN; ++i) {
+      for (int i = 0; i < TN; ++i) {
         const int n = nb + 16 * i;
         asm volatile("" : "+a"(acc[i][j]));
         const v4f v = acc[i][j] * alpha;
@@ -790,6 +790,287 @@ __global__ void __launch_bounds__(kThreads, 1)
     store_outputs<OUT, true>(acc, alpha, s_glob, mb, nb, M, N, D, d_scales, vec_out, r16, g);
 }
 
+// ------------------------------------------------ MXFP4 kernel, 8 waves --
+// The MXFP4 GEMM with 8 waves (2 per SIMD) on the same 256 x 256 tile: a
+// 2 x 4 wave grid, each wave 128 x 64 outputs (8 A tiles by 4 W tiles of
+// 16 x 16, 128 accumulator registers).  Stages, tile swizzle, load schedule,
+// A's scale layout and the epilogue are those of k_gemm.  With two waves on a
+// SIMD, one wave's MFMAs run while the other is held up issuing its
+// direct-to-LDS loads, reading LDS or at the stage barrier.  A wave reads 8 A
+// and 4 W fragments per k-step, so a CU reads 96 KB of fragments per k-step
+// (64 KB with 4 waves of 128 x 128).  W's scale layout follows the wave
+// quarters: entry (q, g, r16, i) holds the two bytes (k-steps 0 and 1) of lane
+// group g for row r16 of MFMA tile i of W quarter q, so a lane reads its 4
+// tiles' bytes with one 8-byte read.
+constexpr int kThreads8 = 512;
+constexpr int kW8N = 4;                          // waves along W (2 along A)
+constexpr int kT8N = 4;                          // W tiles per wave (kTM A tiles)
+static_assert(16 * kTM * 2 == BM && 16 * kT8N * kW8N == BN, "the 8-wave grid covers the tile");
+
+// Block q (of 4) of this wave's share of an operand tile: block b = wave + 8q
+// holds rows 8b .. 8b + 7 (their swizzle depends only on b's parity, the
+// wave's), filled as in dma_block.
+template <bool SCALE_VEC>
+__device__ __forceinline__ void dma_block8(__amdgpu_buffer_rsrc_t src, uint8_t* tile, int rowb, int K,
+                                           int k0, int q) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = 8 * wave + (lane >> 3);
+  const int ch = (lane & 7) ^ ((row0 >> 1) & 7);
+  const int kc = k0 + 32 * ch;
+  lds_void* dst = (lds_void*)(tile + 1024 * (wave + 8 * q));
+  if (SCALE_VEC)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, row0 * rowb + kc / 2, 64 * q * rowb, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, kc < K ? (row0 + 64 * q) * rowb + kc / 2 : kOutOfRange,
+                                             0, 0, 0);
+}
+
+template <bool SCALE_VEC>
+__device__ __forceinline__ void dma_tile8(__amdgpu_buffer_rsrc_t src, uint8_t* tile, int rowb, int K,
+                                          int k0) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dma_block8<SCALE_VEC>(src, tile, rowb, K, k0, q);
+}
+
+// Threads 0..255 hold A's scale row t of a stage, threads 256..511 W's row
+// t - 256 (8 bytes each).
+__device__ __forceinline__ bool holds_a_scales() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4;
+}
+
+template <bool SCALE_VEC>
+__device__ __forceinline__ void load_scales8(StageScales<true>& r, __amdgpu_buffer_rsrc_t sa,
+                                             __amdgpu_buffer_rsrc_t sw, int nsc, int k0) {
+  const __amdgpu_buffer_rsrc_t src = holds_a_scales() ? sa : sw;
+  const int kb = k0 / 32;
+  const int sr = threadIdx.x & 255;
+  if (SCALE_VEC) {   // K % 256 == 0 and 16-byte aligned scale rows
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(src, sr * nsc + kb, 0, 0);
+    r.s[0] = v.x;
+    r.s[1] = v.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = kb + 4 * q + i;
+        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(src, b < nsc ? sr * nsc + b : kOutOfRange,
+                                                             0, 0) << (8 * i);
+      }
+      r.s[q] = v;
+    }
+  }
+}
+
+__device__ __forceinline__ void store_scales8(const StageScales<true>& r, uint8_t* __restrict__ sc_a,
+                                              uint8_t* __restrict__ sc_w) {
+  const int t = threadIdx.x & 255, r16 = t & 15;
+  const bool a = holds_a_scales();
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint16_t v = (uint16_t)(r.s[g >> 1] >> (16 * (g & 1)));
+    if (a)   // A: (half h, g, r16, tile i of 8), as store_scales
+      reinterpret_cast<uint16_t*>(sc_a)[(((t >> 7) * 4 + g) * 16 + r16) * 8 + ((t >> 4) & 7)] = v;
+    else     // W: (quarter q, g, r16, tile i of 4)
+      reinterpret_cast<uint16_t*>(sc_w)[(((t >> 6) * 4 + g) * 16 + r16) * 4 + ((t >> 4) & 3)] = v;
+  }
+}
+
+// Persistent: the grid is at most one workgroup per CU, and workgroup w takes
+// tiles w, w + G, w + 2G, ... (G = grid size, a multiple of the XCD count, so
+// a workgroup stays on one XCD and tile_of's XCD ranges hold).  The load
+// schedule runs on across tiles: the last stage of a tile loads the first two
+// stages of the next one, and the tile's output stores drain while the next
+// tile computes (with one tile per workgroup launch, every tile's stores and
+// load fill stood between two tiles' MFMAs: ~15% of the 8192 x 28672 x 8192
+// GEMM).  A tile's stages are padded to an even count (two per loop
+// iteration); a padding stage loads nothing and adds exact zeros.
+template <int OUT, bool SCALE_VEC>
+__global__ void __launch_bounds__(kThreads8, 1)
+    k_gemm_mx8(const uint8_t* __restrict__ A, const uint8_t* __restrict__ as,
+               const uint8_t* __restrict__ W, const uint8_t* __restrict__ ws, float g_d, int M,
+               int N, int K, void* __restrict__ D, uint8_t* __restrict__ d_scales,
+               const float* __restrict__ d_amax, float* __restrict__ d_gscale, int tiles_m,
+               int tiles_n, bool vec_out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int T = tiles_m * tiles_n, G = gridDim.x;
+  int bid = blockIdx.x;
+  if (bid >= T) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / kW8N, wn = wave % kW8N;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int rowb = K / 2, nsc = K / 32;
+
+  // tile b's origin and rows that exist (none past the last tile: loads
+  // through its empty ranges read zeros and touch no memory)
+  struct TileRows {
+    int m0, n0, rows_a, rows_w;
+  };
+  auto tile_rows = [&](int b) {
+    TileRows t{0, 0, 0, 0};
+    if (b < T) {
+      int tm, tn;
+      tile_of(b, tiles_m, tiles_n, tm, tn);
+      t.m0 = tm * BM;
+      t.n0 = tn * BN;
+      t.rows_a = min(BM, M - t.m0);
+      t.rows_w = min(BN, N - t.n0);
+    }
+    return t;
+  };
+  auto rsrc_a = [&](const TileRows& t) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A) + (int64_t)t.m0 * rowb, 0,
+                                             t.rows_a * rowb, kBufferWord3);
+  };
+  auto rsrc_w = [&](const TileRows& t) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W) + (int64_t)t.n0 * rowb, 0,
+                                             t.rows_w * rowb, kBufferWord3);
+  };
+  auto rsrc_as = [&](const TileRows& t) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(as) + (int64_t)t.m0 * nsc, 0,
+                                             t.rows_a * nsc, kBufferWord3);
+  };
+  auto rsrc_ws = [&](const TileRows& t) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ws) + (int64_t)t.n0 * nsc, 0,
+                                             t.rows_w * nsc, kBufferWord3);
+  };
+
+  v4f acc[kT8N][kTM];   // [W tile][A tile]
+#pragma unroll
+  for (int i = 0; i < kT8N; ++i)
+#pragma unroll
+    for (int j = 0; j < kTM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nk = (K + BK - 1) / BK, nk2 = (nk + 1) & ~1;
+  // LDS layout as k_gemm's MXFP4 layout
+  constexpr int kScA = Cfg<true>::kScaleA, kScW = Cfg<true>::kScaleW;
+  constexpr int kTiles = 2 * (kScA + kScW);
+  auto sc_a = [&](int b) { return smem + b * kScA; };
+  auto sc_w = [&](int b) { return smem + 2 * kScA + b * kScW; };
+  auto tile_a = [&](int b) { return smem + kTiles + b * kTileA; };
+  auto tile_w = [&](int b) { return smem + kTiles + 2 * kTileA + b * kTileW; };
+  const __amdgpu_buffer_rsrc_t none =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A), 0, 0, kBufferWord3);
+  const int ra0 = wm * 16 * kTM + r16, rw0 = wn * 16 * kT8N + r16;
+
+  // this lane's scale bytes of a stage: A tile j's two bytes are bytes
+  // 2 (j & 1) + ks of dword j / 2 of sa, W tile i's of dword i / 2 of sw
+  auto read_scales = [&](int b, uint32_t (&sa)[4], uint32_t (&sw)[2]) {
+    const u32x4 va = *reinterpret_cast<const u32x4*>(sc_a(b) + ((wm * 4 + g) * 16 + r16) * 16);
+    const u32x2 vw = *reinterpret_cast<const u32x2*>(sc_w(b) + ((wn * 4 + g) * 16 + r16) * 8);
+    sa[0] = va.x; sa[1] = va.y; sa[2] = va.z; sa[3] = va.w;
+    sw[0] = vw.x; sw[1] = vw.y;
+  };
+  auto frag = [&](const uint8_t* tile, int row, int chunk) {
+    return *reinterpret_cast<const u32x4*>(tile + swz(row, chunk));
+  };
+  // row i of k-step ks: W tile i against the kTM A tiles
+  auto mx_row = [&](auto i_c, auto ks_c, const u32x4 (&fa)[kTM], const u32x4 (&fw)[kT8N],
+                    const uint32_t (&sa)[4], const uint32_t (&sw)[2]) {
+    constexpr int i = decltype(i_c)::value;
+    constexpr int ks = decltype(ks_c)::value;
+    static_for<kTM>([&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      mfma_fp4<2 * (i & 1) + ks, 2 * (j & 1) + ks>(acc[i][j], fw[i], fa[j], sw[i >> 1], sa[j >> 1]);
+    });
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+
+  TileRows cur = tile_rows(bid), nxt = tile_rows(bid + G);
+  // Stage s of a tile lives in buffer s & 1 (nk2 is even, so every tile starts
+  // in buffer 0); loads run two stages ahead as in k_gemm's MXFP4 loop, every
+  // loop body branch-free.
+  StageScales<true> ss;
+  load_scales8<SCALE_VEC>(ss, rsrc_as(cur), rsrc_ws(cur), nsc, 0);
+  dma_tile8<SCALE_VEC>(rsrc_a(cur), tile_a(0), rowb, K, 0);
+  dma_tile8<SCALE_VEC>(rsrc_w(cur), tile_w(0), rowb, K, 0);
+  store_scales8(ss, sc_a(0), sc_w(0));
+  const bool two = nk > 1;
+  load_scales8<SCALE_VEC>(ss, two ? rsrc_as(cur) : none, two ? rsrc_ws(cur) : none, nsc, BK);
+  dma_tile8<SCALE_VEC>(two ? rsrc_a(cur) : none, tile_a(1), rowb, K, BK);
+  dma_tile8<SCALE_VEC>(two ? rsrc_w(cur) : none, tile_w(1), rowb, K, BK);
+  wait_dma();
+  __syncthreads();
+  uint32_t sa0[4], sw0[2], sa1[4], sw1[2];
+  u32x4 fa0[kTM], fw0[kT8N], fa1[kTM], fw1[kT8N];
+  read_scales(0, sa0, sw0);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) fa0[i] = frag(tile_a(0), ra0 + 16 * i, 2 * g);
+#pragma unroll
+  for (int i = 0; i < kT8N; ++i) fw0[i] = frag(tile_w(0), rw0 + 16 * i, 2 * g);
+  wait_lgkm();
+  // One stage: buffer CB holds stage kt (scales sa / sw); row i of a k-step
+  // also reads A fragments 2i, 2i + 1 and W fragment i of the next k-step (the
+  // order the next k-step's first row needs them in).  The loads of stage
+  // kt + 2 come from this tile, or past its (padded) end from the next tile.
+  auto mx_stage = [&](auto cb_c, int kt, const uint32_t (&sa)[4], const uint32_t (&sw)[2],
+                      uint32_t (&sa_n)[4], uint32_t (&sw_n)[2]) {
+    constexpr int cb = decltype(cb_c)::value, nb = cb ^ 1;
+    mfma_lead();
+    static_for<kT8N>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      mx_row(i_c, K0{}, fa0, fw0, sa, sw);
+      fa1[2 * i] = frag(tile_a(cb), ra0 + 32 * i, 2 * g + 1);
+      fa1[2 * i + 1] = frag(tile_a(cb), ra0 + 32 * i + 16, 2 * g + 1);
+      fw1[i] = frag(tile_w(cb), rw0 + 16 * i, 2 * g + 1);
+    });
+    store_scales8(ss, sc_a(nb), sc_w(nb));   // the next stage
+    wait_dma();        // the next stage (issued during the previous stage) has landed
+    __syncthreads();   // it is in buffer nb; nobody reads buffer cb any more
+    const int kl = kt + 2;
+    const bool nx = kl >= nk2;                   // stage kl - nk2 of the next tile
+    const bool live = nx || kl < nk;
+    const int k_ld = (nx ? kl - nk2 : kl) * BK;
+    TileRows lt = nx ? nxt : cur;
+    if (!live) lt.rows_a = lt.rows_w = 0;        // a padding stage: empty ranges
+    const __amdgpu_buffer_rsrc_t la = rsrc_a(lt), lw = rsrc_w(lt);
+    load_scales8<SCALE_VEC>(ss, rsrc_as(lt), rsrc_ws(lt), nsc, k_ld);
+    mfma_lead();
+    static_for<kT8N>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      mx_row(i_c, K1{}, fa1, fw1, sa, sw);
+      if constexpr (i == 0) read_scales(nb, sa_n, sw_n);
+      dma_block8<SCALE_VEC>(la, tile_a(cb), rowb, K, k_ld, i);
+      dma_block8<SCALE_VEC>(lw, tile_w(cb), rowb, K, k_ld, i);
+      fa0[2 * i] = frag(tile_a(nb), ra0 + 32 * i, 2 * g);
+      fa0[2 * i + 1] = frag(tile_a(nb), ra0 + 32 * i + 16, 2 * g);
+      fw0[i] = frag(tile_w(nb), rw0 + 16 * i, 2 * g);
+    });
+    mfma_drain();
+  };
+
+  float s_glob = 1.0f;
+  if (OUT == 0) {
+    s_glob = nv_global_scale(*d_amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *d_gscale = s_glob;
+  }
+  for (;;) {
+    for (int kt = 0; kt < nk2; kt += 2) {
+      mx_stage(std::integral_constant<int, 0>{}, kt, sa0, sw0, sa1, sw1);
+      mx_stage(std::integral_constant<int, 1>{}, kt + 1, sa1, sw1, sa0, sw0);
+    }
+    const int m0 = cur.m0, n0 = cur.n0;
+    const int mb = m0 + wm * 16 * kTM + r16, nb = n0 + wn * 16 * kT8N + 4 * g;
+    if (vec_out && m0 + BM <= M && n0 + BN <= N)
+      store_outputs<OUT, false, kT8N, kTM>(acc, g_d, s_glob, mb, nb, M, N, D, d_scales, true, r16, g);
+    else
+      store_outputs<OUT, true, kT8N, kTM>(acc, g_d, s_glob, mb, nb, M, N, D, d_scales, vec_out, r16, g);
+    bid += G;
+    if (bid >= T) break;
+    cur = nxt;
+    nxt = tile_rows(bid + G);
+    // (compile-time indices: the accumulators stay in registers)
+    static_for<kT8N>([&](auto i_c) {
+      static_for<kTM>([&](auto j_c) {
+        acc[decltype(i_c)::value][decltype(j_c)::value] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      });
+    });
+  }
+}
+
 // Output of one GEMM call: D, plus the NVFP4 scale bytes, given amax and
 // written tensor scale when D holds NVFP4 codes.
 struct OutArgs {
@@ -813,17 +1094,32 @@ hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const
   // grouped: each group adds at most one partial row tile to ceil(M / BM)
   const int tiles_m = (M + BM - 1) / BM + (GROUPED ? gr.ngroups : 0);
   constexpr int lds = Cfg<MX>::kLdsBytes;
+  // MXFP4: the 8-wave kernel (grouped launches: k_gemm, whose group lookup
+  // would not fit the 8-wave kernel's 256 registers without spills); NVFP4: k_gemm
+  constexpr bool kMx8 = MX && !GROUPED;
+  const void* fn = kMx8 ? reinterpret_cast<const void*>(&k_gemm_mx8<OUT, SCALE_VEC>)
+                        : reinterpret_cast<const void*>(&k_gemm<MX, OUT, SCALE_VEC, GROUPED>);
   static std::atomic<uint64_t> lds_set{0};   // devices on which this kernel's LDS limit is set
-  const hipError_t e = fp4impl::set_lds_limit_once(
-      lds_set, reinterpret_cast<const void*>(&k_gemm<MX, OUT, SCALE_VEC, GROUPED>), lds);
+  const hipError_t e = fp4impl::set_lds_limit_once(lds_set, fn, lds);
   if (e != hipSuccess) return e;
   // 4 outputs per store when every row start is aligned to 4 outputs
   // (NVFP4: 4 outputs are 2 bytes)
   const bool vec_out =
       N % 4 == 0 && reinterpret_cast<uintptr_t>(o.D) % (OUT == 0 ? 2 : 4 * OUT) == 0;
-  hipLaunchKernelGGL((k_gemm<MX, OUT, SCALE_VEC, GROUPED>), dim3(tiles_m * tiles_n), dim3(kThreads),
-                     lds, stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, o.D, o.d_scales, o.d_amax,
-                     o.d_gscale, tiles_m, tiles_n, vec_out, gr.offsets, gr.ngroups);
+  if constexpr (kMx8) {
+    // persistent: at most one workgroup per CU, a multiple of the XCD count
+    // when there are more tiles than CUs
+    const int T = tiles_m * tiles_n, ncu = fp4impl::num_cus();
+    const int grid = T <= ncu ? T : (ncu >= kXcds ? ncu / kXcds * kXcds : ncu);
+    hipLaunchKernelGGL((k_gemm_mx8<OUT, SCALE_VEC>), dim3(grid), dim3(kThreads8), lds, stream, A,
+                       as, W, ws, g_d, M, N, K, o.D, o.d_scales, o.d_amax, o.d_gscale, tiles_m,
+                       tiles_n, vec_out);
+  } else {
+    hipLaunchKernelGGL((k_gemm<MX, OUT, SCALE_VEC, GROUPED>), dim3(tiles_m * tiles_n),
+                       dim3(kThreads), lds, stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, o.D,
+                       o.d_scales, o.d_amax, o.d_gscale, tiles_m, tiles_n, vec_out, gr.offsets,
+                       gr.ngroups);
+  }
   return hipGetLastError();
 }
 

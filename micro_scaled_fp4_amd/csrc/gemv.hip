@@ -501,10 +501,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
         const int grows = lr < nmine ? min(16, N - r0) : 0;
         const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, grows * srow, kBufferWord3);
-        // (the whole offset in the VGPR operand, so that the range check covers
-        // it: a group can reach past the scale row, and past the last row's end)
-        sga = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 16 * pp, 0, 0);
-        sgb = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 8 * srow + 16 * pp, 0, 0);
+        // (a group can reach past the scale row, and past the last row's end:
+        // such reads fail the range check and return zeros)
+        sga = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane, 16 * pp, 0);
+        sgb = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 8 * srow, 16 * pp, 0);
       }
     } else {
       const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
@@ -833,10 +833,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
       const int grows = lr < nmine ? min(16, N - r0) : 0;
       const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, grows * srow, kBufferWord3);
-      // (the whole offset in the VGPR operand, so that the range check covers it:
-      // a group can reach past the scale row, and past the last row's end)
-      sga = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 16 * pp, 0, 0);
-      sgb = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 8 * srow + 16 * pp, 0, 0);
+      // (a group can reach past the scale row, and past the last row's end:
+      // such reads fail the range check and return zeros)
+      sga = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane, 16 * pp, 0);
+      sgb = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane + 8 * srow, 16 * pp, 0);
     }
     if (++le >= Ep) { le = 0; ++lr; }
   };
@@ -1029,25 +1029,6 @@ __global__ void __launch_bounds__(256) k_zero_fill(int64_t n, T* __restrict__ y)
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) y[i] = 0;
 }
 
-// Compute units per device (0: not queried yet), cached per device so that
-// calls from several host threads, or on devices of different sizes (compute
-// partitions), each see their own device's count.
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_num_cus[kMaxDevices];
-
-int num_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  int n = g_num_cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    int cus = 0;
-    n = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0
-            ? cus : 256;
-    g_num_cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 struct StreamArgs {
   const void* x;
   const uint8_t* ws;
@@ -1143,7 +1124,7 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
                        const uint8_t* w_scales, const float* g_w, int64_t N, int64_t K, float g_d,
                        void* y, bool y_bf16, void* workspace, hipStream_t stream) {
   if (N > (1 << 30) || K > (1 << 30)) return hipErrorInvalidValue;
-  const int ncu = num_cus();
+  const int ncu = fp4impl::num_cus();
   if (K == 0) return launch_zero_fill(y, B * N, y_bf16 ? 2 : 4, stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int nstrips = (int)((N + 15) / 16);
