@@ -379,8 +379,10 @@ def main():
                                       1.0, P(yv), fp4.FP4_BF16, P(wsv), wsz, stream_of())
             assert st == 0, st
 
+        kern = ("k_gemv_fp4 (x quantized in every workgroup, W codes into the FP4 MFMA)" if B <= 4 else
+                "k_gemv_xquant + k_gemv_stream (x quantized once, W dequantized to fp16 in registers)")
         ops.append(Op(f"gemv_b{B}", gemv, nG, "GB/s", w_bytes + B * Kv * 2 + B * Nv * 2,
-                      HBM_PEAK_GBS, "hbm", "k_gemv_stream (x quantized in-kernel, W streamed)", gsrc))
+                      HBM_PEAK_GBS, "hbm", kern, gsrc))
 
     # -------------------------------------------------------- prefill GEMM --
     Mg, Ng, Kg = 8192, 28672, 8192
@@ -439,7 +441,7 @@ def main():
         Op("gemm_nvfp4", gemm_nv, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp16"], "mfma",
            "k_gemm<NV> (fp16 MFMA after exact in-register dequant)", msrc),
         Op("gemm_mxfp4", gemm_mx, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp4"], "mfma",
-           "k_gemm<MX> (scaled FP4 MFMA)", msrc),
+           "k_gemm_mx8 (scaled FP4 MFMA, 8 waves, persistent)", msrc),
         Op("gemm_nvfp4_e4m3_out", gemm_nv_e4m3, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp16"], "mfma",
            "k_gemm<NV, E4M3 out> (output requantized to FP8 E4M3 in the epilogue)", msrc),
         Op("gemm_nvfp4_nvfp4_out", gemm_nv_nv4, 3, "TFLOP/s", flops, MFMA_PEAK_TFLOPS["fp16"],
