@@ -446,45 +446,103 @@ __global__ void __launch_bounds__(kThreads, 1)
            bool vec_out, const int32_t* __restrict__ goff, int ngroups) {
   static_assert(!GROUPED || OUT != 0, "grouped launches write float32, bf16 or E4M3");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int tm, tn;
-  if constexpr (GROUPED) {
-    // the groups' tiles (the grid is an upper bound) dealt to the XCDs in
-    // contiguous ranges; the column tile runs fastest, so the workgroups of an
-    // XCD share the row tile of A in its L2
-    int t, e, lo, hi;
-    if (!xcd_tile(blockIdx.x, group_row_tiles(goff, ngroups, M) * tiles_n, t)) return;
-    if (!group_tile_of(goff, ngroups, M, t / tiles_n, e, tm, lo, hi)) return;
-    tn = t % tiles_n;
-    const int kb = MX ? 32 : 16;
-    A += (int64_t)lo * (K / 2);
-    as += (int64_t)lo * (K / kb);
-    W += (int64_t)e * N * (K / 2);
-    ws += (int64_t)e * N * (K / kb);
-    if (!MX) g_b += e;
-    D = reinterpret_cast<uint8_t*>(D) + (int64_t)lo * N * OUT;
-    M = hi - lo;
-  } else {
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  }
-  const int m0 = tm * BM, n0 = tn * BN;
+  // Plain launches are persistent: at most one workgroup per CU, workgroup w
+  // taking tiles w, w + G, ... (G a multiple of the XCD count), with the load
+  // schedule running on across tiles as in k_gemm_mx8 (the last stage of a
+  // tile loads the next tile's first two stages; the tile's output stores
+  // drain while the next tile computes; a tile's stages are padded to an even
+  // count).  Grouped launches take one tile per workgroup (their group lookup
+  // inside the tile loop would not fit the registers without spills).
+  constexpr bool kPersist = !GROUPED;
+  const int G = gridDim.x;
+  // grouped: the groups' tiles (the grid is an upper bound) dealt to the XCDs
+  // in contiguous ranges; the column tile runs fastest, so the workgroups of an
+  // XCD share the row tile of A in its L2
+  const int T = GROUPED ? group_row_tiles(goff, ngroups, M) * tiles_n : tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if (bid >= T) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int r16 = lane & 15, g = lane >> 4;
   constexpr int bs = MX ? 32 : 16;
   const int rowb = K / 2, nsc = K / bs;
 
-  __amdgpu_buffer_rsrc_t src_a, src_w, src_as, src_ws;
-  {
-    const int rows_a = min(BM, M - m0), rows_w = min(BN, N - n0);
-    src_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A) + (int64_t)m0 * rowb, 0,
-                                              rows_a * rowb, kBufferWord3);
-    src_w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W) + (int64_t)n0 * rowb, 0,
-                                              rows_w * rowb, kBufferWord3);
-    src_as = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(as) + (int64_t)m0 * nsc, 0,
-                                               rows_a * nsc, kBufferWord3);
-    src_ws = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ws) + (int64_t)n0 * nsc, 0,
-                                               rows_w * nsc, kBufferWord3);
+  // Tile b: its first row of A (a_row) and of W (w_row, group included), the
+  // rows of each that exist, its origin inside its group (m0, n0), the group's
+  // rows (m_rows) and the group (e).  Past the last tile: no rows, so loads
+  // through its empty ranges read zeros and touch no memory.
+  struct TileRows {
+    int64_t a_row, w_row;
+    int rows_a, rows_w, m0, n0, m_rows, e;
+  };
+  auto tile_rows = [&](int b) {
+    TileRows t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (b >= T) return t;
+    int tm = 0, tn = 0, lo = 0;
+    t.m_rows = M;
+    if constexpr (GROUPED) {
+      int tt, hi;
+      xcd_tile(b, T, tt);
+      if (!group_tile_of(goff, ngroups, M, tt / tiles_n, t.e, tm, lo, hi)) return t;
+      tn = tt % tiles_n;
+      t.m_rows = hi - lo;
+    } else {
+      tile_of(b, tiles_m, tiles_n, tm, tn);
+    }
+    t.m0 = tm * BM;
+    t.n0 = tn * BN;
+    t.a_row = (int64_t)lo + t.m0;
+    t.w_row = (int64_t)t.e * N + t.n0;
+    t.rows_a = min(BM, t.m_rows - t.m0);
+    t.rows_w = min(BN, N - t.n0);
+    return t;
+  };
+  auto rsrc_a = [&](const TileRows& t) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A) + t.a_row * rowb, 0,
+                                             t.rows_a * rowb, kBufferWord3);
+  };
+  auto rsrc_w = [&](const TileRows& t) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W) + t.w_row * rowb, 0,
+                                             t.rows_w * rowb, kBufferWord3);
+  };
+  auto rsrc_as = [&](const TileRows& t) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(as) + t.a_row * nsc, 0,
+                                             t.rows_a * nsc, kBufferWord3);
+  };
+  auto rsrc_ws = [&](const TileRows& t) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ws) + t.w_row * nsc, 0,
+                                             t.rows_w * nsc, kBufferWord3);
+  };
+  // A grouped workgroup's one tile is looked up once.  Plain launches carry
+  // the coordinates (tile row, tile column; -1 past the last tile) of the
+  // current and the next tile from tile to tile, and derive the rest where it
+  // is needed (few scalar registers, no division inside the loop).
+  const TileRows tile0 = tile_rows(bid);
+  auto rows_of = [&](int tm, int tn) {
+    TileRows t{0, 0, 0, 0, 0, 0, M, 0};
+    if (tm >= 0) {
+      t.m0 = tm * BM;
+      t.n0 = tn * BN;
+      t.a_row = t.m0;
+      t.w_row = t.n0;
+      t.rows_a = min(BM, M - t.m0);
+      t.rows_w = min(BN, N - t.n0);
+    }
+    return t;
+  };
+  auto coords = [&](int b, int& tm, int& tn) {
+    tm = tn = -1;
+    if (b < T) tile_of(b, tiles_m, tiles_n, tm, tn);
+  };
+  int ctm = -1, ctn = -1, xtm = -1, xtn = -1;
+  if constexpr (kPersist) {
+    coords(bid, ctm, ctn);
+    coords(bid + G, xtm, xtn);
   }
+  auto tile_at = [&](bool next) {
+    if constexpr (kPersist) return next ? rows_of(xtm, xtn) : rows_of(ctm, ctn);
+    else return next ? TileRows{0, 0, 0, 0, 0, 0, 0, 0} : tile0;
+  };
 
   v4f acc[kTN][kTM];   // [W tile][A tile]: rows n, columns m of the MFMA
 #pragma unroll
@@ -492,7 +550,17 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
     for (int j = 0; j < kTM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = (K + BK - 1) / BK;
+  const int nk = (K + BK - 1) / BK, nk2 = (nk + 1) & ~1;
+  // The loads of stage kt + 2 of the current tile: from this tile, from the
+  // next tile past the (padded) end, or nothing for a padding stage.
+  auto load_tile = [&](int kt, int& k_ld) {
+    const int kl = kt + 2;
+    const bool nx = kl >= nk2;
+    k_ld = (nx ? kl - nk2 : kl) * BK;
+    TileRows t = tile_at(nx);
+    if (!nx && kl >= nk) t.rows_a = t.rows_w = 0;
+    return t;
+  };
   // LDS layout: A scales of buffers 0, 1 | W scales 0, 1 | A tiles 0, 1 | W tiles 0, 1
   // (every access of one kind differs from the others by a 16-bit LDS offset)
   constexpr int kScA = Cfg<MX>::kScaleA, kScW = Cfg<MX>::kScaleW;
@@ -570,6 +638,39 @@ __global__ void __launch_bounds__(kThreads, 1)
   using K0 = std::integral_constant<int, 0>;
   using K1 = std::integral_constant<int, 1>;
 
+  // epilogue of tile t: lane holds D[m][n .. n+3] for each tile pair;
+  // D = acc * ((g_a * g_b) * g_d)
+  float s_glob = 1.0f;   // NVFP4 output: tensor scale of D from its given amax, as the quantizer's
+  if (OUT == 0) {
+    s_glob = nv_global_scale(*d_amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *d_gscale = s_glob;
+  }
+  auto epilogue = [&](const TileRows& t) {
+    float alpha = g_d;
+    if (!MX) alpha = ((*g_a) * g_b[t.e]) * g_d;
+    // a grouped tile writes the rows of its group, which start at row a_row - m0
+    void* Dt = reinterpret_cast<uint8_t*>(D) + (t.a_row - t.m0) * N * OUT;
+    const int mb = t.m0 + wm * 16 * kTM + r16, nb = t.n0 + wn * 16 * kTN + 4 * g;
+    if (vec_out && t.m0 + BM <= t.m_rows && t.n0 + BN <= N)
+      store_outputs<OUT, false>(acc, alpha, s_glob, mb, nb, t.m_rows, N, Dt, d_scales, true, r16, g);
+    else
+      store_outputs<OUT, true>(acc, alpha, s_glob, mb, nb, t.m_rows, N, Dt, d_scales, vec_out, r16, g);
+  };
+  // next tile: zero the accumulators (compile-time indices keep them in registers)
+  auto next_tile = [&]() {
+    if constexpr (!kPersist) return false;
+    bid += G;
+    if (bid >= T) return false;
+    ctm = xtm;
+    ctn = xtn;
+    coords(bid + G, xtm, xtn);
+    static_for<kTN>([&](auto i_c) {
+      static_for<kTM>([&](auto j_c) {
+        acc[decltype(i_c)::value][decltype(j_c)::value] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      });
+    });
+    return true;
+  };
   // Every loop body below is branch-free (a branch lets the compiler sink the
   // MFMAs past the stores and the barrier): stages past the last one are loaded
   // through the empty range (zeros into a buffer that is never read again).
@@ -580,17 +681,17 @@ __global__ void __launch_bounds__(kThreads, 1)
     // kt has finished with, and must land by the next barrier.  The operand
     // fragments of the first k-step of stage kt + 1 are read during the second
     // k-step's MFMAs of stage kt, so no MFMA waits for LDS after a barrier.
-    load_scales<MX, SCALE_VEC>(ssa, src_as, nsc, 0);
-    load_scales<MX, SCALE_VEC>(ssw, src_ws, nsc, 0);
-    dma_tile<SCALE_VEC>(src_a, tile_a(0), rowb, K, 0);
-    dma_tile<SCALE_VEC>(src_w, tile_w(0), rowb, K, 0);
+    load_scales<MX, SCALE_VEC>(ssa, rsrc_as(tile0), nsc, 0);
+    load_scales<MX, SCALE_VEC>(ssw, rsrc_ws(tile0), nsc, 0);
+    dma_tile<SCALE_VEC>(rsrc_a(tile0), tile_a(0), rowb, K, 0);
+    dma_tile<SCALE_VEC>(rsrc_w(tile0), tile_w(0), rowb, K, 0);
     store_scales<MX>(ssa, sc_a(0));
     store_scales<MX>(ssw, sc_w(0));
     const bool two = nk > 1;
-    load_scales<MX, SCALE_VEC>(ssa, two ? src_as : none, nsc, BK);
-    load_scales<MX, SCALE_VEC>(ssw, two ? src_ws : none, nsc, BK);
-    dma_tile<SCALE_VEC>(two ? src_a : none, tile_a(1), rowb, K, BK);
-    dma_tile<SCALE_VEC>(two ? src_w : none, tile_w(1), rowb, K, BK);
+    load_scales<MX, SCALE_VEC>(ssa, two ? rsrc_as(tile0) : none, nsc, BK);
+    load_scales<MX, SCALE_VEC>(ssw, two ? rsrc_ws(tile0) : none, nsc, BK);
+    dma_tile<SCALE_VEC>(two ? rsrc_a(tile0) : none, tile_a(1), rowb, K, BK);
+    dma_tile<SCALE_VEC>(two ? rsrc_w(tile0) : none, tile_w(1), rowb, K, BK);
     wait_dma();
     __syncthreads();
     uint32_t sa0[kScDw], sw0[kScDw], sa1[kScDw], sw1[kScDw];
@@ -627,17 +728,18 @@ __global__ void __launch_bounds__(kThreads, 1)
       __syncthreads();   // stage kt + 1 is in buffer nb; nobody reads buffer cb any more
       // k-step 1 of stage kt, issuing one block of each operand's stage kt + 2
       // loads per row and reading the fragments of stage kt + 1, k-step 0
-      const bool more = kt + 2 < nk;
-      const __amdgpu_buffer_rsrc_t la = more ? src_a : none, lw = more ? src_w : none;
-      load_scales<MX, SCALE_VEC>(ssa, more ? src_as : none, nsc, (kt + 2) * BK);
-      load_scales<MX, SCALE_VEC>(ssw, more ? src_ws : none, nsc, (kt + 2) * BK);
+      int k_ld;
+      const TileRows lt = load_tile(kt, k_ld);
+      const __amdgpu_buffer_rsrc_t la = rsrc_a(lt), lw = rsrc_w(lt);
+      load_scales<MX, SCALE_VEC>(ssa, rsrc_as(lt), nsc, k_ld);
+      load_scales<MX, SCALE_VEC>(ssw, rsrc_ws(lt), nsc, k_ld);
       mfma_lead();
       static_for<kTN>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
         mx_row(i_c, K1{}, fa1, fw1, sa, sw);
         if constexpr (i == 0) read_scales(nb, sa_n, sw_n);
-        dma_block<SCALE_VEC>(la, tile_a(cb), rowb, K, (kt + 2) * BK, i);
-        dma_block<SCALE_VEC>(lw, tile_w(cb), rowb, K, (kt + 2) * BK, i);
+        dma_block<SCALE_VEC>(la, tile_a(cb), rowb, K, k_ld, i);
+        dma_block<SCALE_VEC>(lw, tile_w(cb), rowb, K, k_ld, i);
         if constexpr (i < 4) {
           fa0[2 * i] = frag(tile_a(nb), ra0 + 32 * i, 2 * g);
           fa0[2 * i + 1] = frag(tile_a(nb), ra0 + 32 * i + 16, 2 * g);
@@ -653,10 +755,13 @@ __global__ void __launch_bounds__(kThreads, 1)
     // copies.  With an odd stage count the last iteration's second stage is
     // one past the end: it was loaded through the empty range (FP4 codes 0,
     // scale bytes 0) and adds exact zeros.
-    for (int kt = 0; kt < nk; kt += 2) {
-      mx_stage(std::integral_constant<int, 0>{}, kt, sa0, sw0, sa1, sw1);
-      mx_stage(std::integral_constant<int, 1>{}, kt + 1, sa1, sw1, sa0, sw0);
-    }
+    do {
+      for (int kt = 0; kt < nk2; kt += 2) {
+        mx_stage(std::integral_constant<int, 0>{}, kt, sa0, sw0, sa1, sw1);
+        mx_stage(std::integral_constant<int, 1>{}, kt + 1, sa1, sw1, sa0, sw0);
+      }
+      epilogue(tile_at(false));
+    } while (next_tile());
   } else {
     // Stage s lives in buffer s & 1.  A stage is 8 sub-steps; in sub-step u the
     // 64 MFMAs run on the fp16 operands of u while the codes of u + 1 are
@@ -666,17 +771,17 @@ __global__ void __launch_bounds__(kThreads, 1)
     // then issue the loads of stage kt + 2 (into this stage's buffer) and read
     // and dequantize the first codes of stage kt + 1, so no MFMA waits at a
     // stage boundary.
-    load_scales<MX, SCALE_VEC>(ssa, src_as, nsc, 0);
-    load_scales<MX, SCALE_VEC>(ssw, src_ws, nsc, 0);
-    dma_tile<SCALE_VEC>(src_a, tile_a(0), rowb, K, 0);
-    dma_tile<SCALE_VEC>(src_w, tile_w(0), rowb, K, 0);
+    load_scales<MX, SCALE_VEC>(ssa, rsrc_as(tile0), nsc, 0);
+    load_scales<MX, SCALE_VEC>(ssw, rsrc_ws(tile0), nsc, 0);
+    dma_tile<SCALE_VEC>(rsrc_a(tile0), tile_a(0), rowb, K, 0);
+    dma_tile<SCALE_VEC>(rsrc_w(tile0), tile_w(0), rowb, K, 0);
     store_scales<MX>(ssa, sc_a(0));
     store_scales<MX>(ssw, sc_w(0));
     const bool two = nk > 1;
-    load_scales<MX, SCALE_VEC>(ssa, two ? src_as : none, nsc, BK);
-    load_scales<MX, SCALE_VEC>(ssw, two ? src_ws : none, nsc, BK);
-    dma_tile<SCALE_VEC>(two ? src_a : none, tile_a(1), rowb, K, BK);
-    dma_tile<SCALE_VEC>(two ? src_w : none, tile_w(1), rowb, K, BK);
+    load_scales<MX, SCALE_VEC>(ssa, two ? rsrc_as(tile0) : none, nsc, BK);
+    load_scales<MX, SCALE_VEC>(ssw, two ? rsrc_ws(tile0) : none, nsc, BK);
+    dma_tile<SCALE_VEC>(two ? rsrc_a(tile0) : none, tile_a(1), rowb, K, BK);
+    dma_tile<SCALE_VEC>(two ? rsrc_w(tile0) : none, tile_w(1), rowb, K, BK);
     wait_dma();
     __syncthreads();
     uint32_t sa0[kScDw], sw0[kScDw], sa1[kScDw], sw1[kScDw];
@@ -711,8 +816,9 @@ __global__ void __launch_bounds__(kThreads, 1)
     auto nv_stage = [&](auto cb_c, int kt, const uint32_t (&sa)[kScDw], const uint32_t (&sw)[kScDw],
                         uint32_t (&sa_n)[kScDw], uint32_t (&sw_n)[kScDw]) {
       constexpr int cb = decltype(cb_c)::value, nb = cb ^ 1;
-      const bool more = kt + 2 < nk;
-      const __amdgpu_buffer_rsrc_t la = more ? src_a : none, lw = more ? src_w : none;
+      int k_ld;
+      const TileRows lt = load_tile(kt, k_ld);
+      const __amdgpu_buffer_rsrc_t la = rsrc_a(lt), lw = rsrc_w(lt);
       static_for<8>([&](auto u_c) {
         constexpr int u = decltype(u_c)::value;
         constexpr int p = u & 1, q = p ^ 1;
@@ -724,8 +830,8 @@ __global__ void __launch_bounds__(kThreads, 1)
           store_scales<MX>(ssw, sc_w(nb));
           wait_dma();        // stage kt + 1 (issued during the previous stage) has landed
           __syncthreads();   // stage kt + 1 is in buffer nb; buffer cb is free
-          load_scales<MX, SCALE_VEC>(ssa, more ? src_as : none, nsc, (kt + 2) * BK);
-          load_scales<MX, SCALE_VEC>(ssw, more ? src_ws : none, nsc, (kt + 2) * BK);
+          load_scales<MX, SCALE_VEC>(ssa, rsrc_as(lt), nsc, k_ld);
+          load_scales<MX, SCALE_VEC>(ssw, rsrc_ws(lt), nsc, k_ld);
           read_scales(nb, sa_n, sw_n);
         }
         mfma_lead();
@@ -756,8 +862,8 @@ __global__ void __launch_bounds__(kThreads, 1)
               pw[0][2 * i - 8] = scale_pair(sw_n[2 * i - 8], 0);
               pw[0][2 * i - 7] = scale_pair(sw_n[2 * i - 7], 0);
             }
-            if constexpr (u == 6 && j == 2) dma_block<SCALE_VEC>(la, tile_a(cb), rowb, K, (kt + 2) * BK, i);
-            if constexpr (u == 6 && j == 6) dma_block<SCALE_VEC>(lw, tile_w(cb), rowb, K, (kt + 2) * BK, i);
+            if constexpr (u == 6 && j == 2) dma_block<SCALE_VEC>(la, tile_a(cb), rowb, K, k_ld, i);
+            if constexpr (u == 6 && j == 6) dma_block<SCALE_VEC>(lw, tile_w(cb), rowb, K, k_ld, i);
             __builtin_amdgcn_sched_barrier(0);
           });
         });
@@ -768,26 +874,14 @@ __global__ void __launch_bounds__(kThreads, 1)
     // two stages per iteration (scale registers alternate); an odd stage count
     // runs one stage past the end, loaded through the empty range (codes 0,
     // scale bytes 0: exact zeros)
-    for (int kt = 0; kt < nk; kt += 2) {
-      nv_stage(std::integral_constant<int, 0>{}, kt, sa0, sw0, sa1, sw1);
-      nv_stage(std::integral_constant<int, 1>{}, kt + 1, sa1, sw1, sa0, sw0);
-    }
+    do {
+      for (int kt = 0; kt < nk2; kt += 2) {
+        nv_stage(std::integral_constant<int, 0>{}, kt, sa0, sw0, sa1, sw1);
+        nv_stage(std::integral_constant<int, 1>{}, kt + 1, sa1, sw1, sa0, sw0);
+      }
+      epilogue(tile_at(false));
+    } while (next_tile());
   }
-
-  // epilogue: lane holds D[m][n .. n+3] for each tile pair; D = acc * ((g_a * g_b) * g_d)
-  float alpha = g_d;
-  if (!MX) alpha = ((*g_a) * (*g_b)) * g_d;
-  // NVFP4 output: tensor scale of D from its given amax, as the quantizer's
-  float s_glob = 1.0f;
-  if (OUT == 0) {
-    s_glob = nv_global_scale(*d_amax);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *d_gscale = s_glob;
-  }
-  const int mb = m0 + wm * 16 * kTM + r16, nb = n0 + wn * 16 * kTN + 4 * g;
-  if (vec_out && m0 + BM <= M && n0 + BN <= N)
-    store_outputs<OUT, false>(acc, alpha, s_glob, mb, nb, M, N, D, d_scales, true, r16, g);
-  else
-    store_outputs<OUT, true>(acc, alpha, s_glob, mb, nb, M, N, D, d_scales, vec_out, r16, g);
 }
 
 // ------------------------------------------------ MXFP4 kernel, 8 waves --
@@ -1106,16 +1200,17 @@ hipError_t launch_t(const uint8_t* A, const uint8_t* as, const uint8_t* W, const
   // (NVFP4: 4 outputs are 2 bytes)
   const bool vec_out =
       N % 4 == 0 && reinterpret_cast<uintptr_t>(o.D) % (OUT == 0 ? 2 : 4 * OUT) == 0;
+  // persistent kernels: at most one workgroup per CU, a multiple of the XCD
+  // count when there are more tiles than CUs (grouped: tiles_m * tiles_n is an
+  // upper bound on the tiles)
+  const int T = tiles_m * tiles_n, ncu = fp4impl::num_cus();
+  const int grid = GROUPED || T <= ncu ? T : (ncu >= kXcds ? ncu / kXcds * kXcds : ncu);
   if constexpr (kMx8) {
-    // persistent: at most one workgroup per CU, a multiple of the XCD count
-    // when there are more tiles than CUs
-    const int T = tiles_m * tiles_n, ncu = fp4impl::num_cus();
-    const int grid = T <= ncu ? T : (ncu >= kXcds ? ncu / kXcds * kXcds : ncu);
     hipLaunchKernelGGL((k_gemm_mx8<OUT, SCALE_VEC>), dim3(grid), dim3(kThreads8), lds, stream, A,
                        as, W, ws, g_d, M, N, K, o.D, o.d_scales, o.d_amax, o.d_gscale, tiles_m,
                        tiles_n, vec_out);
   } else {
-    hipLaunchKernelGGL((k_gemm<MX, OUT, SCALE_VEC, GROUPED>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((k_gemm<MX, OUT, SCALE_VEC, GROUPED>), dim3(grid),
                        dim3(kThreads), lds, stream, A, as, W, ws, g_a, g_b, g_d, M, N, K, o.D,
                        o.d_scales, o.d_amax, o.d_gscale, tiles_m, tiles_n, vec_out, gr.offsets,
                        gr.ngroups);
