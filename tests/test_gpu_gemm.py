@@ -109,6 +109,32 @@ def test_gemm_small_shapes(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["nv", "mx"])
+@pytest.mark.parametrize("K", [1280, 1056])
+def test_gemm_workgroups_take_several_tiles(fmt, K):
+    """More 256 x 256 tiles than compute units (2300 x 7700: 9 x 31 = 279), so
+    workgroups go on to further tiles, the load schedule running on from one
+    tile into the next; ragged M and N edges; an odd number of 256-value
+    stages (K = 1280: 5, so every tile ends on a padding stage; K = 1056: a
+    32-value tail).  Every float32 output against the oracle; the bf16 output
+    is the float32 result rounded to bf16; E4M3 and NVFP4 outputs (other
+    epilogues between tiles) against the oracle's encoding of that result."""
+    M, N = 2300, 7700
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 9 * 31 > ncu, "the shape is meant to give some workgroups a second tile"
+    announce(f"gemm several tiles per workgroup {fmt} {M}x{N}x{K}")
+    ops = _operands(fmt, M, N, K, 120 + K)
+    D32 = _gpu_gemm(fmt, ops, K, 1.0, torch.float32)
+    d32 = D32.cpu().numpy()
+    _check(d32, fmt, ops, K, 1.0, False)
+    Db = _gpu_gemm(fmt, ops, K, 1.0, torch.bfloat16)
+    assert np.array_equal(Db.cpu().view(torch.int16).numpy().view(np.uint16), o.f32_to_bf16_bits(d32))
+    D8 = _gpu_gemm(fmt, ops, K, 1.0, torch.float8_e4m3fn)
+    assert np.array_equal(D8.view(torch.uint8).cpu().numpy(), o.gemm_e4m3_output(d32))
+    amax = float(np.max(np.abs(d32)))
+    _check_nv_out(_gpu_gemm_nv_out(fmt, ops, K, 1.0, amax), d32, amax, what=f"{fmt} K={K}")
+
+
+@pytest.mark.parametrize("fmt", ["nv", "mx"])
 def test_gemm_empty_k_writes_zeros(fmt):
     """K = 0: D is the empty sum, exactly 0; M = 0 or N = 0 writes nothing."""
     announce(f"gemm K=0 {fmt}")
