@@ -40,10 +40,13 @@ def test_gemv_small_matches_oracle(B, N, K):
     _run_and_check(o.bf16_bits_to_f32(x), False, Wq, Ws, float(g_w), N, K, 2.0, torch.float32)
 
 
-@pytest.mark.parametrize("B,N,K", [(16, 64, 20480), (2, 100, 32768), (12, 70, 5120), (9, 33, 4096)])
+@pytest.mark.parametrize("B,N,K", [(16, 64, 20480), (2, 100, 32768), (12, 70, 5120), (9, 33, 4096),
+                                   (16, 33, 1 << 20)])
 def test_gemv_long_k_and_wide_batch(B, N, K):
     """Shapes that take the other kernel paths: x kept in LDS as codes + scales
-    (wide batch or long K) and the split-K path for K too long for LDS."""
+    (wide batch or long K) and the split-K path for K too long for LDS, up to
+    K = 2^20 at B = 16 (x's global amax computed once, by the amax pass, and
+    read by the prep launch)."""
     announce(f"gemv path B={B} N={N} K={K}")
     Wq = workloads.random_codes((N, K // 2), seed=K + 1)
     Ws = workloads.random_bytes((N, K // 16), 0x18, 0x58, seed=K + 2)
@@ -57,8 +60,8 @@ def test_gemv_long_k_and_wide_batch(B, N, K):
 def test_gemv_several_rounds(B, N, K):
     """More 16-row strips than one pass of the workgroups takes (2048 per round
     on 256 CUs), so strips come in rounds; covers the per-round exchange of the
-    two K halves, per-pair scale loads (K = 1056) and per-round scale blocks
-    with exactly as many pairs per half as the prefetch depth (K = 2048)."""
+    two K halves, per-pair scale loads (K = 1056) and scale groups that reach
+    past a K half (K = 2048: 4 pairs per half, groups of 8)."""
     announce(f"gemv rounds B={B} N={N} K={K}")
     Wq = workloads.random_codes((N, K // 2), seed=N + 1)
     Ws = workloads.random_bytes((N, K // 16), 0x18, 0x58, seed=N + 2)
