@@ -20,7 +20,10 @@
 // v_mfma_f32_16x16x32_f16 accumulates in float32.  Ceiling: the fp16 MFMA rate.
 //
 // Tiling: BM x BN (256 x 256) output tile per workgroup, 2 x 2 waves, each with
-// its own 8 x 8 block of 16x16 MFMA tiles (accumulators in AGPRs).  K advances 256 values
+// its own 8 x 8 block of 16x16 MFMA tiles (accumulators in AGPRs); the plain
+// MXFP4 launch runs 2 x 4 waves of 8 x 4 tiles instead (k_gemm_mx8, below).
+// Plain launches are persistent (one workgroup per CU walks several tiles, its
+// loads running on from one tile into the next).  K advances 256 values
 // (128 bytes per row) per stage in two k-steps of 128; stages are
 // double-buffered in LDS and filled by buffer loads that write LDS directly
 // (no register staging, no LDS store instructions), one barrier per stage.
@@ -40,7 +43,8 @@
 // Workgroup -> tile map: workgroups are dealt round-robin to the 8 XCDs, so
 // each XCD is given a contiguous range of tiles; tiles are visited in groups
 // of 8 row-tiles so concurrently running workgroups of an XCD share operand
-// rows in its L2.
+// rows in its L2.  A persistent workgroup w takes tiles w, w + G, ... with G a
+// multiple of 8, so it stays on one XCD and the ranges hold.
 #include <atomic>
 #include <type_traits>
 #include <utility>
@@ -99,7 +103,7 @@ __device__ __forceinline__ bool xcd_tile(int bid, int T, int& t) {
 
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   int t;
-  xcd_tile(bid, tiles_m * tiles_n, t);   // the grid is exactly the tile count
+  xcd_tile(bid, tiles_m * tiles_n, t);   // callers pass bid < tiles_m * tiles_n
   const int in_group = kGroupM * tiles_n;
   const int group = t / in_group;
   const int first_m = group * kGroupM;
