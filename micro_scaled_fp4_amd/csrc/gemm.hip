@@ -211,8 +211,9 @@ __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\
 
 // Wait until this wave's buffer loads, including those that write LDS
 // directly, have completed (vmcnt(0); the lgkm and exp counters are left
-// alone).  The compiler does not count direct-to-LDS loads as LDS writes, so
-// each barrier that publishes such loads to the workgroup is preceded by this.
+// alone).  The compiler orders a wave's direct-to-LDS loads only before that
+// wave's own later LDS reads, never before another wave's, so each barrier
+// that publishes such loads to the workgroup is preceded by this.
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // lgkmcnt(0): LDS and scalar-memory operations of this wave have completed
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
