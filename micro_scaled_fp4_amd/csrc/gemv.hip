@@ -10,14 +10,20 @@
 // significant bits, magnitudes in [2^-10, 2688]), so their products are exact
 // and only the float32 accumulation rounds.
 //
-// Launch 1 (k_gemv_xquant): x -> NVFP4 once, exactly as nvfp4_quantize does,
-//   into the workspace: as exact fp16 x' rows (when the streaming kernel keeps
-//   x' in LDS, or for the long-K kernel) or as codes + scale bytes (wider
-//   batches), zero past K.  Small x: every prep workgroup reduces all of x for
-//   the global amax itself; larger x: a first launch writes per-workgroup
+// Kernels by shape (launch_gemv):
+//   B <= 4: k_gemv_fp4, one launch (every workgroup quantizes the small x).
+//   5 <= B <= 16, K a multiple of 256 up to 5120: k_gemv_xquant, then
+//     k_gemv_xreg (x' in registers).
+//   otherwise while x fits LDS: k_gemv_stream (x quantized in every workgroup
+//     when fp16 x' fits, else by k_gemv_xquant first).
+//   longer K: k_gemv_xquant, then k_gemv_mfma.
+// k_gemv_xquant: x -> NVFP4 once, exactly as nvfp4_quantize does, into the
+//   workspace: as exact fp16 x' rows (for the long-K kernel) or as codes +
+//   scale bytes, zero past K.  Small x: every prep workgroup reduces all of x
+//   for the global amax itself; larger x: a first launch writes per-workgroup
 //   partial maxima (the quantizer's amax pass) and the prep reduces those.
-// Launch 2, the streaming kernel (k_gemv_stream; below): one workgroup per CU
-//   copies x from the workspace into LDS and streams W past it.
+// The streaming kernels (k_gemv_stream, k_gemv_fp4, k_gemv_xreg; below) run
+//   one workgroup per CU, persistent over 16-row strips of W.
 // Long K (x not fitting LDS): k_gemv_mfma, W streaming on
 //   v_mfma_f32_16x16x32_f16.  The batch
 //   rows are the MFMA's M side (rows >= B are zero), 16 W rows its N side, so
@@ -44,14 +50,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-constexpr int kPrepThreads = 1024;
+constexpr int kPrepThreads = 512;
 // Workspace: [0, 4 KiB) partial maxima of x (larger x) | [4 KiB, +256) header,
 // s_global of x | from kWsData: x quantized by the prep launch.
 constexpr size_t kWsPartials = 0;
 constexpr size_t kWsHeader = 4096;
 constexpr size_t kWsData = 4096 + 256;
 // x of at most this many values: each prep workgroup reduces all of it for the
-// amax (at most 8 workgroups, each reading at most 512 KB)
+// amax (at most 16 workgroups, each reading at most 512 KB)
 constexpr int64_t kSmallX = (int64_t)1 << 17;
 constexpr int kMaxWaves = 16;
 constexpr int kMaxSteps = 3;           // 128-value steps per wave kept in registers
@@ -70,7 +76,7 @@ __global__ void __launch_bounds__(kPrepThreads)
     k_gemv_xquant(const void* __restrict__ x, int64_t B, int64_t K, int64_t Kpad,
                   const uint32_t* __restrict__ partials, int npart, uint8_t* __restrict__ ws) {
   __shared__ uint32_t red[kPrepThreads / 64];
-  constexpr int kUnroll = 12;   // 16-byte vectors in flight per thread in the amax loop
+  constexpr int kUnroll = 20;   // 16-byte vectors in flight per thread in the amax loop
   const int64_t bpr = Kpad / 16;
   const int64_t blk = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
   const int64_t row = blk / bpr, c0 = (blk - row * bpr) * 16;
@@ -377,6 +383,7 @@ constexpr int kGroupPairs = 8;                   // pairs per W scale group
 constexpr int kGroupLds = 16 * kGroupPairs * 16; // a scale group in LDS: [pair][16 rows] x 16 bytes
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer descriptor word 3 (gfx9 family)
 constexpr int kLoadNT = 2;                      // buffer load cache policy: nontemporal
+constexpr int kBufferFar = 0x7ffffff0;          // a buffer offset past every range: reads 0
 
 // XSRC: where x comes from -- kXFromWs: the prep launch's quantized x in the
 // workspace; kXBf16 / kXF32: x itself, quantized here by every workgroup.
@@ -739,7 +746,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
 // block dot product per output.  Lane (g, n) of the MFMA output holds
 // D[4g + j][n], j = 0..3: W row n against x blocks 4 (g % 2) + j of batch row
 // 2t + g / 2; it applies the two E4M3 block scales, acc += (s_x s_w) D, the
-// product exact (at most 8 + 12 significant bits), one rounding per block; W's
+// product exact (at most 8 + 12 significant bits), one rounding per block (so
+// a fused multiply-add gives the same sum in one instruction); W's
 // four scale bytes for those blocks are contiguous.  Rounds, strips, the split
 // of K between two waves and the exchange of partial sums are those of
 // k_gemv_stream; every workgroup quantizes the small x itself.
@@ -1001,10 +1009,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
           const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               xo, wo, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, 127, 0, 127);
           const f32x4 sx = *reinterpret_cast<const f32x4*>(sx_lane + 2 * t * bpr + 8 * (step + st));
-          acc[t] = acc[t] + (sx.x * w01.x) * d.x;
-          acc[t] = acc[t] + (sx.y * w01.y) * d.y;
-          acc[t] = acc[t] + (sx.z * w23.x) * d.z;
-          acc[t] = acc[t] + (sx.w * w23.y) * d.w;
+          acc[t] = __builtin_fmaf(sx.x * w01.x, d.x, acc[t]);
+          acc[t] = __builtin_fmaf(sx.y * w01.y, d.y, acc[t]);
+          acc[t] = __builtin_fmaf(sx.z * w23.x, d.z, acc[t]);
+          acc[t] = __builtin_fmaf(sx.w * w23.y, d.w, acc[t]);
         }
       }
     }
@@ -1021,6 +1029,213 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
   }
   // every wave takes part in all R rounds' exchanges (see k_gemv_stream)
   for (int r = Ep > 0 ? nmine : 0; r < R; ++r) finish(r, r < nmine);
+}
+
+// ------------------------------------------ GEMV with x' in registers --
+// Wider batches (5 to 16 rows) with K a multiple of 256 up to 5120: x,
+// quantized once by the prep launch (codes + scale bytes), is copied into LDS
+// and each wave dequantizes its share of it once, into registers, instead of
+// once per strip (fp16 x' of 16 rows x 5120 values would need all of LDS).
+// A workgroup of 8 waves (two per SIMD, 256 registers each) serves two strips
+// at a time; the four waves of a strip take a quarter of K each and hold its
+// exact fp16 x' (at most 5 pairs of 128-value steps: 160 registers) for the
+// whole kernel.  W streams as in k_gemv_stream (8 rows x 128 bytes per load,
+// through a wave-private transpose tile; W scale bytes of the wave's pairs of
+// a strip with two loads of 8 rows x 16 bytes per pair), with a ring of one
+// round (the wave's pairs of its next strip) in flight.  Per round, the three
+// upper quarters' partial tiles go through LDS (double-buffered by round
+// parity, one barrier per round) to the lowest quarter's wave, which adds them
+// in a fixed order and writes y.  K order inside a pair and the MFMA use are
+// those of k_gemv_stream.
+constexpr int kXrThreads = 512;
+constexpr int kXrWaves = kXrThreads / 64;
+constexpr int kXrSplit = 4;                      // waves per strip (K parts)
+constexpr int kXrSlots = kXrWaves / kXrSplit;    // strips per workgroup and round
+constexpr int kXrMaxPairs = 5;                   // pairs of x' per wave (K <= 5120)
+constexpr int kXrChunks = 6;                     // 16-byte x chunks per thread (16 rows, K <= 5120)
+
+// LDS for x of B rows of Kq values: codes [B][Kq / 2 + 16] then scale bytes
+// [B][Kq / 16] (a multiple of 16 bytes); 16 spare bytes follow
+__host__ __device__ inline int xreg_lds_bytes(int B, int Kq) { return B * (Kq / 2 + 16) + B * (Kq / 16); }
+
+// y is written through a buffer descriptor with 32-bit offsets (the host
+// keeps B * N * sizeof(y) below 2^31).
+template <bool YBF16>
+__global__ void __launch_bounds__(kXrThreads, 1)
+    k_gemv_xreg(const uint8_t* __restrict__ ws, int B, const uint8_t* __restrict__ W,
+                const uint8_t* __restrict__ w_scales, const float* __restrict__ g_w, int N, int K,
+                int Kq, float g_d, void* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kXrWaves][2048];
+  __shared__ __attribute__((aligned(16))) uint8_t sgroup[kXrWaves][kGroupLds];
+  __shared__ v4f red[2][kXrSlots][kXrSplit - 1][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = lane & 15, g = lane >> 4;
+  const int r8 = lane >> 3, c8 = lane & 7;
+  const int nstrips = (N + 15) / 16;
+  const int wrow = K / 2, srow = K / 16;
+  const int part = wave / kXrSlots, slot = wave - part * kXrSlots;
+  const int Pq = Kq / 256;
+  const int Ph = (Pq + kXrSplit - 1) / kXrSplit;  // <= kXrMaxPairs (host check)
+  const int pbeg = min(part * Ph, Pq), pend = min(pbeg + Ph, Pq);
+  const int E = pend - pbeg;                       // this wave's pairs
+  const int G = gridDim.x * kXrSlots;              // strips per round
+  const int s_first = slot * gridDim.x + blockIdx.x;
+  const int R = (nstrips + G - 1) / G;             // rounds (the same in every workgroup)
+  const int nmine = s_first < nstrips ? (nstrips - s_first + G - 1) / G : 0;
+  uint8_t* tb = tiles[wave];
+  uint8_t* sa = sgroup[wave];
+
+  // ---- x from the workspace (codes [B][Kq/2], then scale bytes [B][Kq/16]) in
+  // 16-byte chunks, into registers first: these loads are issued before W's
+  // so that waiting for them does not wait for W (loads complete in order)
+  const int xc_row = Kq / 2 + 16, bpr = Kq / 16;
+  const int row_chunks = Kq / 32;
+  const int nchunk = B * row_chunks + B * bpr / 16;
+  const u32x4* xsrc = reinterpret_cast<const u32x4*>(ws + kWsData);
+  u32x4 xch[kXrChunks];
+#pragma unroll
+  for (int i = 0; i < kXrChunks; ++i) {
+    const int c = threadIdx.x + i * kXrThreads;
+    xch[i] = xsrc[c < nchunk ? c : 0];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- W ring: slot e holds pair pbeg + e of the strip of round r.  Reads of
+  // rounds without a strip and of pairs past E go through an empty range
+  // (zeros, no memory touched).
+  u32x4 ra[kXrMaxPairs], rb[kXrMaxPairs];
+  u32x4 sga, sgb;                                  // scale bytes of a round's pairs in flight
+  const int w_lane = r8 * wrow + 16 * c8;
+  // scale loads: lane (r8, c8) takes the 16 bytes of pair pbeg + c8 of rows r8
+  // and 8 + r8 (pairs past E: offset out of every range)
+  const int g_lane = c8 < E ? r8 * srow + 16 * c8 : kBufferFar;
+  const int g_lane8 = c8 < E ? (8 + r8) * srow + 16 * c8 : kBufferFar;
+  auto strip_rows = [&](int r) {
+    const int r0 = r < nmine ? (s_first + r * G) * 16 : 0;
+    return r < nmine ? min(16, N - r0) : 0;
+  };
+  auto strip_row0 = [&](int r) { return r < nmine ? (s_first + r * G) * 16 : 0; };
+  auto load_pair = [&](int r, int e) {
+    const int r0 = strip_row0(r);
+    const int rows = e < E ? strip_rows(r) : 0;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W) + (int64_t)r0 * wrow, 0, rows * wrow, kBufferWord3);
+    ra[e] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, 128 * (pbeg + e), kLoadNT);
+    rb[e] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + 8 * wrow, 128 * (pbeg + e), kLoadNT);
+  };
+  auto load_scales = [&](int r) {
+    const int r0 = strip_row0(r);
+    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(w_scales) + (int64_t)r0 * srow, 0, strip_rows(r) * srow, kBufferWord3);
+    sga = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane, 16 * pbeg, 0);
+    sgb = __builtin_amdgcn_raw_buffer_load_b128(rsc, g_lane8, 16 * pbeg, 0);
+  };
+  // issue order: the scale bytes, then the pairs in order, as inside the loop,
+  // so that the loop's waits count only the loads it needs (loads complete in
+  // order)
+  __builtin_amdgcn_sched_barrier(0);
+  load_scales(0);
+#pragma unroll
+  for (int e = 0; e < kXrMaxPairs; ++e) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair(0, e);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- x into LDS, then this wave's x' into registers: lane (b, g) holds
+  // x'[b][256 p + 64 g + 32 st + 8 s4, +8) (batch rows >= B: row B - 1, any
+  // finite x, never stored)
+  // (every thread stores every chunk, those past nchunk into a spare 16 bytes
+  // after x: a store under a branch would let the compiler move its load
+  // there, behind W's)
+#pragma unroll
+  for (int i = 0; i < kXrChunks; ++i) {
+    const int c = threadIdx.x + i * kXrThreads;
+    const int row = c / row_chunks;
+    const int off = c >= nchunk ? xreg_lds_bytes(B, Kq)
+                    : c < B * row_chunks ? row * xc_row + 16 * (c - row * row_chunks)
+                                         : B * xc_row + 16 * (c - B * row_chunks);
+    *reinterpret_cast<u32x4*>(xlds + off) = xch[i];
+  }
+  __syncthreads();
+  const int xrow = min(b, B - 1);
+  v8h xr[kXrMaxPairs][2][4];
+#pragma unroll
+  for (int e = 0; e < kXrMaxPairs; ++e) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // (registers past E are never used: any pair inside x)
+      const int v0 = 256 * min(pbeg + min(e, max(E - 1, 0)), Pq - 1) + 64 * g + 32 * st;
+      const u32x4 xc = *reinterpret_cast<const u32x4*>(xlds + xrow * xc_row + v0 / 2);
+      const uint32_t xsb = *reinterpret_cast<const uint16_t*>(xlds + B * xc_row + xrow * bpr + v0 / 16);
+      const v2h hp = e4m3_pair_h<false>(xsb);
+      const v2h h0 = v2h{hp.x, hp.x}, h1 = v2h{hp.y, hp.y};
+      xr[e][st][0] = dq8(xc.x, h0);
+      xr[e][st][1] = dq8(xc.y, h0);
+      xr[e][st][2] = dq8(xc.z, h1);
+      xr[e][st][3] = dq8(xc.w, h1);
+    }
+  }
+
+  const float gscale = *reinterpret_cast<const float*>(ws + kWsHeader) * (*g_w);
+  const __amdgpu_buffer_rsrc_t ry =
+      __builtin_amdgcn_make_buffer_rsrc(y, 0, B * N * (YBF16 ? 2 : 4), kBufferWord3);
+  const int wsw = (r8 ^ c8) << 4;
+  for (int r = 0; r < R; ++r) {
+    const bool mine = r < nmine;
+    v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+#pragma unroll
+    for (int e = 0; e < kXrMaxPairs; ++e) {
+      if (e == 0) {   // [pair q][row] x 16 bytes
+        *reinterpret_cast<u32x4*>(sa + (16 * c8 + r8) * 16) = sga;
+        *reinterpret_cast<u32x4*>(sa + (16 * c8 + 8 + r8) * 16) = sgb;
+        load_scales(r + 1);
+      }
+      *reinterpret_cast<u32x4*>(tb + r8 * 128 + wsw) = ra[e];
+      *reinterpret_cast<u32x4*>(tb + (8 + r8) * 128 + (wsw ^ 64)) = rb[e];
+      load_pair(r + 1, e);
+      if (mine && e < E) {
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(sa + (16 * e + b) * 16 + 4 * g);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int c = 2 * g + st;
+          const u32x4 codes = *reinterpret_cast<const u32x4*>(
+              tb + b * 128 + ((c ^ (b & 7) ^ ((b >> 3) << 2)) << 4));
+          const v2h wp = st ? e4m3_pair_h<true>(sw) : e4m3_pair_h<false>(sw);
+          const v2h w0 = v2h{wp.x, wp.x}, w1 = v2h{wp.y, wp.y};
+          v4f& acc = st ? acc1 : acc0;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xr[e][st][0], dq8(codes.x, w0), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xr[e][st][1], dq8(codes.y, w0), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xr[e][st][2], dq8(codes.z, w1), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xr[e][st][3], dq8(codes.w, w1), acc, 0, 0, 0);
+        }
+      }
+    }
+    // the upper quarters' partial tiles to the lowest quarter's wave (every
+    // wave takes part in every round's barrier)
+    v4f a = acc0 + acc1;
+    if (part != 0) red[r & 1][slot][part - 1][lane] = a;
+    __syncthreads();
+    if (part == 0 && mine) {
+#pragma unroll
+      for (int p = 0; p < kXrSplit - 1; ++p) a += red[r & 1][slot][p][lane];
+      const int n0 = (s_first + r * G) * 16;     // D[4g + q][b] of this strip
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ob = 4 * g + q;
+        if (ob < B && n0 + b < N) {
+          const float v = (a[q] * gscale) * g_d;
+          if (YBF16)
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16(v), ry,
+                                                  2 * (ob * N + b), 2 * n0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, 4 * (ob * N + b), 4 * n0, 0);
+        }
+      }
+    }
+  }
 }
 
 // K = 0: every output is an empty sum.
@@ -1065,6 +1280,22 @@ hipError_t launch_stream(const StreamArgs& a, int grid, int lds, hipStream_t str
   hipLaunchKernelGGL((k_gemv_stream<XS, XF, SCM>), dim3(grid), dim3(kStreamThreads), lds, stream,
                      a.x, a.ws, a.B, a.W, a.w_scales, a.g_w, a.N, a.K, a.Kq, a.lds_x, a.g_d, a.y,
                      a.y_bf16);
+  return hipGetLastError();
+}
+
+template <bool YB>
+hipError_t launch_xreg(const uint8_t* ws, int64_t B, const uint8_t* W, const uint8_t* w_scales,
+                       const float* g_w, int64_t N, int64_t K, int64_t Kq, float g_d, void* y,
+                       int grid, int lds_x, hipStream_t stream) {
+  // the most dynamic LDS any call uses (16 rows, K = 5120), set once per device
+  static std::atomic<uint64_t> lds_set{0};
+  const int lds_max = xreg_lds_bytes(16, 256 * kXrSplit * kXrMaxPairs) + 16;
+  const hipError_t e = fp4impl::set_lds_limit_once(
+      lds_set, reinterpret_cast<const void*>(&k_gemv_xreg<YB>), lds_max);
+  if (e != hipSuccess) return e;
+  if (lds_x > lds_max) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gemv_xreg<YB>, dim3(grid), dim3(kXrThreads), lds_x, stream, ws, (int)B, W,
+                     w_scales, g_w, (int)N, (int)K, (int)Kq, g_d, y);
   return hipGetLastError();
 }
 
@@ -1140,6 +1371,20 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   const bool xf16 = lds_f16 + lds_fixed <= lds_max;
   // (the strip-relative buffer offsets need 16 rows of W to span < 2^31 bytes;
   // the x' sizes above already keep K far below that)
+  // 5 to 16 batch rows, K a multiple of 256 up to 5120, 16-aligned scale rows:
+  // x quantized once, then x' held in registers; the grid is cut so that every
+  // workgroup serves the same number of rounds
+  if (B > 4 && B <= 16 && K % 256 == 0 && Kq / 256 <= kXrSplit * kXrMaxPairs &&
+      reinterpret_cast<uintptr_t>(w_scales) % 16 == 0 && B * N * 4 < ((int64_t)1 << 31)) {
+    const int lds_x = xreg_lds_bytes((int)B, (int)Kq) + 16;
+    hipError_t e = launch_xquant(x, x_bf16, B, K, Kq, false, ws, stream);
+    if (e != hipSuccess) return e;
+    const int per_round = ncu * kXrSlots;
+    const int rounds = (nstrips + per_round - 1) / per_round;
+    const int grid = (nstrips + kXrSlots * rounds - 1) / (kXrSlots * rounds);
+    return y_bf16 ? launch_xreg<true>(ws, B, W, w_scales, g_w, N, K, Kq, g_d, y, grid, lds_x, stream)
+                  : launch_xreg<false>(ws, B, W, w_scales, g_w, N, K, Kq, g_d, y, grid, lds_x, stream);
+  }
   // narrow batches (K a multiple of 64, 4-aligned scale rows): the FP4-MFMA kernel
   if (B <= 4 && K % 64 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 4 == 0 && K < (1 << 27)) {
     const int nmf = (int)((B + 1) / 2);
