@@ -380,7 +380,8 @@ def main():
             assert st == 0, st
 
         kern = ("k_gemv_fp4 (x quantized in every workgroup, W codes into the FP4 MFMA)" if B <= 4 else
-                "k_gemv_xquant + k_gemv_stream (x quantized once, W dequantized to fp16 in registers)")
+                "k_gemv_xquant + k_gemv_xreg (x quantized once and dequantized once per wave into "
+                "registers, W dequantized to fp16 in registers)")
         ops.append(Op(f"gemv_b{B}", gemv, nG, "GB/s", w_bytes + B * Kv * 2 + B * Nv * 2,
                       HBM_PEAK_GBS, "hbm", kern, gsrc))
 
