@@ -12,10 +12,10 @@
 //
 // Kernels by shape (launch_gemv):
 //   B <= 4: k_gemv_fp4, one launch (every workgroup quantizes the small x).
-//   5 <= B <= 16, K a multiple of 256 up to 5120: k_gemv_xquant, then
-//     k_gemv_xreg (x' in registers).
-//   otherwise while x fits LDS: k_gemv_stream (x quantized in every workgroup
-//     when fp16 x' fits, else by k_gemv_xquant first).
+//   fp16 x' fits LDS: k_gemv_stream, x quantized in every workgroup.
+//   else up to 16 rows with K a multiple of 256 up to 5120 (the decode shape
+//     from 8 rows): k_gemv_xquant, then k_gemv_xreg (x' in registers).
+//   else while x fits LDS as codes: k_gemv_xquant, then k_gemv_stream.
 //   longer K: k_gemv_xquant, then k_gemv_mfma.
 // k_gemv_xquant: x -> NVFP4 once, exactly as nvfp4_quantize does, into the
 //   workspace: as exact fp16 x' rows (for the long-K kernel) or as codes +
@@ -1032,8 +1032,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1)
 }
 
 // ------------------------------------------ GEMV with x' in registers --
-// Wider batches (5 to 16 rows) with K a multiple of 256 up to 5120: x,
-// quantized once by the prep launch (codes + scale bytes), is copied into LDS
+// Batches whose fp16 x' does not fit LDS, up to 16 rows, K a multiple of 256
+// up to 5120: x, quantized once by the prep launch (codes + scale bytes), is copied into LDS
 // and each wave dequantizes its share of it once, into registers, instead of
 // once per strip (fp16 x' of 16 rows x 5120 values would need all of LDS).
 // A workgroup of 8 waves (two per SIMD, 256 registers each) serves two strips
@@ -1371,20 +1371,6 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
   const bool xf16 = lds_f16 + lds_fixed <= lds_max;
   // (the strip-relative buffer offsets need 16 rows of W to span < 2^31 bytes;
   // the x' sizes above already keep K far below that)
-  // 5 to 16 batch rows, K a multiple of 256 up to 5120, 16-aligned scale rows:
-  // x quantized once, then x' held in registers; the grid is cut so that every
-  // workgroup serves the same number of rounds
-  if (B > 4 && B <= 16 && K % 256 == 0 && Kq / 256 <= kXrSplit * kXrMaxPairs &&
-      reinterpret_cast<uintptr_t>(w_scales) % 16 == 0 && B * N * 4 < ((int64_t)1 << 31)) {
-    const int lds_x = xreg_lds_bytes((int)B, (int)Kq) + 16;
-    hipError_t e = launch_xquant(x, x_bf16, B, K, Kq, false, ws, stream);
-    if (e != hipSuccess) return e;
-    const int per_round = ncu * kXrSlots;
-    const int rounds = (nstrips + per_round - 1) / per_round;
-    const int grid = (nstrips + kXrSlots * rounds - 1) / (kXrSlots * rounds);
-    return y_bf16 ? launch_xreg<true>(ws, B, W, w_scales, g_w, N, K, Kq, g_d, y, grid, lds_x, stream)
-                  : launch_xreg<false>(ws, B, W, w_scales, g_w, N, K, Kq, g_d, y, grid, lds_x, stream);
-  }
   // narrow batches (K a multiple of 64, 4-aligned scale rows): the FP4-MFMA kernel
   if (B <= 4 && K % 64 == 0 && reinterpret_cast<uintptr_t>(w_scales) % 4 == 0 && K < (1 << 27)) {
     const int nmf = (int)((B + 1) / 2);
@@ -1399,6 +1385,20 @@ hipError_t launch_gemv(const void* x, bool x_bf16, int64_t B, const uint8_t* W,
       return nmf == 1 ? launch_fp4<false, 1>(sa, grid, (int)lds_k, stream)
                       : launch_fp4<false, 2>(sa, grid, (int)lds_k, stream);
     }
+  }
+  // fp16 x' too large for LDS, up to 16 batch rows, K a multiple of 256 up to
+  // 5120, 16-aligned scale rows: x quantized once, then x' held in registers;
+  // the grid is cut so that every workgroup serves the same number of rounds
+  if (!xf16 && B <= 16 && K % 256 == 0 && Kq / 256 <= kXrSplit * kXrMaxPairs &&
+      reinterpret_cast<uintptr_t>(w_scales) % 16 == 0 && B * N * 4 < ((int64_t)1 << 31)) {
+    const int lds_x = xreg_lds_bytes((int)B, (int)Kq) + 16;
+    hipError_t e = launch_xquant(x, x_bf16, B, K, Kq, false, ws, stream);
+    if (e != hipSuccess) return e;
+    const int per_round = ncu * kXrSlots;
+    const int rounds = (nstrips + per_round - 1) / per_round;
+    const int grid = (nstrips + kXrSlots * rounds - 1) / (kXrSlots * rounds);
+    return y_bf16 ? launch_xreg<true>(ws, B, W, w_scales, g_w, N, K, Kq, g_d, y, grid, lds_x, stream)
+                  : launch_xreg<false>(ws, B, W, w_scales, g_w, N, K, Kq, g_d, y, grid, lds_x, stream);
   }
   if ((xf16 || lds_fp4 + lds_fixed <= lds_max) && K < (1 << 27)) {
     // x' fits LDS as fp16 (narrow batches): every workgroup quantizes the

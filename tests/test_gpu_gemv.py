@@ -69,14 +69,15 @@ def test_gemv_several_rounds(B, N, K):
     _run_and_check(x, True, Wq, Ws, 0.02, N, K, 1.0, torch.float32)
 
 
-@pytest.mark.parametrize("B,N,K", [(5, 33, 256), (16, 17, 1280), (8, 300, 4864), (13, 40000, 2048),
-                                   (16, 1, 5120), (6, 4099, 768)])
+@pytest.mark.parametrize("B,N,K", [(16, 17, 2304), (16, 300, 2560), (8, 40000, 5120), (12, 1, 5120),
+                                   (9, 4099, 4864), (16, 70, 3328)])
 def test_gemv_x_in_registers(B, N, K):
-    """5 to 16 batch rows with K a multiple of 256 up to 5120: x dequantized
-    once per wave into registers, a quarter of K per wave.  Covers quarters
-    with no pairs (K = 256: one pair in all), uneven quarters (K = 1280, 4864),
-    many rounds of two strips per workgroup (N = 40000), a single strip, ragged
-    last strips, and float32 x."""
+    """Batches whose fp16 x' does not fit LDS (8 to 16 rows, K a multiple of
+    256 up to 5120): x dequantized once per wave into registers, a quarter of K
+    per wave.  Covers a quarter with no pairs (K = 2304: 3, 3, 3, 0 pairs),
+    uneven quarters (K = 2560, 3328, 4864), many rounds of two strips per
+    workgroup (N = 40000), a single strip of one row, ragged last strips, and
+    float32 x."""
     announce(f"gemv x' in registers B={B} N={N} K={K}")
     Wq = workloads.random_codes((N, K // 2), seed=N + K)
     Ws = workloads.random_bytes((N, K // 16), 0x18, 0x58, seed=N + K + 1)
