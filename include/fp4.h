@@ -302,8 +302,9 @@ fp4_status fp4_gemv_batched(const void* x, fp4_dtype xt, int64_t B, const uint8_
  * The global amax is that of the rotated tensor (computed unless amax_given).
  *   mode FP4_RNE: as nvfp4_quantize.
  *   mode FP4_SR:  element codes rounded stochastically (scales stay nearest):
- *     for lo <= |q| < hi adjacent E2M1 magnitudes, round up iff
- *     u16 < ((|q| - lo) / (hi - lo)) * 65536, where u16 are 16 bits of
+ *     for lo <= |q| < hi adjacent E2M1 magnitudes and f = (|q| - lo) / (hi - lo),
+ *     round up iff floor(f * 2^22) + 64 * u16 >= 2^22 (probability
+ *     floor(f * 2^16) / 2^16; |q| >= 6 gives 6), where u16 are 16 bits of
  *     Philox4x32-10 (Salmon et al., SC'11) with key (seed low, seed high) and
  *     counter (i/8 low, i/8 high, 0, 0) for flat element index i, taking word
  *     (i%8)/2, low half for even i%8, high half for odd.

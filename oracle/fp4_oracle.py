@@ -38,11 +38,12 @@ design notes):
   * Hadamard: orthonormal Sylvester-order FWHT over 128 contiguous channels,
     butterfly stages h = 1, 2, 4, ..., 64 in float32, then one multiply by
     fl32(1/sqrt(128)); global amax taken over the rotated tensor
-  * stochastic rounding: element rounding only; round up with probability equal
-    to the position inside the E2M1 interval, compared against 16 random bits
-    per element drawn from Philox4x32-10 (Salmon et al., "Parallel random
-    numbers: as easy as 1, 2, 3", SC'11) keyed by the 64-bit seed, counter =
-    flat element index // 8, bits taken 16 at a time, low half first
+  * stochastic rounding: element rounding only; the position inside the E2M1
+    interval, truncated to 22 bits, plus 64 times 16 random bits per element
+    carries into the code (round up with probability floor(f 2^16) / 2^16 for
+    position f); the bits come from Philox4x32-10 (Salmon et al., "Parallel
+    random numbers: as easy as 1, 2, 3", SC'11) keyed by the 64-bit seed,
+    counter = flat element index // 8, bits taken 16 at a time, low half first
 """
 from __future__ import annotations
 
@@ -495,8 +496,10 @@ def sr_bits(rows: int, cols: int, seed: int) -> np.ndarray:
 def sr_round(q: np.ndarray, bits: np.ndarray) -> np.ndarray:
     """Stochastic E2M1 rounding ([WIKI] 技術實現與量化方法 names stochastic
     rounding as the NVFP4 element rounding option).  For lo <= |q| < hi adjacent
-    E2M1 magnitudes, round up to hi with probability (|q|-lo)/(hi-lo): up iff
-    float(u16) < frac * 65536.  |q| >= 6 gives 6.  Sign from q."""
+    E2M1 magnitudes and f = (|q|-lo)/(hi-lo), the position's top 22 bits
+    D = floor(f * 2^22) plus 64 * u16 carry into the code: up to hi iff
+    D + 64 * u16 >= 2^22 (probability floor(f * 2^16) / 2^16 for uniform u16).
+    |q| >= 6 gives 6.  Sign from q."""
     q = np.asarray(q, dtype=F32)
     m = np.abs(q).astype(F64)
     mags = E2M1_MAGNITUDES
@@ -505,8 +508,9 @@ def sr_round(q: np.ndarray, bits: np.ndarray) -> np.ndarray:
     lo = mags[lo_idx]
     hi = mags[hi_idx]
     span = np.where(hi_idx > lo_idx, hi - lo, 1.0)
-    frac = np.where(hi_idx > lo_idx, (m - lo) / span, 0.0)
-    up = np.asarray(bits, dtype=F64) < frac * 65536.0
+    frac = np.where(hi_idx > lo_idx, (m - lo) / span, 0.0)   # exact in float64
+    D = np.floor(frac * 2.0 ** 22)
+    up = D + 64.0 * np.asarray(bits, dtype=F64) >= 2.0 ** 22
     code = np.where(up, hi_idx, lo_idx)
     sign = np.signbit(q).astype(np.int64) << 3
     return (code | sign).astype(np.uint8)

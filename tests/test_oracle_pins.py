@@ -485,6 +485,15 @@ def test_philox_known_answers():
         assert [int(w[0]) for w in out] == v[6:]
 
 
+def test_sr_rule_hand_worked(golden):
+    """Single elements against hand-worked codes (tests/golden/sr_rule.txt),
+    including a position whose bits below 2^-22 are dropped (q = 0.25 + 2^-25)
+    and the sign of a zero."""
+    for qh, u, c in golden("sr_rule.txt"):
+        q = np.array([int(qh, 16)], np.uint32).view(F32)
+        assert int(o.sr_round(q, np.array([int(u)], np.uint16))[0]) == int(c, 16), (qh, u)
+
+
 def test_sr_unbiased_and_deterministic():
     n = 1_000_000
     bits = o.sr_bits(1000, 1000, workloads.SEED_SR).reshape(-1)
