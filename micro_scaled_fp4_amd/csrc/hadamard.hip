@@ -156,35 +156,30 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
   }
 }
 
-// Stochastic E2M1 code of q given 16 random bits u: for lo <= |q| < hi
-// adjacent magnitudes, round up iff u < (|q| - lo) / (hi - lo) * 65536,
-// evaluated exactly as u * (hi - lo) * 2^-16 < |q| - lo.  |q| >= 6 gives 6.
-__device__ __forceinline__ uint32_t e2m1_code_sr(float q, uint32_t u) {
-  const uint32_t bits = __float_as_uint(q);
-  const float m = __uint_as_float(bits & 0x7fffffffu);
-  const uint32_t sign = (bits >> 28) & 8u;
-  if (m >= 6.0f) return 7u | sign;
-  uint32_t lo_code;
-  float lo, span;
-  if (m < 1.0f) {
-    const bool half = m >= 0.5f;
-    lo_code = half ? 1u : 0u;
-    lo = half ? 0.5f : 0.0f;
-    span = 0.5f;
-  } else {
-    const uint32_t mb = bits & 0x7fffffffu;
-    lo_code = (mb >> 22) - 252u;                               // 1.0 -> 2, ..., 4.0 -> 6
-    lo = __uint_as_float(mb & 0xffc00000u);                     // truncate to 1 mantissa bit
-    span = __uint_as_float((mb & 0x7f800000u) - 0x00800000u);   // half the binade's power
+// Stochastic E2M1 codes of eight values q (value j in nibble j) given the four
+// Philox words of their counter: value j takes the 16 bits u_j of word j / 2
+// (low half for even j).  For lo <= |q| < hi adjacent E2M1 magnitudes and
+// f = (|q| - lo) / (hi - lo), the code rounds up iff
+// floor(f * 2^22) + 64 u_j >= 2^22 (|q| >= 6 gives 6, the sign is q's).
+// v_cvt_scalef32_sr_pk_fp4_f32 rounds exactly so: it adds 22 bits of its
+// random operand (bits 10..31 for the pair's first value, 9..30 for the
+// second) to the 22 bits of |q| below the code and keeps the carry.  Each
+// value gets an operand of its own, u_j in the top 16 of its 22 bits and zeros
+// below, with 0 in the pair's other slot (code 0), so the two values of a pair
+// never share random bits.  The instruction leaves the destination's other
+// bytes undefined, so only byte 0 of each result is used.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e2m1_pack8_sr(const float (&q)[8], const uint32_t (&ctr)[4]) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t r0 = ctr[p] << 16;                 // low half at bits 16..31, 10..15 zero
+    const uint32_t r1 = (ctr[p] >> 1) & 0x7fff8000u;  // high half at bits 15..30, 9..14 zero
+    const uint32_t a = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2v{q[2 * p], 0.0f}, r0, 1.0f, 0);
+    const uint32_t b = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2v{0.0f, q[2 * p + 1]}, r1, 1.0f, 0);
+    out |= ((a & 0x0fu) | (b & 0xf0u)) << (8 * p);
   }
-  const float d = m - lo;                   // exact
-  const float t = (float)u * span * 0x1p-16f;   // exact
-  return (lo_code + (t < d ? 1u : 0u)) | sign;
-}
-
-__device__ __forceinline__ uint32_t pack8(const uint32_t (&c)[8]) {
-  return c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) | (c[5] << 20) |
-         (c[6] << 24) | (c[7] << 28);
+  return out;
 }
 
 // ------------------------------------------------------------------ kernels --
@@ -273,17 +268,14 @@ __global__ void __launch_bounds__(kThreads)
       for (int half = 0; half < 2; ++half) {
         const int base = 16 * blk + 8 * half;
         if (SR) {
-          uint32_t c[8];
           // elements 32s + base .. +7 share Philox counter (32s + base) / 8
           const uint64_t g = (uint64_t)(4 * s + 2 * blk + half);
           uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), 0u, 0u};
           philox4x32_10(ctr, k0, k1);
+          float qv[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t u = (j & 1) ? (ctr[j >> 1] >> 16) : (ctr[j >> 1] & 0xffffu);
-            c[j] = e2m1_code_sr(v[base + j] * r, u);
-          }
-          w[2 * blk + half] = pack8(c);
+          for (int j = 0; j < 8; ++j) qv[j] = v[base + j] * r;
+          w[2 * blk + half] = e2m1_pack8_sr(qv, ctr);
         } else {
           float qv[8];
 #pragma unroll
@@ -399,13 +391,7 @@ __global__ void __launch_bounds__(kThreads)
         const uint64_t g = (uint64_t)(4 * s + g8);
         uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), 0u, 0u};
         philox4x32_10(ctr, k0, k1);
-        uint32_t c[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t u = (j & 1) ? (ctr[j >> 1] >> 16) : (ctr[j >> 1] & 0xffffu);
-          c[j] = e2m1_code_sr(qv[j], u);
-        }
-        w[g8] = pack8(c);
+        w[g8] = e2m1_pack8_sr(qv, ctr);
       } else {
         w[g8] = e2m1_pack8(qv);
       }
