@@ -90,6 +90,42 @@ def test_every_call_replays_in_a_graph():
         del junk
 
 
+def test_gemv_register_path_replays_in_a_graph():
+    """The GEMV path whose fp16 x' does not fit LDS (16 rows, K = 2560: the
+    prep launch, then x' in registers) captured in a graph and replayed with
+    new inputs and eager work between, byte-equal to eager calls."""
+    announce("graph capture and replay of the register-x GEMV")
+    dev = "cuda:0"
+    Nw, Kw, B = 300, 2560, 16
+    qw = torch.from_numpy(workloads.random_codes((Nw, Kw // 2), 1401)).to(dev)
+    sw = torch.from_numpy(workloads.random_bytes((Nw, Kw // 16), 0x18, 0x58, 1402)).to(dev)
+    gw = torch.tensor([0.02], dtype=torch.float32, device=dev)
+    inputs = [to_gpu_bf16(workloads.gemv_x(B, Kw, seed=1410 + k)) for k in range(4)]
+    x = inputs[0].clone()
+
+    def call(xx):
+        return fp4.fp4_gemv_batched(xx, qw, sw, gw, Kw, 1.0, torch.bfloat16)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y = call(x)
+    for k in (1, 2, 3, 1):
+        x.copy_(inputs[k])
+        junk = torch.randn(1 << 20, device=dev).sum()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = call(inputs[k])
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.uint8), ref.view(torch.uint8)), f"replay {k}"
+        del junk
+
+
 def test_concurrent_calls_from_two_threads_on_two_streams():
     announce("two host threads, two streams")
     dev = "cuda:0"
@@ -151,12 +187,17 @@ swm = torch.from_numpy(workloads.random_bytes((N, K // 32), 120, 134, 6))
 qa, qw, sa, sw, sam, swm = (t.to(dev) for t in (qa, qw, sa, sw, sam, swm))
 g = torch.ones(1, dtype=torch.float32, device=dev)
 x = torch.from_numpy(workloads.normal((4, K), 7)).to(dev).to(torch.bfloat16)
+K2 = 2560                      # 16 rows: the GEMV path with x' in registers
+qw2 = torch.from_numpy(workloads.random_codes((N, K2 // 2), 8)).to(dev)
+sw2 = torch.from_numpy(workloads.random_bytes((N, K2 // 16), 0x20, 0x50, 9)).to(dev)
+x2 = torch.from_numpy(workloads.normal((16, K2), 10)).to(dev).to(torch.bfloat16)
 torch.cuda.synchronize()
 
 def work():
     return [fp4.fp4_scaled_gemm(fp4.FP4_NVFP4, qa, sa, g, qw, sw, g, K, 1.0, torch.bfloat16),
             fp4.fp4_scaled_gemm(fp4.FP4_MXFP4, qa, sam, None, qw, swm, None, K, 1.0, torch.float32),
-            fp4.fp4_gemv_batched(x, qw, sw, g, K, 1.0, torch.float32)]
+            fp4.fp4_gemv_batched(x, qw, sw, g, K, 1.0, torch.float32),
+            fp4.fp4_gemv_batched(x2, qw2, sw2, g, K2, 1.0, torch.float32)]
 
 streams = [torch.cuda.Stream() for _ in range(2)]
 results, errors = [None, None], []
