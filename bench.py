@@ -16,7 +16,8 @@ workload's shape:
                and to NVFP4 at a given (calibrated) amax
   MoE          grouped GEMM, 64 experts x (N 2048, K 7168), 32768 routed rows with
                uneven expert loads, NVFP4, bf16 output, one launch
-  rotate       16384x8192 bf16, 16 outlier channels x60: FWHT-128 + NVFP4, RNE and SR
+  rotate       16384x8192 bf16, 16 outlier channels x60: FWHT-128 + NVFP4, RNE and SR;
+               FWHT-128 + MXFP4 (one pass), RNE and SR; FWHT-128 alone
 Each call kind is captured in its own HIP graph of R back-to-back calls that
 cycle through input copies totalling >= 1 GiB (more than the 256 MiB Infinity
 Cache), so consecutive calls never find their inputs in cache and no host
@@ -532,16 +533,21 @@ def main():
                                  stream_of())
         assert st == 0, st
 
-    def had_mx(i):
-        st = lib.hadamard_quantize_mx(P(xh_c[i]), fp4.FP4_BF16, R_H, C_H, 128, fp4.FP4_RNE,
-                                      ctypes.c_uint64(0), P(qhm), P(shm), stream_of())
+    def had_mx(i, mode=fp4.FP4_RNE):
+        st = lib.hadamard_quantize_mx(P(xh_c[i]), fp4.FP4_BF16, R_H, C_H, 128, mode,
+                                      ctypes.c_uint64(workloads.SEED_SR), P(qhm), P(shm), stream_of())
         assert st == 0, st
+
+    def had_mx_sr(i):
+        had_mx(i, fp4.FP4_SR)
 
     ops += [
         Op("hadamard_rotate_bf16", had_rot, nH, "GB/s", eh * 4, HBM_PEAK_GBS, "hbm",
            "k_had_rotate (FWHT-128 alone)", hsrc),
         Op("hadamard_quantize_mx", had_mx, nH, "GB/s", eh * 2 + eh // 2 + eh // 32, HBM_PEAK_GBS,
            "hbm", "k_had_quant_mx (FWHT-128 + MXFP4, one pass)", hsrc),
+        Op("hadamard_quantize_mx_sr", had_mx_sr, nH, "GB/s", eh * 2 + eh // 2 + eh // 32, HBM_PEAK_GBS,
+           "hbm", "k_had_quant_mx (FWHT-128 + MXFP4, stochastic rounding, one pass)", hsrc),
     ]
 
     L.ops = {op.name: op for op in ops}
@@ -1031,6 +1037,14 @@ def oracle_leg(L, seconds):
     record("hadamard_quantize_mx", gq.size + gs_.size,
            np.count_nonzero(gq != ref[0]) + np.count_nonzero(gs_ != ref[1]), "codes and E8M0 bytes of 32 rows")
     rate("hadamard_quantize_mx", len(rows_h) * xh.shape[1] * (2 + 0.5 + 1 / 32), dt, "32 sampled rows")
+    # stochastic rounding on rows 0..31, whose flat element indices (the SR
+    # counters) are the same in the 32-row sample as in the whole tensor
+    L.run("hadamard_quantize_mx_sr")
+    gq, gs_ = host(L.qhm)[:32], host(L.shm)[:32]
+    ref, dt = timed(lambda: o.hadamard_quantize_mx(xh[:32], rounding="sr", seed=L.seed_sr))
+    record("hadamard_quantize_mx_sr", gq.size + gs_.size,
+           np.count_nonzero(gq != ref[0]) + np.count_nonzero(gs_ != ref[1]), "codes and E8M0 bytes of rows 0..31")
+    rate("hadamard_quantize_mx_sr", 32 * xh.shape[1] * (2 + 0.5 + 1 / 32), dt, "rows 0..31")
 
     cpu = {"value": head_value, "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": head_sample,
